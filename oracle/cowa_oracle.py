@@ -1,0 +1,311 @@
+"""Plain CPU oracle of CoWindow Attention (CoWA) — TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The GPU library never calls it, and this module
+imports nothing from the GPU library: the two share no code, no headers and no
+constants.  Everything here is plain NumPy in float64, written from the pages'
+description of the method, step by step, with no blocking or fusion beyond what the
+definition states.
+
+What the method computes (the pages' description, restated):
+
+* CoWindow Attention: Full Causal Coverage Is a Collective Property — abstract (as
+  carried on the crimsonlingua.com and humanity-list.pdj.dev pages) and the
+  slinene.github.io ai-papers-daily page, section "method key points" (方法关键点):
+  every KV head keeps a near-diagonal window of recent context and a prefix-sink window
+  at the start of the sequence, both shared by all heads; the history left beyond the
+  near window is split at breakpoints into equal-width long-range windows, one per KV
+  head, so each head is dense nearby and sparse far away while the union over heads
+  covers the whole causal prefix.
+* Same page, method key point 2: one bottom-right-aligned causal distance defines
+  training, prefill and decoding; a window is the quadruple
+  (sink width, near width, gap, long-range width).
+* Same page, method key point 3: windows follow the global KV-head index; the
+  traversal skips KV blocks that are invisible.
+
+The attention itself is exact masked softmax attention under that fixed mask (the
+method saves work by skipping masked keys, not by approximating), so the oracle is the
+plain definition: build the mask element by element, then softmax(scale q k^T) v over
+the visible keys in float64.
+
+Readings where the pages are silent (each is also listed in the design notes):
+  distance       d = i + (Lk - Lq) - j  (bottom-right alignment); causal iff d >= 0
+  sink           absolute key index j < sink, shared by all heads, still causal
+  near           0 <= d < near (half-open, includes the diagonal)
+  gap            distances [near, near + gap) belong to no band
+  bands          head h owns distances [near + gap + h*lr, near + gap + (h+1)*lr),
+                 lr = ceil((Lmax - near - gap) / Hkv); "duplicated" gives every head
+                 band 0; "dense" widens every band to all larger distances
+  overlaps       the mask is the OR of the three windows (a key counts once)
+  GQA            query head q reads KV head q // (Hq // Hkv)
+  LSE            natural log of sum over visible keys of exp(scale * q.k)
+  empty row      O = 0, LSE = -inf (only possible when near = 0)
+
+Every function here is pinned by tests that do not re-use its formulas: textbook
+dense attention (torch SDPA in float64) for the dense special case, brute-force loops on
+tiny inputs, finite differences for the gradients, coverage / disjointness / width
+invariants of the mask, and edge counts from an independent interval-arithmetic count.
+"""
+
+import math
+
+import numpy as np
+
+COMPLEMENTARY = "complementary"
+DUPLICATED = "duplicated"
+DENSE = "dense"
+MODES = (COMPLEMENTARY, DUPLICATED, DENSE)
+
+
+# --------------------------------------------------------------------------- window
+
+def complementary_width(Lmax, Hkv, near, gap):
+    """Width of each long-range band: the history beyond near (+gap) up to the longest
+    distance Lmax split into Hkv equal widths (method key point 1, "equal widths";
+    ceiling so that the Hkv bands reach Lmax)."""
+    rest = Lmax - near - gap
+    if rest <= 0:
+        return 0
+    return -(-rest // Hkv)
+
+
+class Window:
+    """The quadruple (sink, near, gap, lr) of method key point 2, plus the band mode."""
+
+    def __init__(self, sink, near, gap, lr, mode=COMPLEMENTARY):
+        assert mode in MODES
+        assert min(sink, near, gap, lr) >= 0
+        self.sink, self.near, self.gap, self.lr, self.mode = sink, near, gap, lr, mode
+
+    @classmethod
+    def for_length(cls, Lmax, Hkv, sink, near, gap=0, mode=COMPLEMENTARY):
+        return cls(sink, near, gap, complementary_width(Lmax, Hkv, near, gap), mode)
+
+    def band(self, h):
+        """Distances [lo, hi) of KV head h's long-range window (hi = None: unbounded)."""
+        start = self.near + self.gap
+        if self.mode == DENSE:
+            return start, None
+        slot = h if self.mode == COMPLEMENTARY else 0
+        lo = start + slot * self.lr
+        return lo, lo + self.lr
+
+    def __repr__(self):
+        return (f"Window(sink={self.sink}, near={self.near}, gap={self.gap}, "
+                f"lr={self.lr}, mode={self.mode})")
+
+
+def mask_rows(rows, Lq, Lk, h, win):
+    """Boolean mask [len(rows), Lk]: key j visible to query row i under KV head h.
+
+    Evaluated element by element on the full (i, j) grid from the definition — no
+    interval arithmetic — so it stays independent of any block planner."""
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(Lk, dtype=np.int64)[None, :]
+    d = i + (Lk - Lq) - j
+    causal = d >= 0
+    in_sink = j < win.sink
+    in_near = d < win.near
+    lo, hi = win.band(h)
+    in_band = d >= lo
+    if hi is not None:
+        in_band = in_band & (d < hi)
+    return causal & (in_sink | in_near | in_band)
+
+
+def full_mask(Lq, Lk, h, win):
+    return mask_rows(np.arange(Lq), Lq, Lk, h, win)
+
+
+# --------------------------------------------------------------------------- forward
+
+def _f64(x):
+    """Upcast (exactly) to float64 NumPy; accepts NumPy arrays or torch CPU tensors."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        import torch  # only for the dtype conversion of torch inputs
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _masked_softmax_row_stats(s, m):
+    """Row max, denominator and probabilities of a masked score matrix s [R, Lk]."""
+    s = np.where(m, s, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    empty = ~np.isfinite(mx)
+    mx = np.where(empty, 0.0, mx)
+    e = np.where(m, np.exp(s - mx), 0.0)
+    den = e.sum(axis=1, keepdims=True)
+    p = np.where(den > 0, e / np.where(den > 0, den, 1.0), 0.0)
+    lse = np.where(den > 0, mx + np.log(np.where(den > 0, den, 1.0)), -np.inf)
+    return p, lse[:, 0]
+
+
+def attn_fwd(q, k, v, win, scale, rows=None):
+    """Masked-softmax attention forward on query rows `rows` (default: all).
+
+    q [B, Lq, Hq, D], k/v [B, Lk, Hkv, D]  ->  O [B, R, Hq, D], LSE [B, Hq, R]
+    For query head qh (KV head h = qh // G): s_ij = scale q_i.k_j, masked to the
+    visible keys; O_i = sum_j softmax(s)_ij v_j; LSE_i = log sum_j exp(s_ij)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Lq, Hq, D = q.shape
+    _, Lk, Hkv, _ = k.shape
+    G = Hq // Hkv
+    rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    O = np.zeros((B, len(rows), Hq, D))
+    LSE = np.zeros((B, Hq, len(rows)))
+    for h in range(Hkv):
+        m = mask_rows(rows, Lq, Lk, h, win)
+        for b in range(B):
+            for qh in range(h * G, (h + 1) * G):
+                s = scale * (q[b, rows, qh, :] @ k[b, :, h, :].T)
+                p, lse = _masked_softmax_row_stats(s, m)
+                O[b, :, qh, :] = p @ v[b, :, h, :]
+                LSE[b, qh, :] = lse
+    return O, LSE
+
+
+# --------------------------------------------------------------------------- backward
+
+def attn_bwd(q, k, v, do, win, scale):
+    """Full gradients of L = sum(O * dO) for the forward above (all rows).
+
+    P = softmax of the masked scores; Delta_i = dO_i . O_i; dP_ij = dO_i . v_j;
+    dS_ij = P_ij (dP_ij - Delta_i); dQ_i = scale sum_j dS_ij k_j;
+    dK_j = scale sum over the KV head's query heads and rows of dS_ij q_i;
+    dV_j = sum over the same of P_ij dO_i.
+    Returns (dQ [B,Lq,Hq,D], dK [B,Lk,Hkv,D], dV [B,Lk,Hkv,D])."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Lq, Hq, D = q.shape
+    _, Lk, Hkv, _ = k.shape
+    G = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(Hkv):
+        m = full_mask(Lq, Lk, h, win)
+        for b in range(B):
+            for qh in range(h * G, (h + 1) * G):
+                s = scale * (q[b, :, qh, :] @ k[b, :, h, :].T)
+                p, _ = _masked_softmax_row_stats(s, m)
+                o = p @ v[b, :, h, :]
+                delta = (do[b, :, qh, :] * o).sum(axis=1, keepdims=True)
+                dp = do[b, :, qh, :] @ v[b, :, h, :].T
+                ds = p * (dp - delta)
+                dq[b, :, qh, :] = scale * (ds @ k[b, :, h, :])
+                dk[b, :, h, :] += scale * (ds.T @ q[b, :, qh, :])
+                dv[b, :, h, :] += p.T @ do[b, :, qh, :]
+    return dq, dk, dv
+
+
+def attn_bwd_dq_rows(q, k, v, do, win, scale, rows):
+    """dQ on the query rows `rows` only: needs just those rows' own softmax and
+    Delta_i = dO_i . O_i with O_i from the rows' own forward.  -> [B, R, Hq, D]"""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Lq, Hq, D = q.shape
+    _, Lk, Hkv, _ = k.shape
+    G = Hq // Hkv
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((B, len(rows), Hq, D))
+    for h in range(Hkv):
+        m = mask_rows(rows, Lq, Lk, h, win)
+        for b in range(B):
+            for qh in range(h * G, (h + 1) * G):
+                s = scale * (q[b, rows, qh, :] @ k[b, :, h, :].T)
+                p, _ = _masked_softmax_row_stats(s, m)
+                o = p @ v[b, :, h, :]
+                delta = (do[b, rows, qh, :] * o).sum(axis=1, keepdims=True)
+                dp = do[b, rows, qh, :] @ v[b, :, h, :].T
+                ds = p * (dp - delta)
+                dq[b, :, qh, :] = scale * (ds @ k[b, :, h, :])
+    return dq
+
+
+def attn_bwd_dkdv_cols(q, k, v, do, win, scale, cols, row_chunk=512):
+    """dK and dV on the key columns `cols` only.
+
+    A column j receives from every query row that sees it, so the rows are found from
+    the explicit mask, and each such row's full softmax (over all its visible keys) is
+    computed before its contribution to the requested columns is summed.
+    -> dK [B, C, Hkv, D], dV [B, C, Hkv, D]"""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Lq, Hq, D = q.shape
+    _, Lk, Hkv, _ = k.shape
+    G = Hq // Hkv
+    cols = np.asarray(cols, dtype=np.int64)
+    dk = np.zeros((B, len(cols), Hkv, D))
+    dv = np.zeros((B, len(cols), Hkv, D))
+    for h in range(Hkv):
+        # rows that see at least one requested column
+        need = np.zeros(Lq, dtype=bool)
+        for start in range(0, Lq, row_chunk):
+            r = np.arange(start, min(Lq, start + row_chunk))
+            need[r] = mask_rows(r, Lq, Lk, h, win)[:, cols].any(axis=1)
+        rows_all = np.nonzero(need)[0]
+        for start in range(0, len(rows_all), row_chunk):
+            rows = rows_all[start:start + row_chunk]
+            m = mask_rows(rows, Lq, Lk, h, win)
+            for b in range(B):
+                for qh in range(h * G, (h + 1) * G):
+                    s = scale * (q[b, rows, qh, :] @ k[b, :, h, :].T)
+                    p, _ = _masked_softmax_row_stats(s, m)
+                    o = p @ v[b, :, h, :]
+                    delta = (do[b, rows, qh, :] * o).sum(axis=1, keepdims=True)
+                    pc = p[:, cols]
+                    dpc = do[b, rows, qh, :] @ v[b, cols, h, :].T
+                    dsc = pc * (dpc - delta)
+                    dk[b, :, h, :] += scale * (dsc.T @ q[b, rows, qh, :])
+                    dv[b, :, h, :] += pc.T @ do[b, rows, qh, :]
+    return dk, dv
+
+
+# --------------------------------------------------------------------------- decode
+
+def decode(q, k_cache, v_cache, win, scale):
+    """One new query token per sequence over a cache of Lk positions holding the new
+    token; the query is at position Lk - 1, i.e. the forward with Lq = 1 under the same
+    bottom-right distance (method key point 2).  q [B, 1, Hq, D] -> O [B, 1, Hq, D],
+    LSE [B, Hq, 1]."""
+    return attn_fwd(q, k_cache, v_cache, win, scale, rows=[0])
+
+
+# --------------------------------------------------------------------------- tiles
+
+def tile_lists(Lq, Lk, Hkv, Bq, Bk, win):
+    """Per KV head and q-block, the visible k-blocks with their FULL flag, read off
+    the explicit mask: a tile is listed iff ANY of its elements is visible, and FULL
+    iff every one of its Bq x Bk elements is in range and visible (method key point 3:
+    only visible blocks are traversed).  -> lists[h][qb] = [(kb, full), ...] ascending."""
+    nqb = -(-Lq // Bq)
+    nkb = -(-Lk // Bk)
+    out = []
+    for h in range(Hkv):
+        per_h = []
+        for qb in range(nqb):
+            rows = np.arange(qb * Bq, min(Lq, (qb + 1) * Bq))
+            m = mask_rows(rows, Lq, Lk, h, win)
+            ent = []
+            for kb in range(nkb):
+                t = m[:, kb * Bk:min(Lk, (kb + 1) * Bk)]
+                if t.any():
+                    full = bool(t.all()) and t.shape == (Bq, Bk)
+                    ent.append((kb, full))
+            per_h.append(ent)
+        out.append(per_h)
+    return out
+
+
+def edge_counts(Lq, Lk, Hkv, win, row_chunk=256):
+    """Visible (query row, key) pairs per KV head, counted on the explicit mask."""
+    counts = []
+    for h in range(Hkv):
+        c = 0
+        for start in range(0, Lq, row_chunk):
+            r = np.arange(start, min(Lq, start + row_chunk))
+            c += int(mask_rows(r, Lq, Lk, h, win).sum())
+        counts.append(c)
+    return counts
+
+
+def default_scale(D):
+    return 1.0 / math.sqrt(D)
