@@ -1,0 +1,209 @@
+// CoWindow Attention decode, bf16 KV cache, head dim 128, for gfx950.
+//
+// One new query token per sequence sits at key position Lk - 1; its bottom-right
+// distance to key j is Lk - 1 - j, the same definition the forward uses
+// (slinene.github.io ai-papers-daily page, method key point 2).  Each KV head reads
+// only the k-blocks in its row of the planner's lists (sink, its own long-range band,
+// near window), so HBM traffic is the visible part of the cache only (same page,
+// practical note 3 and method key point 3).
+//
+// Split-KV: work group (split s, KV head h, sequence b) streams a contiguous share of
+// the head's visible blocks.  Inside the group, 16 slots of 16 lanes each take one key
+// at a time; a lane holds 8 of the 128 dims (16-byte loads, so a slot reads one 256-byte
+// K or V row), and the G query heads of the KV head share every K/V read.  Scores are
+// reduced across the 16 lanes of a slot; the online softmax runs per slot, four keys at
+// a time.  The 16 slots are merged through LDS into one partial (max, sum, o[128]) per
+// query head and split; a second kernel merges the splits (log-sum-exp) into O and LSE.
+
+#include "device_common.h"
+
+namespace cowa {
+namespace {
+
+constexpr int D = 128;
+constexpr int BK = kDecBk;
+constexpr int SLOTS = 16;
+
+__device__ __forceinline__ void unpack8(const u32x4& w, float* x) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(w[k] << 16);
+    x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+  __shared__ float sm[SLOTS][G];
+  __shared__ float sl[SLOTS][G];
+  __shared__ float so[SLOTS][G][D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int li = lane & 15;
+  const int slot = tid >> 4;
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int p = a.Lk - 1;
+  const HeadBand band = head_band(a.win, h);
+
+  // query rows of the G heads, 8 dims per lane, as fp32
+  float q[G][8];
+  const __bf16* Qb = (const __bf16*)a.q + ((int64_t)b * a.Hq + h * G) * D + 8 * li;
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) unpack8(*(const u32x4*)(Qb + gi * D), q[gi]);
+
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    m[gi] = -INFINITY;
+    l[gi] = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) o[gi][x] = 0.f;
+  }
+
+  const int e0 = a.row_ptr[h], e1 = a.row_ptr[h + 1];
+  const int chunk = (e1 - e0 + a.nsplit - 1) / a.nsplit;
+  const int s0 = e0 + split * chunk;
+  const int s1 = min(e1, s0 + chunk);
+  const __bf16* Kb = (const __bf16*)a.k + ((int64_t)b * a.Lk * a.Hkv + h) * D + 8 * li;
+  const __bf16* Vb = (const __bf16*)a.v + ((int64_t)b * a.Lk * a.Hkv + h) * D + 8 * li;
+  const int64_t rstride = (int64_t)a.Hkv * D;
+
+  for (int e = s0; e < s1; ++e) {
+    const int ent = a.row_ent[e];
+    const int kb = ent >> 1;
+    const bool partial = ent & 1;
+    u32x4 kw[4], vw[4];
+    bool ok[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int j = kb * BK + rr * SLOTS + slot;
+      ok[rr] = j < a.Lk;
+      const int jj = ok[rr] ? j : 0;
+      kw[rr] = *(const u32x4*)(Kb + jj * rstride);
+      vw[rr] = *(const u32x4*)(Vb + jj * rstride);
+      if (partial) ok[rr] = ok[rr] && visible(p, j, a.Lk, a.win.sink, a.win.near_w, band);
+    }
+    float s[4][G];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float kx[8];
+      unpack8(kw[rr], kx);
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        float acc = 0.f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc = fmaf(q[gi][x], kx[x], acc);
+        acc += __shfl_xor(acc, 1, 16);
+        acc += __shfl_xor(acc, 2, 16);
+        acc += __shfl_xor(acc, 4, 16);
+        acc += __shfl_xor(acc, 8, 16);
+        s[rr][gi] = ok[rr] ? acc * a.scale_log2 : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const float mt = fmaxf(fmaxf(s[0][gi], s[1][gi]), fmaxf(s[2][gi], s[3][gi]));
+      const float mn = fmaxf(m[gi], mt);
+      if (mn == -INFINITY) continue;
+      const float alpha = (m[gi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[gi] - mn);
+      m[gi] = mn;
+      l[gi] *= alpha;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) o[gi][x] *= alpha;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float vx[8];
+      unpack8(vw[rr], vx);
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const float pr = (m[gi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[rr][gi] - m[gi]);
+        l[gi] += pr;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) o[gi][x] = fmaf(pr, vx[x], o[gi][x]);
+      }
+    }
+  }
+
+  // ---- merge the 16 slots
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    if (li == 0) {
+      sm[slot][gi] = m[gi];
+      sl[slot][gi] = l[gi];
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) so[slot][gi][8 * li + x] = o[gi][x];
+  }
+  __syncthreads();
+  for (int x = tid; x < G * D; x += 256) {
+    const int gi = x / D, d = x - gi * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k) M = fmaxf(M, sm[k][gi]);
+    float L = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < SLOTS; ++k) {
+        const float w = (sm[k][gi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[k][gi] - M);
+        L += w * sl[k][gi];
+        acc += w * so[k][gi][d];
+      }
+    }
+    const int64_t row = ((int64_t)b * a.Hq + h * G + gi) * a.nsplit + split;
+    a.part[row * D + d] = acc;
+    if (d == 0) {
+      a.part_ml[2 * row] = M;
+      a.part_ml[2 * row + 1] = L;
+    }
+  }
+}
+
+__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+  const int bh = blockIdx.x;  // b * Hq + hq
+  const int d = threadIdx.x;
+  const int64_t base = (int64_t)bh * a.nsplit;
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * (base + s)]);
+  float L = 0.f, acc = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float ms = a.part_ml[2 * (base + s)];
+      const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+      L += w * a.part_ml[2 * (base + s) + 1];
+      acc += w * a.part[(base + s) * D + d];
+    }
+  }
+  const float out = L > 0.f ? acc / L : 0.f;
+  ((__bf16*)a.o)[(int64_t)bh * D + d] = (__bf16)out;
+  if (a.lse && d == 0) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+template <int G>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(a.nsplit, a.Hkv, a.B), dim3(256), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(D), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t s) {
+  switch (a.G) {
+    case 1: return launch_g<1>(a, s);
+    case 2: return launch_g<2>(a, s);
+    case 4: return launch_g<4>(a, s);
+    case 5: return launch_g<5>(a, s);
+    case 8: return launch_g<8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool decode_supports_group(int G) { return G == 1 || G == 2 || G == 4 || G == 5 || G == 8; }
+
+}  // namespace cowa

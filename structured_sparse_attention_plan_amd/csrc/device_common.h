@@ -1,0 +1,92 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, MFMA wrappers, LDS
+// transpose loads and the window predicate.
+//
+// MFMA lane layouts (v_mfma_f32_16x16x32_bf16, wave64), with i = lane % 16, g = lane / 16:
+//   A (16 x 32): lane holds A[i][8g .. 8g+7]          (8 bf16)
+//   B (32 x 16): lane holds B[8g .. 8g+7][i]          (8 bf16)
+//   C (16 x 16): lane holds C[4g .. 4g+3][i]          (4 fp32)
+// ds_read_b64_tr_b16: within each 16-lane group, lane j supplies the address of 4
+// consecutive bf16 at row r0 + j/4, column c0 + 4 (j%4) of a row-major matrix M; lane i
+// then receives M[r0 .. r0+3][c0 + i].  Two such loads give one A/B operand whose 8
+// contracted values come from two runs of 4 rows, which is exactly how a C-layout
+// accumulator tile maps onto the contracted index of the next product.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace cowa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed LDS load (see the header comment).  `p` points into __shared__ memory.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
+  const lds_i16x4* lp = (const lds_i16x4*)(__attribute__((address_space(3))) const void*)(p);
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lp);
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 join(const bf16x4& lo, const bf16x4& hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x8 load16(const void* p) {
+  return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
+}
+
+__device__ __forceinline__ void store16(void* p, const bf16x8& v) {
+  *(u32x4*)p = __builtin_bit_cast(u32x4, v);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0}); }
+
+__device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
+  bf16x4 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  r[2] = (__bf16)c;
+  r[3] = (__bf16)d;
+  return r;
+}
+
+// Window of KV head h as distances [lo, hi); hi clamped to int32.
+struct HeadBand {
+  int32_t lo, hi;
+};
+
+__device__ __forceinline__ HeadBand head_band(const DevWindow& w, int h) {
+  int64_t lo = (int64_t)w.band_lo0 + (int64_t)h * w.band_step;
+  int64_t hi = lo + w.band_w;
+  const int64_t cap = 0x7fffffff;
+  return {(int32_t)(lo < cap ? lo : cap), (int32_t)(hi < cap ? hi : cap)};
+}
+
+// Key j (< Lk) visible to the query at key position p under a head's window.
+__device__ __forceinline__ bool visible(int p, int j, int Lk, int sink, int near_w, HeadBand b) {
+  const int d = p - j;
+  return (j < Lk) & (d >= 0) & ((j < sink) | (d < near_w) | ((d >= b.lo) & (d < b.hi)));
+}
+
+}  // namespace cowa

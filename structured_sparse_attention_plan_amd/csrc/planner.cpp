@@ -1,0 +1,200 @@
+// Block-visibility planner for CoWindow Attention.
+//
+// The traversal of the operator visits only KV blocks that hold visible keys
+// (slinene.github.io ai-papers-daily page, "CoWindow Attention: Full Causal Coverage Is
+// a Collective Property", method key point 3).  For a block of consecutive query rows
+// every window — prefix sink, near diagonal and the head's long-range band (method key
+// point 1) — is a key interval whose end points move by one per row, so the keys a
+// q-block can see are the union of at most three intervals.  The planner turns those
+// into k-block ranges and emits them, so its work is proportional to the number of
+// visible tiles: masked tiles are never enumerated.
+//
+// Host-only code: no device memory, no HIP calls.
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "cowa.h"
+#include "window.h"
+
+namespace {
+
+struct Range {  // half-open [a, b)
+  int64_t a, b;
+};
+
+// Keys any row of [p0, p1] (positions p = i + Lk - Lq) can see, as up to three
+// half-open key intervals (empty ones dropped).
+int block_key_ranges(const cowa::Band& band, int64_t sink, int64_t near_w, int64_t p0,
+                     int64_t p1, Range out[3]) {
+  int n = 0;
+  // prefix sink: keys [0, sink) that are causal for some row
+  if (sink > 0 && p1 >= 0) out[n++] = {0, std::min<int64_t>(sink, p1 + 1)};
+  // near diagonal: distances [0, near) -> keys (p - near, p]
+  if (near_w > 0 && p1 >= 0) out[n++] = {std::max<int64_t>(0, p0 - near_w + 1), p1 + 1};
+  // long-range band: distances [lo, hi) -> keys (p - hi, p - lo]; rows with p < lo see none
+  if (band.width() > 0 && p1 >= band.lo) {
+    int64_t pf = std::max<int64_t>(p0, band.lo);
+    int64_t a = band.unbounded() ? 0 : std::max<int64_t>(0, pf - band.hi + 1);
+    out[n++] = {a, p1 - band.lo + 1};
+  }
+  return n;
+}
+
+// Number of keys a single row at position p sees (union of its three intervals).
+int64_t row_visible(const cowa::Band& band, int64_t sink, int64_t near_w, int64_t p) {
+  Range r[3];
+  int n = block_key_ranges(band, sink, near_w, p, p, r);
+  std::sort(r, r + n, [](const Range& x, const Range& y) { return x.a < y.a; });
+  int64_t total = 0, end = 0;
+  for (int k = 0; k < n; ++k) {
+    int64_t a = std::max(r[k].a, end);
+    if (r[k].b > a) {
+      total += r[k].b - a;
+      end = r[k].b;
+    }
+  }
+  return total;
+}
+
+// True iff every (row, key) of rows [p0, p1] x keys [j0, j1] (inclusive) is visible.
+// Keys below `sink` are visible iff causal; for the others visibility depends only on
+// the distance d = p - j, and the tile covers every d in [p0 - j1, p1 - j0'].
+bool tile_full(const cowa::Band& band, int64_t sink, int64_t near_w, int64_t p0, int64_t p1,
+               int64_t j0, int64_t j1) {
+  if (j0 < sink) {  // sink part [j0, min(j1, sink - 1)]
+    int64_t js = std::min<int64_t>(j1, sink - 1);
+    if (p0 - js < 0) return false;
+  }
+  int64_t jr = std::max<int64_t>(j0, sink);
+  if (jr > j1) return true;
+  int64_t dlo = p0 - j1, dhi = p1 - jr;
+  if (dlo < 0) return false;
+  if (dhi < near_w) return true;
+  if (band.width() > 0) {
+    bool below_hi = band.unbounded() || dhi < band.hi;
+    if (dlo >= band.lo && below_hi) return true;
+    // near window and band touch or overlap: one run [0, hi)
+    if (band.lo <= near_w && below_hi) return true;
+  }
+  return false;
+}
+
+}  // namespace
+
+extern "C" int cowa_window_make(int32_t Lmax, int32_t Hkv, int32_t sink, int32_t near_w,
+                                int32_t gap, int32_t band_mode, cowa_window* out) {
+  if (!out || Hkv < 1 || Lmax < 0 || sink < 0 || near_w < 0 || gap < 0) return COWA_ERR_INVALID_ARG;
+  if (band_mode < COWA_BAND_COMPLEMENTARY || band_mode > COWA_BAND_DENSE) return COWA_ERR_INVALID_ARG;
+  int64_t rest = (int64_t)Lmax - near_w - gap;
+  out->sink = sink;
+  out->near_w = near_w;
+  out->gap = gap;
+  out->lr = rest > 0 ? (int32_t)((rest + Hkv - 1) / Hkv) : 0;
+  out->band_mode = band_mode;
+  return COWA_OK;
+}
+
+extern "C" int cowa_plan_blocks(int32_t Lq, int32_t Lk, int32_t Hkv, int32_t Bq, int32_t Bk,
+                                const cowa_window* win, cowa_plan_info* info, int32_t* row_ptr,
+                                int32_t* row_ent, int32_t* col_ptr, int32_t* col_ent,
+                                int32_t* row_order, int32_t* col_order) {
+  if (!win || !info) return COWA_ERR_INVALID_ARG;
+  if (Lq < 1 || Lk < 1 || Hkv < 1 || Bq < 1 || Bk < 1) return COWA_ERR_INVALID_ARG;
+  if (!cowa::window_valid(*win)) return COWA_ERR_INVALID_ARG;
+  const bool want = row_ptr || row_ent || col_ptr || col_ent || row_order || col_order;
+  if (want && !(row_ptr && row_ent && col_ptr && col_ent && row_order && col_order))
+    return COWA_ERR_INVALID_ARG;
+
+  const int64_t off = (int64_t)Lk - Lq;
+  const int32_t nqb = (Lq + Bq - 1) / Bq, nkb = (Lk + Bk - 1) / Bk;
+  const int64_t sink = win->sink, near_w = win->near_w;
+
+  // Pass 1: per row item, the merged k-block ranges; counts and edges.
+  std::vector<int32_t> row_cnt((size_t)Hkv * nqb, 0);
+  int64_t nnz = 0, n_partial = 0, edges = 0, visited = 0;
+  std::vector<int32_t> ents;  // only filled when the caller wants the lists
+  std::vector<int32_t> col_cnt(want ? (size_t)Hkv * nkb : 0, 0);
+  if (want) row_ptr[0] = 0;
+
+  for (int32_t h = 0; h < Hkv; ++h) {
+    const cowa::Band band = cowa::band_of(*win, h);
+    for (int64_t i = 0; i < Lq; ++i) edges += row_visible(band, sink, near_w, i + off);
+    for (int32_t qb = 0; qb < nqb; ++qb) {
+      const int64_t r0 = (int64_t)qb * Bq, r1 = std::min<int64_t>(Lq, r0 + Bq) - 1;
+      const bool rows_whole = (r0 + Bq) <= Lq;
+      const int64_t p0 = r0 + off, p1 = r1 + off;
+      Range kr[3];
+      int n = block_key_ranges(band, sink, near_w, p0, p1, kr);
+      // key ranges -> k-block ranges, merged in ascending order
+      Range br[3];
+      for (int k = 0; k < n; ++k) {
+        int64_t a = std::max<int64_t>(0, kr[k].a), b = std::min<int64_t>(Lk, kr[k].b);
+        br[k] = (b > a) ? Range{a / Bk, (b - 1) / Bk + 1} : Range{0, 0};
+      }
+      std::sort(br, br + n, [](const Range& x, const Range& y) { return x.a < y.a; });
+      int64_t end = 0;
+      int32_t cnt = 0;
+      for (int k = 0; k < n; ++k) {
+        for (int64_t kb = std::max(br[k].a, end); kb < br[k].b; ++kb) {
+          ++visited;
+          const int64_t j0 = kb * Bk, j1 = std::min<int64_t>(Lk, j0 + Bk) - 1;
+          const bool keys_whole = (j0 + Bk) <= Lk;
+          const bool full = rows_whole && keys_whole && tile_full(band, sink, near_w, p0, p1, j0, j1);
+          n_partial += full ? 0 : 1;
+          ++cnt;
+          if (want) {
+            ents.push_back((int32_t)((kb << 1) | (full ? 0 : 1)));
+            ++col_cnt[(size_t)h * nkb + kb];
+          }
+        }
+        end = std::max(end, br[k].b);
+      }
+      row_cnt[(size_t)h * nqb + qb] = cnt;
+      nnz += cnt;
+      if (nnz > INT32_MAX) return COWA_ERR_UNSUPPORTED;
+      if (want) row_ptr[(size_t)h * nqb + qb + 1] = (int32_t)nnz;
+    }
+  }
+
+  info->Lq = Lq;
+  info->Lk = Lk;
+  info->Hkv = Hkv;
+  info->Bq = Bq;
+  info->Bk = Bk;
+  info->nqb = nqb;
+  info->nkb = nkb;
+  info->nnz = nnz;
+  info->n_partial = n_partial;
+  info->visited = visited;
+  info->edges = edges;
+  if (!want) return COWA_OK;
+
+  std::memcpy(row_ent, ents.data(), sizeof(int32_t) * (size_t)nnz);
+
+  // Column lists: transpose, keeping q-blocks ascending within a column.
+  col_ptr[0] = 0;
+  for (size_t c = 0; c < col_cnt.size(); ++c) col_ptr[c + 1] = col_ptr[c] + col_cnt[c];
+  std::vector<int32_t> fill(col_ptr, col_ptr + col_cnt.size());
+  for (int32_t h = 0; h < Hkv; ++h)
+    for (int32_t qb = 0; qb < nqb; ++qb) {
+      const size_t it = (size_t)h * nqb + qb;
+      for (int32_t e = row_ptr[it]; e < row_ptr[it + 1]; ++e) {
+        const int32_t kb = COWA_ENT_BLOCK(row_ent[e]);
+        col_ent[fill[(size_t)h * nkb + kb]++] = (qb << 1) | COWA_ENT_PARTIAL(row_ent[e]);
+      }
+    }
+
+  // Longest-processing-time-first work orders (ties: smaller item id first).
+  auto lpt = [](const std::vector<int32_t>& cnt, int32_t* order) {
+    std::iota(order, order + cnt.size(), 0);
+    std::stable_sort(order, order + cnt.size(),
+                     [&](int32_t x, int32_t y) { return cnt[x] > cnt[y]; });
+  };
+  lpt(row_cnt, row_order);
+  lpt(col_cnt, col_order);
+  return COWA_OK;
+}

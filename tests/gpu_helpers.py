@@ -1,0 +1,40 @@
+"""Helpers for the GPU parity tests: error metrics and stratified row samples."""
+
+import numpy as np
+import torch
+
+BF16_MAX_ABS = 2e-2   # bf16 outputs and gradients: max-abs and relative-L2 bars
+BF16_REL_L2 = 1e-2
+F32_MAX_ABS = 1e-4    # fp32 forward
+
+
+def errors(got, want):
+    g = got.detach().to("cpu", torch.float64).numpy() if hasattr(got, "detach") else np.asarray(got, np.float64)
+    w = np.asarray(want, dtype=np.float64)
+    assert g.shape == w.shape, (g.shape, w.shape)
+    fin = np.isfinite(w)
+    assert np.array_equal(fin, np.isfinite(g)), "non-finite pattern differs"
+    d = np.abs(g[fin] - w[fin])
+    max_abs = float(d.max()) if d.size else 0.0
+    nrm = float(np.linalg.norm(w[fin]))
+    rel = float(np.linalg.norm(g[fin] - w[fin]) / nrm) if nrm > 0 else 0.0
+    return max_abs, rel
+
+
+def assert_bf16_close(name, got, want):
+    max_abs, rel = errors(got, want)
+    print(f"  {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+    assert max_abs <= BF16_MAX_ABS, f"{name}: max_abs {max_abs}"
+    assert rel <= BF16_REL_L2, f"{name}: rel_l2 {rel}"
+
+
+def sample_rows(L, sink, near, lr, Hkv, Bq, n, seed):
+    """Mandatory boundary rows (tile, sink, near and band edges, first/last) plus seeded
+    random rows, sorted and unique."""
+    must = {0, 1, Bq - 1, Bq, sink - 1, sink, near - 1, near, L - 1}
+    for h in range(1, Hkv):
+        must |= {near + h * lr - 1, near + h * lr}
+    must = {r for r in must if 0 <= r < L}
+    rng = np.random.default_rng(seed)
+    extra = rng.choice(L, size=max(0, n - len(must)), replace=False)
+    return np.array(sorted(must | set(int(x) for x in extra)), dtype=np.int64)

@@ -1,0 +1,134 @@
+"""Host planner (cowa_plan_blocks) against the oracle's explicit mask — bit-exact tile
+lists, FULL/PARTIAL flags, column lists, work orders and counters.  CPU only."""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(__file__))
+import oracle  # noqa: E402
+from interval_count import head_edges  # noqa: E402
+
+api = pytest.importorskip("structured_sparse_attention_plan_amd.api")
+
+
+def _lib_lists(plan, Hkv):
+    a = plan.arrays
+    nqb, nkb = plan.info.nqb, plan.info.nkb
+    rows = [[[(int(e) >> 1, not (int(e) & 1)) for e in a["row_ent"][a["row_ptr"][h * nqb + qb]:
+                                                                  a["row_ptr"][h * nqb + qb + 1]]]
+             for qb in range(nqb)] for h in range(Hkv)]
+    cols = [[[(int(e) >> 1, not (int(e) & 1)) for e in a["col_ent"][a["col_ptr"][h * nkb + kb]:
+                                                                  a["col_ptr"][h * nkb + kb + 1]]]
+             for kb in range(nkb)] for h in range(Hkv)]
+    return rows, cols
+
+
+CASES = [
+    # (Lq, Lk, Hkv, Bq, Bk, sink, near, gap, mode)
+    (1024, 1024, 2, 64, 64, 64, 128, 0, "complementary"),
+    (1024, 1024, 2, 64, 64, 64, 128, 0, "duplicated"),
+    (1024, 1024, 2, 64, 64, 64, 128, 0, "dense"),
+    (1000, 1000, 8, 51, 64, 16, 100, 0, "complementary"),
+    (777, 1500, 4, 25, 128, 7, 33, 5, "complementary"),
+    (300, 300, 3, 64, 32, 0, 1, 0, "complementary"),
+    (1, 4096, 8, 1, 64, 128, 256, 0, "complementary"),
+    (1, 5000, 8, 1, 64, 100, 300, 0, "duplicated"),
+    (2048, 2048, 8, 25, 128, 128, 512, 0, "complementary"),
+    (130, 130, 2, 64, 64, 200, 0, 0, "complementary"),
+    (500, 200, 2, 64, 64, 3, 10, 0, "complementary"),  # Lq > Lk: early rows see nothing
+]
+
+
+@pytest.mark.parametrize("Lq,Lk,Hkv,Bq,Bk,sink,near,gap,mode", CASES)
+def test_plan_matches_oracle_mask(Lq, Lk, Hkv, Bq, Bk, sink, near, gap, mode):
+    owin = oracle.Window.for_length(max(Lk, 1), Hkv, sink, near, gap, mode=mode)
+    win = api.window(owin.sink, owin.near, owin.gap, owin.lr, mode)
+    plan = api.plan_blocks(Lq, Lk, Hkv, Bq, Bk, win)
+    want = oracle.tile_lists(Lq, Lk, Hkv, Bq, Bk, owin)
+    rows, cols = _lib_lists(plan, Hkv)
+    assert rows == want
+    # column lists are the transpose, q-blocks ascending
+    nkb = plan.info.nkb
+    for h in range(Hkv):
+        tr = [[] for _ in range(nkb)]
+        for qb, ent in enumerate(want[h]):
+            for kb, full in ent:
+                tr[kb].append((qb, full))
+        assert cols[h] == tr
+    info = plan.info
+    nnz = sum(len(e) for hl in want for e in hl)
+    assert info.nnz == nnz and info.visited == nnz
+    assert info.n_partial == sum(1 for hl in want for e in hl for _, f in e if not f)
+    assert info.edges == sum(oracle.edge_counts(Lq, Lk, Hkv, owin))
+    # longest-first work orders
+    a = plan.arrays
+    rl = np.diff(a["row_ptr"])
+    assert sorted(a["row_order"].tolist()) == list(range(len(rl)))
+    assert all(rl[a["row_order"][i]] >= rl[a["row_order"][i + 1]] for i in range(len(rl) - 1))
+    cl = np.diff(a["col_ptr"])
+    assert sorted(a["col_order"].tolist()) == list(range(len(cl)))
+    assert all(cl[a["col_order"][i]] >= cl[a["col_order"][i + 1]] for i in range(len(cl) - 1))
+
+
+def test_info_only_call_matches_full_call():
+    win = api.make_window(4096, 8, 128, 512)
+    info = api.plan_info(4096, 4096, 8, 51, 64, win)
+    full = api.plan_blocks(4096, 4096, 8, 51, 64, win)
+    for f in ("nqb", "nkb", "nnz", "n_partial", "visited", "edges"):
+        assert getattr(info, f) == getattr(full.info, f)
+
+
+@pytest.mark.parametrize("L,sink,near,Bq,Bk,tiles,partial", [
+    # tile counts at the 32K and 128K workloads with 128x128 tiles (also derivable by hand
+    # from the band edges; listed in the design notes)
+    (32768, 128, 2048, 128, 128, 64914, 5387),
+    (131072, 128, 4096, 128, 128, 768050, 22059),
+])
+def test_large_tile_counts(L, sink, near, Bq, Bk, tiles, partial):
+    win = api.make_window(L, 8, sink, near)
+    info = api.plan_info(L, L, 8, Bq, Bk, win)
+    assert info.nnz == tiles and info.n_partial == partial and info.visited == tiles
+
+
+@pytest.mark.parametrize("L,sink,near", [(32768, 128, 2048), (131072, 128, 4096)])
+@pytest.mark.parametrize("mode", ["complementary", "duplicated", "dense"])
+def test_large_edge_counts_match_interval_count(L, sink, near, mode):
+    win = api.make_window(L, 8, sink, near, 0, mode)
+    info = api.plan_info(L, L, 8, 64, 64, win)
+    assert info.edges == sum(head_edges(L, L, 8, sink, near, 0, win.lr, mode))
+
+
+def test_decode_plan_reads_only_visible_blocks():
+    # 131072-token cache, query at the last position: per head sink + near + band blocks
+    win = api.make_window(131072, 8, 128, 4096)
+    plan = api.plan_blocks(1, 131072, 8, 1, 64, win)
+    rl = np.diff(plan.arrays["row_ptr"])
+    # blocks of 64: sink 2 + band 248 + near 64; head 7's band [0, 15872) holds the sink
+    assert rl.tolist() == [314] * 7 + [312]
+    owin = oracle.Window.for_length(131072, 8, 128, 4096)
+    want = oracle.tile_lists(1, 131072, 8, 1, 64, owin)
+    assert rl.tolist() == [len(want[h][0]) for h in range(8)]
+    assert plan.info.edges == 7 * 20096 + 19968
+
+
+def test_planner_rejects_bad_arguments():
+    from structured_sparse_attention_plan_amd import _cowa as C
+    import ctypes
+    win = api.window(1, 2, 0, 3)
+    info = C.cowa_plan_info()
+    assert C.lib.cowa_plan_blocks(0, 10, 1, 8, 8, ctypes.byref(win), ctypes.byref(info),
+                                  None, None, None, None, None, None) == C.COWA_ERR_INVALID_ARG
+    bad = api.window(-1, 2, 0, 3)
+    assert C.lib.cowa_plan_blocks(10, 10, 1, 8, 8, ctypes.byref(bad), ctypes.byref(info),
+                                  None, None, None, None, None, None) == C.COWA_ERR_INVALID_ARG
+    arr = (ctypes.c_int32 * 16)()
+    # some but not all output arrays
+    assert C.lib.cowa_plan_blocks(10, 10, 1, 8, 8, ctypes.byref(win), ctypes.byref(info),
+                                  arr, None, None, None, None, None) == C.COWA_ERR_INVALID_ARG
+    w = C.cowa_window()
+    assert C.lib.cowa_window_make(100, 0, 1, 2, 0, 0, ctypes.byref(w)) == C.COWA_ERR_INVALID_ARG
+    assert C.lib.cowa_window_make(131072, 8, 128, 4096, 0, 0, ctypes.byref(w)) == C.COWA_OK
+    assert (w.sink, w.near_w, w.gap, w.lr, w.band_mode) == (128, 4096, 0, 15872, 0)
