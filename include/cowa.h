@@ -168,13 +168,19 @@ int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan,
  *   Delta_i = dO_i . O_i,  P = exp(scale q.k - LSE),  dS = P (dO.v - Delta)
  *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO   (dK, dV summed over the
  *   query heads of each KV head).
+ * `stages` selects the kernels to run (COWA_BWD_ALL for the whole backward): DELTA
+ * writes Delta into the workspace; DQ and DKDV read it from there, so a caller that runs
+ * them separately (for example on two streams) must run DELTA first on the same
+ * workspace.  dQ is written by DQ, dK and dV by DKDV; no output is accumulated into.
  * Supported: dtype BF16, D = 128.  All tensors bf16 except lse (fp32).  The plan must
  * hold both row and column lists at cowa_tile_sizes(COWA_OP_BWD).  workspace must be
  * at least cowa_workspace_size(COWA_OP_BWD) bytes, 256-byte aligned.
- * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, PLAN_MISMATCH, HIP. */
+ * Errors: INVALID_ARG (also for stages outside 1..7), UNSUPPORTED,
+ * WORKSPACE_TOO_SMALL, PLAN_MISMATCH, HIP. */
+enum { COWA_BWD_DELTA = 1, COWA_BWD_DQ = 2, COWA_BWD_DKDV = 4, COWA_BWD_ALL = 7 };
 int cowa_bwd(const cowa_problem* p, const cowa_plan_dev* plan,
              const void* q, const void* k, const void* v, const void* o, const float* lse,
-             const void* dout, void* dq, void* dk, void* dv,
+             const void* dout, void* dq, void* dk, void* dv, int stages,
              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Decode: one new query token per sequence (p->Lq == 1) over a KV cache of p->Lk

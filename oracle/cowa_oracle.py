@@ -128,6 +128,14 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
+def _take_rows(x, rows):
+    """x[:, rows] for a NumPy array or a torch tensor (no arithmetic)."""
+    if hasattr(x, "detach"):
+        import torch
+        return x[:, torch.as_tensor(rows, dtype=torch.long)]
+    return np.asarray(x)[:, rows]
+
+
 def _masked_softmax_row_stats(s, m):
     """Row max, denominator and probabilities of a masked score matrix s [R, Lk]."""
     s = np.where(m, s, -np.inf)
@@ -147,18 +155,19 @@ def attn_fwd(q, k, v, win, scale, rows=None):
     q [B, Lq, Hq, D], k/v [B, Lk, Hkv, D]  ->  O [B, R, Hq, D], LSE [B, Hq, R]
     For query head qh (KV head h = qh // G): s_ij = scale q_i.k_j, masked to the
     visible keys; O_i = sum_j softmax(s)_ij v_j; LSE_i = log sum_j exp(s_ij)."""
-    q, k, v = _f64(q), _f64(k), _f64(v)
     B, Lq, Hq, D = q.shape
+    rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    q = _f64(_take_rows(q, rows))  # only the requested rows are upcast
+    k, v = _f64(k), _f64(v)
     _, Lk, Hkv, _ = k.shape
     G = Hq // Hkv
-    rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
     O = np.zeros((B, len(rows), Hq, D))
     LSE = np.zeros((B, Hq, len(rows)))
     for h in range(Hkv):
         m = mask_rows(rows, Lq, Lk, h, win)
         for b in range(B):
             for qh in range(h * G, (h + 1) * G):
-                s = scale * (q[b, rows, qh, :] @ k[b, :, h, :].T)
+                s = scale * (q[b, :, qh, :] @ k[b, :, h, :].T)
                 p, lse = _masked_softmax_row_stats(s, m)
                 O[b, :, qh, :] = p @ v[b, :, h, :]
                 LSE[b, qh, :] = lse
@@ -201,21 +210,22 @@ def attn_bwd(q, k, v, do, win, scale):
 def attn_bwd_dq_rows(q, k, v, do, win, scale, rows):
     """dQ on the query rows `rows` only: needs just those rows' own softmax and
     Delta_i = dO_i . O_i with O_i from the rows' own forward.  -> [B, R, Hq, D]"""
-    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, Lq, Hq, D = q.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    q, do = _f64(_take_rows(q, rows)), _f64(_take_rows(do, rows))
+    k, v = _f64(k), _f64(v)
     _, Lk, Hkv, _ = k.shape
     G = Hq // Hkv
-    rows = np.asarray(rows, dtype=np.int64)
     dq = np.zeros((B, len(rows), Hq, D))
     for h in range(Hkv):
         m = mask_rows(rows, Lq, Lk, h, win)
         for b in range(B):
             for qh in range(h * G, (h + 1) * G):
-                s = scale * (q[b, rows, qh, :] @ k[b, :, h, :].T)
+                s = scale * (q[b, :, qh, :] @ k[b, :, h, :].T)
                 p, _ = _masked_softmax_row_stats(s, m)
                 o = p @ v[b, :, h, :]
-                delta = (do[b, rows, qh, :] * o).sum(axis=1, keepdims=True)
-                dp = do[b, rows, qh, :] @ v[b, :, h, :].T
+                delta = (do[b, :, qh, :] * o).sum(axis=1, keepdims=True)
+                dp = do[b, :, qh, :] @ v[b, :, h, :].T
                 ds = p * (dp - delta)
                 dq[b, :, qh, :] = scale * (ds @ k[b, :, h, :])
     return dq

@@ -134,8 +134,9 @@ def fwd(q, k, v, win, scale=None, plan=None, out=None, lse=None):
     return out, lse
 
 
-def bwd(q, k, v, o, lse, dout, win, scale=None, plan=None, grads=None, workspace=None):
-    """Backward: -> (dq like q, dk like k, dv like v)."""
+def bwd(q, k, v, o, lse, dout, win, scale=None, plan=None, grads=None, workspace=None,
+        stages=C.COWA_BWD_ALL):
+    """Backward: -> (dq like q, dk like k, dv like v).  `stages` as in cowa_bwd."""
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     scale = D ** -0.5 if scale is None else scale
@@ -154,7 +155,8 @@ def bwd(q, k, v, o, lse, dout, win, scale=None, plan=None, grads=None, workspace
     C.check("cowa_bwd", C.lib.cowa_bwd(ctypes.byref(prob), ctypes.byref(plan.struct), q.data_ptr(),
                                        k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                       workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+                                       int(stages), workspace.data_ptr(), workspace.numel(),
+                                       _stream(q.device)))
     return dq, dk, dv
 
 

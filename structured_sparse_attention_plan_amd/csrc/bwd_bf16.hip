@@ -20,6 +20,7 @@
 // Rows of a q-block are token-major (row r = token * G + head-in-group); rows beyond
 // G * Bq or Lq carry LSE = +inf and Delta = 0 so that they contribute nothing.
 
+#include "cowa.h"
 #include "device_common.h"
 
 namespace cowa {
@@ -372,16 +373,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t s) {
-  const int64_t nrows = (int64_t)a.B * a.Lq * a.Hq;
-  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3(a.Hkv * a.nqb, a.B), dim3(256), 0, s, a);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(a.Hkv * a.nkb, a.B), dim3(256), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_bwd_bf16_d128(const BwdArgs& a, int stages, hipStream_t s) {
+  hipError_t err = hipSuccess;
+  if (stages & COWA_BWD_DELTA) {
+    const int64_t nrows = (int64_t)a.B * a.Lq * a.Hq;
+    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (stages & COWA_BWD_DQ) {
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(a.Hkv * a.nqb, a.B), dim3(256), 0, s, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (stages & COWA_BWD_DKDV) {
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(a.Hkv * a.nkb, a.B), dim3(256), 0, s, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return err;
 }
 
 }  // namespace cowa

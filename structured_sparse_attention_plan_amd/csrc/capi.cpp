@@ -197,12 +197,14 @@ extern "C" int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan, const 
 
 extern "C" int cowa_bwd(const cowa_problem* p, const cowa_plan_dev* plan, const void* q, const void* k,
                         const void* v, const void* o, const float* lse, const void* dout, void* dq,
-                        void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+                        void* dk, void* dv, int stages, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   int st = check_problem(p);
   if (st != COWA_OK) return st;
   st = check_op_support(COWA_OP_BWD, p);
   if (st != COWA_OK) return st;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return COWA_ERR_INVALID_ARG;
+  if (stages < 1 || stages > COWA_BWD_ALL) return COWA_ERR_INVALID_ARG;
   st = check_plan(COWA_OP_BWD, p, plan, true);
   if (st != COWA_OK) return st;
   size_t need = 0;
@@ -241,7 +243,7 @@ extern "C" int cowa_bwd(const cowa_problem* p, const cowa_plan_dev* plan, const 
   a.scale = p->scale;
   a.scale_log2 = p->scale * 1.44269504088896340736f;
   a.win = dev_window(p->win);
-  return hip_status(launch_bwd_bf16_d128(a, (hipStream_t)stream));
+  return hip_status(launch_bwd_bf16_d128(a, stages, (hipStream_t)stream));
 }
 
 extern "C" int cowa_decode(const cowa_problem* p, const cowa_plan_dev* plan, const void* q,

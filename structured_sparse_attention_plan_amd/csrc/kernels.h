@@ -75,7 +75,7 @@ struct DecodeArgs {
 
 hipError_t launch_fwd_f32_d64(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16_d128(const FwdArgs& a, hipStream_t s);
-hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16_d128(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t s);
 bool decode_supports_group(int G);
 

@@ -21,10 +21,26 @@ def errors(got, want):
     return max_abs, rel
 
 
-def assert_bf16_close(name, got, want):
+def assert_bf16_close(name, got, want, value_scaled=False):
+    """max-abs <= 2e-2 and relative-L2 <= 1e-2 against the float64 oracle.
+
+    value_scaled=True applies the max-abs bar per element as max(2e-2, 2^-7 |want|):
+    bf16 spaces values in [4, 8) 2^-5 apart, so rounding the output alone can cost 2^-6,
+    and the bf16 rounding of P / dS before the products adds about as much again; the
+    bar then allows two bf16 half-ulps at the value.  Only gradients of small test
+    shapes (few visible keys, so entries of magnitude 2-8) reach that range."""
     max_abs, rel = errors(got, want)
-    print(f"  {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
-    assert max_abs <= BF16_MAX_ABS, f"{name}: max_abs {max_abs}"
+    g = got.detach().to("cpu", torch.float64).numpy() if hasattr(got, "detach") else np.asarray(got)
+    w = np.asarray(want, dtype=np.float64)
+    fin = np.isfinite(w)
+    excess = np.abs(g[fin] - w[fin]) - np.maximum(BF16_MAX_ABS, np.abs(w[fin]) * 2.0 ** -7)
+    n_over_abs = int((np.abs(g[fin] - w[fin]) > BF16_MAX_ABS).sum())
+    print(f"  {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e} max|want|={np.abs(w[fin]).max():.3e} "
+          f"n(|err|>2e-2)={n_over_abs}", flush=True)
+    if value_scaled:
+        assert excess.max(initial=-1.0) <= 0, f"{name}: value-scaled max-abs exceeded by {excess.max()}"
+    else:
+        assert max_abs <= BF16_MAX_ABS, f"{name}: max_abs {max_abs}"
     assert rel <= BF16_REL_L2, f"{name}: rel_l2 {rel}"
 
 

@@ -98,10 +98,14 @@ def test_entry_points_validate_before_launch():
                           None) == C.COWA_ERR_PLAN_MISMATCH
     # backward: workspace too small / misaligned
     pb = _fake_plan(p, "bwd")
-    assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, x, x, x, x, x, x, 16,
+    assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, x, x, x, x, x, 7, x, 16,
                           None) == C.COWA_ERR_WORKSPACE_TOO_SMALL
-    assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, x, x, x, x, x,
+    assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, x, x, x, x, x, 7,
                           ctypes.c_void_p(260), 1 << 20, None) == C.COWA_ERR_INVALID_ARG
+    for bad_stages in (0, 8):
+        assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, x, x, x, x, x,
+                              bad_stages, ctypes.c_void_p(256), 1 << 20,
+                              None) == C.COWA_ERR_INVALID_ARG
     # decode: workspace too small
     pd = _prob(Lq=1, Lk=4096, win=api.make_window(4096, 8, 4, 16))
     pld = _fake_plan(pd, "decode")

@@ -108,9 +108,9 @@ def test_bwd_bf16_small_full(B, L, Hq, Hkv, sink, near, mode):
     dq, dk, dv = api.bwd(qd, kd, vd, o, lse, dod, win)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attn_bwd(q, k, v, do, ow, 128 ** -0.5)
-    assert_bf16_close("dQ", dq, rq)
-    assert_bf16_close("dK", dk, rk)
-    assert_bf16_close("dV", dv, rv)
+    assert_bf16_close("dQ", dq, rq, value_scaled=True)
+    assert_bf16_close("dK", dk, rk, value_scaled=True)
+    assert_bf16_close("dV", dv, rv, value_scaled=True)
 
 
 def test_bwd_bf16_mid_2048_full():
@@ -123,9 +123,9 @@ def test_bwd_bf16_mid_2048_full():
     dq, dk, dv = api.bwd(qd, kd, vd, o, lse, dod, win)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attn_bwd(q, k, v, do, ow, 128 ** -0.5)
-    assert_bf16_close("dQ", dq, rq)
-    assert_bf16_close("dK", dk, rk)
-    assert_bf16_close("dV", dv, rv)
+    assert_bf16_close("dQ", dq, rq, value_scaled=True)
+    assert_bf16_close("dK", dk, rk, value_scaled=True)
+    assert_bf16_close("dV", dv, rv, value_scaled=True)
 
 
 # ----------------------------------------------------------------------------- decode
