@@ -15,8 +15,8 @@
 //            visible q-blocks; each of the 4 waves keeps 32 keys of K and V in registers
 //            and accumulates dK, dV for them over all G query heads of the KV head:
 //            S = Q K^T and dP = dO V^T on MFMA, then dV += P^T dO and dK += dS^T Q with
-//            P, dS taken from the accumulator registers as A operands and dO, Q read
-//            transposed from LDS.
+//            P, dS taken from the accumulator registers as A operands (dS as a bf16
+//            hi + lo pair) and dO, Q read transposed from LDS.
 // Rows of a q-block are token-major (row r = token * G + head-in-group); rows beyond
 // G * Bq or Lq carry LSE = +inf and Delta = 0 so that they contribute nothing.
 
@@ -341,8 +341,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int hf = 0; hf < 2; ++hf) {
         const bf16x8 pa = join(to_bf16x4(pr[8 * hf], pr[8 * hf + 1], pr[8 * hf + 2], pr[8 * hf + 3]),
                                to_bf16x4(pr[8 * hf + 4], pr[8 * hf + 5], pr[8 * hf + 6], pr[8 * hf + 7]));
-        const bf16x8 sa = join(to_bf16x4(ds[8 * hf], ds[8 * hf + 1], ds[8 * hf + 2], ds[8 * hf + 3]),
-                               to_bf16x4(ds[8 * hf + 4], ds[8 * hf + 5], ds[8 * hf + 6], ds[8 * hf + 7]));
+        // dS as a bf16 pair hi + lo: the sum over rows in dK cancels strongly, so a single
+        // bf16 rounding of dS would dominate its error; hi + lo keeps ~16 mantissa bits
+        bf16x8 sa, sl;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const __bf16 hi = (__bf16)ds[8 * hf + x];
+          sa[x] = hi;
+          sl[x] = (__bf16)(ds[8 * hf + x] - (float)hi);
+        }
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int ro = (32 * rb + 16 * hf + vrow) * PITCH + 32 * db + vcol;
@@ -350,6 +357,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           const bf16x8 qt = join(lds_read_tr4(sQ + ro), lds_read_tr4(sQ + ro + 8 * PITCH));
           accV[db] = mfma32x32x16(pa, dt, accV[db]);
           accK[db] = mfma32x32x16(sa, qt, accK[db]);
+          accK[db] = mfma32x32x16(sl, qt, accK[db]);
         }
       }
     }

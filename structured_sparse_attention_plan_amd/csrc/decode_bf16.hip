@@ -162,21 +162,35 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
+// One work group per (sequence, query head): lane s of the first wave reads split s's
+// (max, sum), the weights exp2(m_s - M) go through LDS, and thread d merges dim d.
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+  __shared__ float w[64];
+  __shared__ float tot[2];
   const int bh = blockIdx.x;  // b * Hq + hq
   const int d = threadIdx.x;
   const int64_t base = (int64_t)bh * a.nsplit;
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * (base + s)]);
-  float L = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ms = a.part_ml[2 * (base + s)];
-      const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      L += w * a.part_ml[2 * (base + s) + 1];
-      acc += w * a.part[(base + s) * D + d];
+  if (d < 64) {
+    const bool in = d < a.nsplit;
+    const float ms = in ? a.part_ml[2 * (base + d)] : -INFINITY;
+    const float ls = in ? a.part_ml[2 * (base + d) + 1] : 0.f;
+    float M = ms;
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+    const float wt = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    float L = wt * ls;
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) L += __shfl_xor(L, x);
+    w[d] = wt;
+    if (d == 0) {
+      tot[0] = M;
+      tot[1] = L;
     }
   }
+  __syncthreads();
+  const float M = tot[0], L = tot[1];
+  float acc = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) acc += w[s] * a.part[(base + s) * D + d];
   const float out = L > 0.f ? acc / L : 0.f;
   ((__bf16*)a.o)[(int64_t)bh * D + d] = (__bf16)out;
   if (a.lse && d == 0) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
