@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
       for (int i = 0; i < 16; ++i) {
         const int j = jb + 32 * k2 + 8 * (i >> 2) + 4 * h2 + (i & 3);
         float pr = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
-        if (partial && !(rvalid && visible(p, j, a.Lk, a.win.sink, a.win.near_w, band))) pr = 0.f;
+        if (partial) pr = (rvalid & visible(p, j, a.Lk, a.win.sink, a.win.near_w, band)) ? pr : 0.f;
         ds[i] = pr * (dp[i] - dlt);
       }
 #pragma unroll
@@ -331,8 +331,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x = __builtin_amdgcn_exp2f(fmaf(s[4 * i4 + i], a.scale_log2, -l4[i]));
-          if (partial && !(kvalid && visible(sTok[rr + i] + off, j, a.Lk, a.win.sink, a.win.near_w, band)))
-            x = 0.f;
+          if (partial)
+            x = (kvalid & visible(sTok[rr + i] + off, j, a.Lk, a.win.sink, a.win.near_w, band)) ? x : 0.f;
           pr[4 * i4 + i] = x;
           ds[4 * i4 + i] = x * (dp[4 * i4 + i] - t4[i]);
         }

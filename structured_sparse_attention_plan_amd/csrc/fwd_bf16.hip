@@ -44,6 +44,18 @@ constexpr int KB2 = BK / 32;         // 2 key blocks of 32
 constexpr int PITCH = D + 16;        // LDS row pitch in elements (288 bytes)
 constexpr float kRescaleThreshold = 8.0f;
 
+// x * alpha for a value held in an accumulation register, done in place: read to a VGPR,
+// multiply, write back.  Only used on the rare rescale path, long after the MFMA that
+// last wrote the register (a whole tile of LDS reads and MFMAs lies in between).
+__device__ __forceinline__ float agpr_scale(float x, float alpha) {
+  float t;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(t) : "a"(x));
+  t *= alpha;
+  float r;
+  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(r) : "v"(t));
+  return r;
+}
+
 __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 sQ[ROWS * PITCH];
   __shared__ __attribute__((aligned(16))) __bf16 sK[BK * PITCH];
@@ -135,8 +147,15 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   const int vrow = 4 * (gg >> 1) + (j16 >> 2);
   const int vcol = 16 * (gg & 1) + 4 * (j16 & 3);
 
-  for (int e = e0; e < e1; ++e) {
-    const int ent = a.row_ent[e];
+  // A rescale of the output accumulators (rare: only when a row's tile max exceeds its
+  // reference by more than the threshold) reads, scales and writes each accumulator
+  // register in place (agpr_scale), so the accumulators stay resident in AGPRs; scaling
+  // them with ordinary VALU code makes the compiler copy all 128 of them every tile.
+  f32x16 s[KB2][CB];
+  float mt[CB];
+  int e = e0;
+  auto stage_and_scores = [&](int ee) {
+    const int ent = a.row_ent[ee];
     const int kb = ent >> 1;
     const bool partial = ent & 1;
     __syncthreads();
@@ -148,10 +167,9 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
       *(u32x4*)(sV + row * PITCH + 8 * cc) = pv[u];
     }
     __syncthreads();
-    if (e + 1 < e1) fetch(e + 1);
+    if (ee + 1 < e1) fetch(ee + 1);
 
     // ---- S^T = K Q^T
-    f32x16 s[KB2][CB];
 #pragma unroll
     for (int k2 = 0; k2 < KB2; ++k2)
 #pragma unroll
@@ -171,7 +189,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
       }
     }
 
-    // ---- mask boundary tiles
+    // ---- mask boundary tiles (branch-free per element)
     if (partial) {
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
@@ -181,14 +199,13 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int j = kb * BK + 32 * k2 + 8 * (i >> 2) + 4 * h2 + (i & 3);
-            if (!(rvalid[c] && visible(p, j, a.Lk, a.win.sink, a.win.near_w, band)))
-              s[k2][c][i] = -INFINITY;
+            const bool vis = rvalid[c] & visible(p, j, a.Lk, a.win.sink, a.win.near_w, band);
+            s[k2][c][i] = vis ? s[k2][c][i] : -INFINITY;
           }
       }
     }
 
-    // ---- online softmax (base 2)
-    float mt[CB];
+    // ---- tile max per row, across the two lane halves of a column
     bool need = false;
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
@@ -201,19 +218,13 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
       mt[c] = x * a.scale_log2;
       need |= mt[c] > m[c] + kRescaleThreshold;
     }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const float mn = fmaxf(m[c], mt[c]);
-        const float alpha = (m[c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[c] - mn);
-        m[c] = mn;
-        l[c] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) acc[c][db] *= alpha;
-      }
-    }
-    // P as bf16 B operands: pf[k2][c][hf] holds keys 32 k2 + 16 hf + {4 h2 .. +3,
-    // 8 + 4 h2 .. +3}, i.e. accumulator elements 8 hf .. 8 hf + 7
+    return __builtin_amdgcn_ballot_w64(need) != 0;
+  };
+
+  // P = exp2(scale log2e S - m) as bf16 B operands, row sums into l, then O^T += V^T P^T.
+  // pf[k2][c][hf] holds keys 32 k2 + 16 hf + {4 h2 .. +3, 8 + 4 h2 .. +3}, i.e.
+  // accumulator elements 8 hf .. 8 hf + 7.
+  auto accumulate = [&]() {
     bf16x8 pf[KB2][CB][2];
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
@@ -233,8 +244,6 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
         }
       l[c] += sum;
     }
-
-    // ---- O^T += V^T P^T
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -248,6 +257,23 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
         }
       }
     }
+  };
+
+  for (; e < e1; ++e) {
+    if (stage_and_scores(e)) {
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const float mn = fmaxf(m[c], mt[c]);
+        const float alpha = (m[c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[c] - mn);
+        m[c] = mn;
+        l[c] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[c][db][i] = agpr_scale(acc[c][db][i], alpha);
+      }
+    }
+    accumulate();
   }
 
   // ---- finalize: l summed over the two lane halves of a column
