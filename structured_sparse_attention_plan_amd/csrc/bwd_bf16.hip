@@ -168,14 +168,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
         s = mfma32x32x16(kf, qf[dd], s);
         dp = mfma32x32x16(vf, df[dd], dp);
       }
-      float ds[16];
+      float pr[16], ds[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = jb + 32 * k2 + 8 * (i >> 2) + 4 * h2 + (i & 3);
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
-        if (partial) pr = (rvalid & visible(p, j, a.Lk, a.win.sink, a.win.near_w, band)) ? pr : 0.f;
-        ds[i] = pr * (dp[i] - dlt);
+      for (int i = 0; i < 16; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
+      if (partial) {  // one uniform branch; the predicate per element, branch-free
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = jb + 32 * k2 + 8 * (i >> 2) + 4 * h2 + (i & 3);
+          pr[i] = (rvalid & visible(p, j, a.Lk, a.win.sink, a.win.near_w, band)) ? pr[i] : 0.f;
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = pr[i] * (dp[i] - dlt);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const bf16x8 dsf = join(to_bf16x4(ds[8 * hf], ds[8 * hf + 1], ds[8 * hf + 2], ds[8 * hf + 3]),
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();
     if (e + 1 < e1) fetch(e + 1);
 
-#pragma unroll 1
+#pragma unroll
     for (int rb = 0; rb < ROWS / 32; ++rb) {
       f32x16 s, dp;
 #pragma unroll
@@ -327,15 +331,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int i4 = 0; i4 < 4; ++i4) {
         const int rr = 32 * rb + 8 * i4 + 4 * h2;
         const f32x4 l4 = *(const f32x4*)(sL + rr);
-        const f32x4 t4 = *(const f32x4*)(sT + rr);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = __builtin_amdgcn_exp2f(fmaf(s[4 * i4 + i], a.scale_log2, -l4[i]));
-          if (partial)
-            x = (kvalid & visible(sTok[rr + i] + off, j, a.Lk, a.win.sink, a.win.near_w, band)) ? x : 0.f;
-          pr[4 * i4 + i] = x;
-          ds[4 * i4 + i] = x * (dp[4 * i4 + i] - t4[i]);
+        for (int i = 0; i < 4; ++i)
+          pr[4 * i4 + i] = __builtin_amdgcn_exp2f(fmaf(s[4 * i4 + i], a.scale_log2, -l4[i]));
+      }
+      if (partial) {  // one uniform branch; the predicate per element, branch-free
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int rr = 32 * rb + 8 * i4 + 4 * h2;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool vis = kvalid & visible(sTok[rr + i] + off, j, a.Lk, a.win.sink, a.win.near_w, band);
+            pr[4 * i4 + i] = vis ? pr[4 * i4 + i] : 0.f;
+          }
         }
+      }
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 t4 = *(const f32x4*)(sT + 32 * rb + 8 * i4 + 4 * h2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ds[4 * i4 + i] = pr[4 * i4 + i] * (dp[4 * i4 + i] - t4[i]);
       }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
