@@ -15,7 +15,7 @@
 //            visible q-blocks; each of the 4 waves keeps 32 keys of K and V in registers
 //            and accumulates dK, dV for them over all G query heads of the KV head:
 //            S = Q K^T and dP = dO V^T on MFMA, then dV += P^T dO and dK += dS^T Q with
-//            P, dS taken from the accumulator registers as A operands (dS as a bf16
+//            P, dS taken from the accumulator registers as A operands (each as a bf16
 //            hi + lo pair) and dO, Q read transposed from LDS.
 // Rows of a q-block are token-major (row r = token * G + head-in-group); rows beyond
 // G * Bq or Lq carry LSE = +inf and Delta = 0 so that they contribute nothing.
@@ -156,18 +156,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
     if (sidx + 1 < n_sub) fetch(sidx + 1);
 
+    // S^T and dP^T for both 32-key halves first: four independent accumulation chains
+    f32x16 s2[SUB / 32], dp2[SUB / 32];
 #pragma unroll
-    for (int k2 = 0; k2 < SUB / 32; ++k2) {
-      f32x16 s, dp;
+    for (int k2 = 0; k2 < SUB / 32; ++k2)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+      for (int i = 0; i < 16; ++i) s2[k2][i] = dp2[k2][i] = 0.f;
 #pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
+    for (int dd = 0; dd < 8; ++dd)
+#pragma unroll
+      for (int k2 = 0; k2 < SUB / 32; ++k2) {
         const bf16x8 kf = load16(sK + (32 * k2 + n) * PITCH + 16 * dd + 8 * h2);
         const bf16x8 vf = load16(sV + (32 * k2 + n) * PITCH + 16 * dd + 8 * h2);
-        s = mfma32x32x16(kf, qf[dd], s);
-        dp = mfma32x32x16(vf, df[dd], dp);
+        s2[k2] = mfma32x32x16(kf, qf[dd], s2[k2]);
+        dp2[k2] = mfma32x32x16(vf, df[dd], dp2[k2]);
       }
+#pragma unroll
+    for (int k2 = 0; k2 < SUB / 32; ++k2) {
+      const f32x16& s = s2[k2];
+      const f32x16& dp = dp2[k2];
       float pr[16], ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
@@ -354,25 +361,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const bf16x8 pa = join(to_bf16x4(pr[8 * hf], pr[8 * hf + 1], pr[8 * hf + 2], pr[8 * hf + 3]),
-                               to_bf16x4(pr[8 * hf + 4], pr[8 * hf + 5], pr[8 * hf + 6], pr[8 * hf + 7]));
-        // dS as a bf16 pair hi + lo: the sum over rows in dK cancels strongly, so a single
-        // bf16 rounding of dS would dominate its error; hi + lo keeps ~16 mantissa bits
-        bf16x8 sa, sl;
+        // P and dS as bf16 pairs hi + lo (~16 mantissa bits): dV and dK sum them over many
+        // rows with strong cancellation, so a single bf16 rounding would dominate the error
+        bf16x8 pa, pl, sa, sl;
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
-          const __bf16 hi = (__bf16)ds[8 * hf + x];
-          sa[x] = hi;
-          sl[x] = (__bf16)(ds[8 * hf + x] - (float)hi);
+          const __bf16 ph = (__bf16)pr[8 * hf + x];
+          pa[x] = ph;
+          pl[x] = (__bf16)(pr[8 * hf + x] - (float)ph);
+          const __bf16 sh = (__bf16)ds[8 * hf + x];
+          sa[x] = sh;
+          sl[x] = (__bf16)(ds[8 * hf + x] - (float)sh);
         }
+        // hi products for all 4 column blocks, then the lo ones: an accumulator is next
+        // updated only after 7 independent MFMAs
+        bf16x8 dt[4], qt[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int ro = (32 * rb + 16 * hf + vrow) * PITCH + 32 * db + vcol;
-          const bf16x8 dt = join(lds_read_tr4(sD + ro), lds_read_tr4(sD + ro + 8 * PITCH));
-          const bf16x8 qt = join(lds_read_tr4(sQ + ro), lds_read_tr4(sQ + ro + 8 * PITCH));
-          accV[db] = mfma32x32x16(pa, dt, accV[db]);
-          accK[db] = mfma32x32x16(sa, qt, accK[db]);
-          accK[db] = mfma32x32x16(sl, qt, accK[db]);
+          dt[db] = join(lds_read_tr4(sD + ro), lds_read_tr4(sD + ro + 8 * PITCH));
+          qt[db] = join(lds_read_tr4(sQ + ro), lds_read_tr4(sQ + ro + 8 * PITCH));
+          accV[db] = mfma32x32x16(pa, dt[db], accV[db]);
+          accK[db] = mfma32x32x16(sa, qt[db], accK[db]);
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          accV[db] = mfma32x32x16(pl, dt[db], accV[db]);
+          accK[db] = mfma32x32x16(sl, qt[db], accK[db]);
         }
       }
     }

@@ -7,22 +7,28 @@
 // one strided run of G * 256 bytes per token.  Four waves own 64 rows each, as two
 // 32-column blocks of v_mfma_f32_32x32x16_bf16.
 //
-// Per visible k-block (64 keys, from the planner's row list; masked blocks are never
-// touched):
-//   1. the 256 threads stage K and V (64 x 128 bf16 each, row-major) in LDS; the next
-//      block's global loads are issued before this block's math;
-//   2. S^T = K Q^T: K from LDS (A operand, one key row per lane), Q^T from LDS (B
-//      operand; each wave stages its own 64 rows once per item), so each lane owns one
-//      query row (column) and 16 of every 32 keys;
-//   3. boundary (PARTIAL) blocks apply the window predicate element by element; FULL
-//      blocks skip it;
-//   4. online softmax in base 2 (scale * log2 e folded into one FMA), the row max taken
-//      across the two lane halves of a column; the running max only moves when a row's
-//      tile max exceeds it by more than 8 (log2 units): exact, because O / l does not
-//      depend on the reference, and P stays <= 256;
-//   5. O^T += V^T P^T: P^T goes from the C-layout accumulator straight into the B
-//      operand (no LDS round trip) and V^T is read from the row-major LDS tile with
-//      ds_read_b64_tr_b16, two 4-key runs per operand matching the accumulator layout.
+// The item walks the planner's row list of visible 64-key blocks (masked blocks are
+// never touched).  Per block t, in one pipelined loop iteration:
+//   [A] S(t+1)^T = K(t+1) Q^T on MFMA: K (A operand, one key row per lane) and Q^T (B
+//       operand) from LDS, so each lane owns one query row (column) and 16 of every 32
+//       keys; a boundary (PARTIAL) block gets the window predicate per element at the
+//       start of its own iteration;
+//   [B] online softmax of S(t) in base 2 (scale * log2 e folded into one FMA), the row
+//       max taken across the two lane halves of a column; the running max only moves
+//       when a row's tile max exceeds it by more than 8 (log2 units) — exact, because
+//       O / l does not depend on the reference, and P stays <= 256; P(t) is computed
+//       with the current reference and recomputed only on such a (rare) move;
+//   [C] O^T += V(t)^T P(t)^T: P^T goes from the C-layout accumulator straight into the B
+//       operand (no LDS round trip) and V^T is read from the row-major LDS tile with
+//       ds_read_b64_tr_b16, two 4-key runs per operand matching the accumulator layout.
+// [A] has no dependence on [B], so the scheduler overlaps the two (MFMA and VALU run
+// in parallel within a wave).
+//
+// Memory pipeline: K and V are double-buffered in LDS and filled by direct
+// global->LDS loads (global_load_lds_dwordx4, no staging registers); the loads of K(t+2)
+// and V(t+1) are issued right after the single barrier of iteration t and waited for at
+// the next one.  LDS rows are 256 bytes with the 16-byte chunks XOR-swizzled by a function
+// of the row, so the row-wise operand reads and the transposed V reads hit distinct banks.
 // Output: O / l in bf16 and LSE = ln 2 * (m + log2 l) in fp32.
 //
 // MFMA lane layouts of v_mfma_f32_32x32x16_bf16 (n = lane % 32, h2 = lane / 32):
@@ -41,8 +47,16 @@ constexpr int WROWS = ROWS / WAVES;  // 64 rows per wave
 constexpr int CB = WROWS / 32;       // 2 column blocks of 32 per wave
 constexpr int BK = kFwdBk;           // 64 keys per tile
 constexpr int KB2 = BK / 32;         // 2 key blocks of 32
-constexpr int PITCH = D + 16;        // LDS row pitch in elements (288 bytes)
+constexpr int TILE = BK * D;         // elements per K or V tile
 constexpr float kRescaleThreshold = 8.0f;
+
+// LDS rows are 256 bytes, so every row starts at bank 0; the 16-byte chunks of row r are
+// permuted by XOR with sw(r).  sw takes 16 distinct values over any 16 consecutive rows
+// (row-wise operand reads: one chunk of 16 rows) and maps 4 aligned rows x 2 adjacent
+// chunks to 8 distinct chunks (the transposed reads).
+__device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// Element offset of (row r, column e) in a swizzled 128-column LDS tile.
+__device__ __forceinline__ int swz(int r, int e) { return r * D + ((((e >> 3) ^ sw(r)) & 15) << 3) + (e & 7); }
 
 // x * alpha for a value held in an accumulation register, done in place: read to a VGPR,
 // multiply, write back.  Only used on the rare rescale path, long after the MFMA that
@@ -56,10 +70,20 @@ __device__ __forceinline__ float agpr_scale(float x, float alpha) {
   return r;
 }
 
+// One 1 KB direct global->LDS copy per wave: lane L moves 16 bytes to lds + 16 L.
+__device__ __forceinline__ void g2lds(const void* src, __bf16* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[ROWS * PITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 sK[BK * PITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[BK * PITCH];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ[ROWS * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV[2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -79,7 +103,6 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   const __bf16* K = (const __bf16*)a.k;
   const __bf16* V = (const __bf16*)a.v;
 
-  // ---- this wave's 64 query rows -> LDS
   int tok[CB], hq[CB];
   bool rvalid[CB];
 #pragma unroll
@@ -90,19 +113,37 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     hq[c] = h * G + (r - rt * G);
     rvalid[c] = (rt < Bq) && (tok[c] < a.Lq);
   }
-  __bf16* sQw = sQ + wave * WROWS * PITCH;
-#pragma unroll 4
-  for (int u = 0; u < WROWS * 16 / 64; ++u) {
-    const int id = lane + 64 * u;
-    const int row = id >> 4, cc = id & 15;
-    const int r = wave * WROWS + row;
-    const int rt = r / G;
-    const int t = qb * Bq + rt;
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (rt < Bq && t < a.Lq)
-      v = *(const u32x4*)(Q + (((int64_t)b * a.Lq + t) * a.Hq + h * G + (r - rt * G)) * D + 8 * cc);
-    *(u32x4*)(sQw + row * PITCH + 8 * cc) = v;
+
+  // ---- direct loads.  Lane L of a 1 KB copy fills row r = 4 * blk + L / 16, physical
+  // chunk L % 16, so it fetches logical chunk (L % 16) ^ sw(r) of that row.
+  const int lrow = lane >> 4;
+  const int lchunk = lane & 15;
+  {  // this wave's 64 query rows (rows past the q-block or Lq read a valid row; unused)
+    __bf16* dst = sQ + wave * WROWS * D;
+#pragma unroll
+    for (int u = 0; u < WROWS / 4; ++u) {
+      const int r = wave * WROWS + 4 * u + lrow;
+      const int rt = r / G;
+      int t = qb * Bq + rt;
+      int g = r - rt * G;
+      if (rt >= Bq || t >= a.Lq) {
+        t = min(qb * Bq, a.Lq - 1);
+        g = 0;
+      }
+      const int c = lchunk ^ sw(r);
+      g2lds(Q + (((int64_t)b * a.Lq + t) * a.Hq + h * G + g) * D + 8 * c, dst + 4 * u * D);
+    }
   }
+  auto load_tile = [&](const __bf16* src, __bf16* dst, int kb) {
+    // wave w copies rows 16 w .. 16 w + 15 (keys past Lk read key Lk - 1; masked)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = 16 * wave + 4 * u + lrow;
+      const int j = min(kb * BK + r, a.Lk - 1);
+      const int c = lchunk ^ sw(r);
+      g2lds(src + (((int64_t)b * a.Lk + j) * a.Hkv + h) * D + 8 * c, dst + (16 * wave + 4 * u) * D);
+    }
+  };
 
   f32x16 acc[CB][4];
 #pragma unroll
@@ -118,28 +159,9 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     l[c] = 0.f;
   }
 
-  // ---- K/V staging: thread tid moves 16-byte chunks tid + 256 u (u < 4): row id / 16,
-  // column chunk id % 16
-  const int e0 = a.row_ptr[item], e1 = a.row_ptr[item + 1];
-  u32x4 pk[4], pv[4];
-  auto fetch = [&](int e) {
-    const int kb = a.row_ent[e] >> 1;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int id = tid + 256 * u;
-      const int row = id >> 4, cc = id & 15;
-      const int j = kb * BK + row;
-      if (j < a.Lk) {
-        const int64_t o = (((int64_t)b * a.Lk + j) * a.Hkv + h) * D + 8 * cc;
-        pk[u] = *(const u32x4*)(K + o);
-        pv[u] = *(const u32x4*)(V + o);
-      } else {
-        pk[u] = u32x4{0, 0, 0, 0};
-        pv[u] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  if (e0 < e1) fetch(e0);
+  const int e0 = a.row_ptr[item];
+  const int nt = a.row_ptr[item + 1] - e0;
+  const __bf16* sQw = sQ + wave * WROWS * D;
 
   // tr-read addressing for the V^T operand: 16-lane group gg covers d columns
   // 16 (gg & 1) .. +15 of a 32-column block and key run 4 (gg >> 1) (+8)
@@ -147,50 +169,10 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   const int vrow = 4 * (gg >> 1) + (j16 >> 2);
   const int vcol = 16 * (gg & 1) + 4 * (j16 & 3);
 
-  // A rescale of the output accumulators (rare: only when a row's tile max exceeds its
-  // reference by more than the threshold) reads, scales and writes each accumulator
-  // register in place (agpr_scale), so the accumulators stay resident in AGPRs; scaling
-  // them with ordinary VALU code makes the compiler copy all 128 of them every tile.
-  f32x16 s[KB2][CB];
-  float mt[CB];
-  int e = e0;
-  auto stage_and_scores = [&](int ee) {
-    const int ent = a.row_ent[ee];
-    const int kb = ent >> 1;
-    const bool partial = ent & 1;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int id = tid + 256 * u;
-      const int row = id >> 4, cc = id & 15;
-      *(u32x4*)(sK + row * PITCH + 8 * cc) = pk[u];
-      *(u32x4*)(sV + row * PITCH + 8 * cc) = pv[u];
-    }
-    __syncthreads();
-    if (ee + 1 < e1) fetch(ee + 1);
-
-    // ---- S^T = K Q^T
-#pragma unroll
-    for (int k2 = 0; k2 < KB2; ++k2)
-#pragma unroll
-      for (int c = 0; c < CB; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[k2][c][i] = 0.f;
-#pragma unroll
-    for (int dd = 0; dd < D / 16; ++dd) {
-      bf16x8 qf[CB];
-#pragma unroll
-      for (int c = 0; c < CB; ++c) qf[c] = load16(sQw + (c * 32 + n) * PITCH + 16 * dd + 8 * h2);
-#pragma unroll
-      for (int k2 = 0; k2 < KB2; ++k2) {
-        const bf16x8 kf = load16(sK + (32 * k2 + n) * PITCH + 16 * dd + 8 * h2);
-#pragma unroll
-        for (int c = 0; c < CB; ++c) s[k2][c] = mfma32x32x16(kf, qf[c], s[k2][c]);
-      }
-    }
-
-    // ---- mask boundary tiles (branch-free per element)
-    if (partial) {
+  // boundary tile t: branch-free window predicate per element
+  auto mask = [&](f32x16 (&s)[KB2][CB], int ent) {
+    if (ent & 1) {
+      const int kb = ent >> 1;
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
         const int p = tok[c] + off;
@@ -204,66 +186,108 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
           }
       }
     }
-
-    // ---- tile max per row, across the two lane halves of a column
-    bool need = false;
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      float x = s[0][c][0];
-#pragma unroll
-      for (int k2 = 0; k2 < KB2; ++k2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x = fmaxf(x, s[k2][c][i]);
-      x = fmaxf(x, __shfl_xor(x, 32));
-      mt[c] = x * a.scale_log2;
-      need |= mt[c] > m[c] + kRescaleThreshold;
-    }
-    return __builtin_amdgcn_ballot_w64(need) != 0;
   };
 
-  // P = exp2(scale log2e S - m) as bf16 B operands, row sums into l, then O^T += V^T P^T.
-  // pf[k2][c][hf] holds keys 32 k2 + 16 hf + {4 h2 .. +3, 8 + 4 h2 .. +3}, i.e.
-  // accumulator elements 8 hf .. 8 hf + 7.
-  auto accumulate = [&]() {
-    bf16x8 pf[KB2][CB][2];
+  auto scores = [&](f32x16 (&s)[KB2][CB], int t) {
+    const __bf16* kt = sK + (t & 1) * TILE;
 #pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const float ref = (m[c] == -INFINITY) ? 0.f : m[c];
-      float sum = 0.f;
+    for (int k2 = 0; k2 < KB2; ++k2)
 #pragma unroll
-      for (int k2 = 0; k2 < KB2; ++k2)
+      for (int c = 0; c < CB; ++c)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          float p[8];
+        for (int i = 0; i < 16; ++i) s[k2][c][i] = 0.f;
 #pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) {
-            p[e2] = __builtin_amdgcn_exp2f(fmaf(s[k2][c][8 * hf + e2], a.scale_log2, -ref));
-            sum += p[e2];
-          }
-          pf[k2][c][hf] = join(to_bf16x4(p[0], p[1], p[2], p[3]), to_bf16x4(p[4], p[5], p[6], p[7]));
-        }
-      l[c] += sum;
-    }
+    for (int dd = 0; dd < D / 16; ++dd) {
+      bf16x8 qf[CB];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+      for (int c = 0; c < CB; ++c) qf[c] = load16(sQw + swz(c * 32 + n, 16 * dd + 8 * h2));
 #pragma unroll
       for (int k2 = 0; k2 < KB2; ++k2) {
+        const bf16x8 kf = load16(kt + swz(32 * k2 + n, 16 * dd + 8 * h2));
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const __bf16* vp = sV + (32 * k2 + 16 * hf + vrow) * PITCH + 32 * db + vcol;
-          const bf16x8 vf = join(lds_read_tr4(vp), lds_read_tr4(vp + 8 * PITCH));
-#pragma unroll
-          for (int c = 0; c < CB; ++c) acc[c][db] = mfma32x32x16(vf, pf[k2][c][hf], acc[c][db]);
-        }
+        for (int c = 0; c < CB; ++c) s[k2][c] = mfma32x32x16(kf, qf[c], s[k2][c]);
       }
     }
   };
 
-  for (; e < e1; ++e) {
-    if (stage_and_scores(e)) {
+  // List entries of tiles t .. t+2 are kept in registers and entry t+3 is loaded one
+  // iteration ahead: a load of it issued after the direct copies and waited for at once
+  // would also wait for those copies (one in-order counter covers both).
+  int ent0 = 0, ent1 = 0, ent2 = 0;
+  auto iteration = [&](int t, f32x16 (&cur)[KB2][CB], f32x16 (&next)[KB2][CB]) {
+    wait_loads_and_barrier();  // K(t+1), V(t), entry t+3 resident; every wave is done with t-1
+    const int ent3 = (t + 3 < nt) ? a.row_ent[e0 + t + 3] : 0;  // made uniform when used
+    if (t + 2 < nt) load_tile(K, sK + (t & 1) * TILE, __builtin_amdgcn_readfirstlane(ent2) >> 1);
+    if (t + 1 < nt) load_tile(V, sV + ((t + 1) & 1) * TILE, __builtin_amdgcn_readfirstlane(ent1) >> 1);
+    mask(cur, __builtin_amdgcn_readfirstlane(ent0));
+    ent0 = ent1;
+    ent1 = ent2;
+    ent2 = ent3;
+
+    // Interleaved block: step i issues one MFMA of S(t+1) (dd = i / 4, (k2, c) = i % 4;
+    // past the last tile it reads a resident buffer and the result is unused), then the
+    // softmax work of two elements of S(t): exp2 with the current reference, running max,
+    // and every 4 steps the bf16 packing and row sum of 8 probabilities.  The scheduling
+    // fences keep this order, so the matrix core and the VALU run at the same time.
+    const __bf16* kt = sK + ((t + 1) & 1) * TILE;
+#pragma unroll
+    for (int k2 = 0; k2 < KB2; ++k2)
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) next[k2][c][i] = 0.f;
+    bf16x8 kf[2][KB2], qf[2][CB];
+#pragma unroll
+    for (int x = 0; x < KB2; ++x) kf[0][x] = load16(kt + swz(32 * x + n, 8 * h2));
+#pragma unroll
+    for (int x = 0; x < CB; ++x) qf[0][x] = load16(sQw + swz(32 * x + n, 8 * h2));
+    float ref[CB], mx[CB], sum[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      ref[c] = (m[c] == -INFINITY) ? 0.f : m[c];
+      mx[c] = -INFINITY;
+      sum[c] = 0.f;
+    }
+    bf16x8 pf[KB2][CB][2];
+    float pb[8];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int dd = i >> 2, k2 = (i >> 1) & 1, c = i & 1;
+      if ((i & 3) == 0 && dd + 1 < D / 16) {
+#pragma unroll
+        for (int x = 0; x < KB2; ++x) kf[(dd + 1) & 1][x] = load16(kt + swz(32 * x + n, 16 * (dd + 1) + 8 * h2));
+#pragma unroll
+        for (int x = 0; x < CB; ++x) qf[(dd + 1) & 1][x] = load16(sQw + swz(32 * x + n, 16 * (dd + 1) + 8 * h2));
+      }
+      next[k2][c] = mfma32x32x16(kf[dd & 1][k2], qf[dd & 1][c], next[k2][c]);
+      __builtin_amdgcn_sched_barrier(0);
+      // elements 2i, 2i+1 of S(t) in (c, k2, hf, e2) order
+      const int ec = i >> 4, ek2 = (i >> 3) & 1, ehf = (i >> 2) & 1, e2 = 2 * (i & 3);
+      const float x0 = cur[ek2][ec][8 * ehf + e2], x1 = cur[ek2][ec][8 * ehf + e2 + 1];
+      mx[ec] = fmaxf(mx[ec], fmaxf(x0, x1));
+      pb[e2] = __builtin_amdgcn_exp2f(fmaf(x0, a.scale_log2, -ref[ec]));
+      pb[e2 + 1] = __builtin_amdgcn_exp2f(fmaf(x1, a.scale_log2, -ref[ec]));
+      sum[ec] += pb[e2] + pb[e2 + 1];  // fp32 row sum (it sets LSE, which the backward reuses)
+      if ((i & 3) == 3)
+        pf[ek2][ec][ehf] = join(to_bf16x4(pb[0], pb[1], pb[2], pb[3]), to_bf16x4(pb[4], pb[5], pb[6], pb[7]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    float mt[CB];
+    bool need[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const float x = fmaxf(mx[c], __shfl_xor(mx[c], 32));
+      mt[c] = x * a.scale_log2;
+      need[c] = mt[c] > m[c] + kRescaleThreshold;
+    }
+    if (__builtin_amdgcn_ballot_w64(need[0] | need[1]) != 0) {
+      // rare: rows whose max moved past the threshold take it as their new reference;
+      // their accumulators, sums and P(t) are rescaled / recomputed, the other rows keep
+      // theirs
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
-        const float mn = fmaxf(m[c], mt[c]);
+        const float mn = need[c] ? mt[c] : m[c];
         const float alpha = (m[c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[c] - mn);
         m[c] = mn;
         l[c] *= alpha;
@@ -272,8 +296,62 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[c][db][i] = agpr_scale(acc[c][db][i], alpha);
       }
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const float rf = (m[c] == -INFINITY) ? 0.f : m[c];
+        float s2 = 0.f;
+#pragma unroll
+        for (int k2 = 0; k2 < KB2; ++k2)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              p[e] = __builtin_amdgcn_exp2f(fmaf(cur[k2][c][8 * hf + e], a.scale_log2, -rf));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s2 += p[e];
+            const bf16x8 pn = join(to_bf16x4(p[0], p[1], p[2], p[3]), to_bf16x4(p[4], p[5], p[6], p[7]));
+            pf[k2][c][hf] = need[c] ? pn : pf[k2][c][hf];
+          }
+        sum[c] = need[c] ? s2 : sum[c];
+      }
     }
-    accumulate();
+#pragma unroll
+    for (int c = 0; c < CB; ++c) l[c] += sum[c];
+    // O^T += V(t)^T P(t)^T
+    // (k2, hf) outermost so that the 8 accumulators rotate: each one is next updated only
+    // after 7 independent MFMAs
+    const __bf16* vt = sV + (t & 1) * TILE;
+#pragma unroll
+    for (int k2 = 0; k2 < KB2; ++k2) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int r0 = 32 * k2 + 16 * hf + vrow;
+          const int col = 32 * db + vcol;
+          const bf16x8 vf = join(lds_read_tr4(vt + swz(r0, col)), lds_read_tr4(vt + swz(r0 + 8, col)));
+#pragma unroll
+          for (int c = 0; c < CB; ++c) acc[c][db] = mfma32x32x16(vf, pf[k2][c][hf], acc[c][db]);
+        }
+      }
+    }
+  };
+
+  if (nt > 0) {
+    ent0 = a.row_ent[e0];
+    ent1 = nt > 1 ? a.row_ent[e0 + 1] : 0;
+    ent2 = nt > 2 ? a.row_ent[e0 + 2] : 0;
+    load_tile(K, sK, __builtin_amdgcn_readfirstlane(ent0) >> 1);
+    load_tile(V, sV, __builtin_amdgcn_readfirstlane(ent0) >> 1);
+    if (nt > 1) load_tile(K, sK + TILE, __builtin_amdgcn_readfirstlane(ent1) >> 1);
+    f32x16 sa[KB2][CB], sb[KB2][CB];
+    wait_loads_and_barrier();
+    scores(sa, 0);
+    for (int t = 0; t < nt; t += 2) {
+      iteration(t, sa, sb);
+      if (t + 1 < nt) iteration(t + 1, sb, sa);
+    }
   }
 
   // ---- finalize: l summed over the two lane halves of a column

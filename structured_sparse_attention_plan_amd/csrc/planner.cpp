@@ -14,7 +14,6 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
-#include <numeric>
 #include <vector>
 
 #include "cowa.h"
@@ -188,13 +187,34 @@ extern "C" int cowa_plan_blocks(int32_t Lq, int32_t Lk, int32_t Hkv, int32_t Bq,
       }
     }
 
-  // Longest-processing-time-first work orders (ties: smaller item id first).
-  auto lpt = [](const std::vector<int32_t>& cnt, int32_t* order) {
-    std::iota(order, order + cnt.size(), 0);
-    std::stable_sort(order, order + cnt.size(),
-                     [&](int32_t x, int32_t y) { return cnt[x] > cnt[y]; });
+  // XCD-aware work orders.  Work groups are dispatched round-robin over the 8 XCDs
+  // (work group b runs on XCD b % 8) and each XCD has its own L2.  Stream x (one per XCD)
+  // takes, for every KV head, one contiguous part of that head's blocks, so the items an
+  // XCD runs together have neighbouring windows and read the same K/V (or Q/dO) tiles from
+  // its L2.  Parts are snaked across heads (part x for even heads, part 7 - x for odd
+  // ones) so that workloads whose lists grow along the sequence stay balanced; the
+  // streams are then merged round-robin.
+  auto xcd_order = [&](int32_t nblk, int32_t* order) {
+    constexpr int X = 8;
+    std::vector<std::vector<int32_t>> stream(X);
+    for (int32_t hh = 0; hh < Hkv; ++hh)
+      for (int x = 0; x < X; ++x) {
+        const int part = (hh & 1) ? (X - 1 - x) : x;
+        const int64_t lo = (int64_t)part * nblk / X, hi = (int64_t)(part + 1) * nblk / X;
+        for (int64_t blk = lo; blk < hi; ++blk) stream[x].push_back((int32_t)(hh * (int64_t)nblk + blk));
+      }
+    size_t pos = 0;
+    std::vector<size_t> next(X, 0);
+    for (bool any = true; any;) {
+      any = false;
+      for (int x = 0; x < X; ++x)
+        if (next[x] < stream[x].size()) {
+          order[pos++] = stream[x][next[x]++];
+          any = true;
+        }
+    }
   };
-  lpt(row_cnt, row_order);
-  lpt(col_cnt, col_order);
+  xcd_order(nqb, row_order);
+  xcd_order(nkb, col_order);
   return COWA_OK;
 }
