@@ -32,14 +32,134 @@ SINK, NEAR = 128, 4096
 DEC_B = 16
 
 
+# Sources each timed kernel is built from: a traffic figure taken with the counters is
+# used only while these files are unchanged.
+KERNEL_SOURCES = {
+    "fwd": ["fwd_bf16.hip"], "bwd_dq": ["bwd_bf16.hip"], "bwd_dkdv": ["bwd_bf16.hip"],
+    "decode": ["decode_bf16.hip"],
+}
+COMMON_SOURCES = ["device_common.h", "kernels.h"]
+KERNEL_SYMBOL = {"fwd": "fwd_bf16_d128_kernel", "bwd_dq": "bwd_dq_kernel",
+                 "bwd_dkdv": "bwd_dkdv_kernel", "decode": "decode_split_kernel"}
+COPY_PROBE_BYTES = 1 << 30
+
+
+def source_digest(phase):
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "structured_sparse_attention_plan_amd", "csrc")
+    for f in KERNEL_SOURCES[phase] + COMMON_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(phase):
+    """HBM bytes per launch recorded by the counter runs for `phase`, or None when there
+    is no record or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{phase}_128k.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("source_digest") != source_digest(phase):
+        return None
+    return float(rec["hbm_bytes_per_launch"])
+
+
+def pmc_per_dispatch(csv_path, symbol, counter, largest_grid=False):
+    """Mean of `counter` over the dispatches of kernels whose name contains `symbol`
+    (with largest_grid, only those with the largest grid: the probe's own copies, not the
+    small device-to-host reads around them)."""
+    import csv
+    rows = []
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if symbol in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                rows.append(r)
+    if largest_grid and rows:
+        g = max(int(r["Grid_Size"]) for r in rows)
+        rows = [r for r in rows if int(r["Grid_Size"]) == g]
+    vals = {}
+    for r in rows:
+        vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {symbol} in {csv_path}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def pmc_summary(phase, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, commands):
+    """Text record of the kernel's HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) scaled by what they read for the runtime's copy of COPY_PROBE_BYTES; the
+    strided elementwise copy of the same size is listed as a cross-check."""
+    sym = KERNEL_SYMBOL[phase]
+    f_kib, nf = pmc_per_dispatch(fetch_csv, sym, "FETCH_SIZE")
+    w_kib, nw = pmc_per_dispatch(write_csv, sym, "WRITE_SIZE")
+    cf_kib, _ = pmc_per_dispatch(copy_fetch_csv, "copyBuffer", "FETCH_SIZE", largest_grid=True)
+    cw_kib, _ = pmc_per_dispatch(copy_write_csv, "copyBuffer", "WRITE_SIZE", largest_grid=True)
+    ef_kib, _ = pmc_per_dispatch(copy_fetch_csv, "elementwise_kernel_manual_unroll", "FETCH_SIZE")
+    ew_kib, _ = pmc_per_dispatch(copy_write_csv, "elementwise_kernel_manual_unroll", "WRITE_SIZE")
+    sf = COPY_PROBE_BYTES / (cf_kib * 1024)
+    sw = COPY_PROBE_BYTES / (cw_kib * 1024)
+    fb, wb = f_kib * 1024 * sf, w_kib * 1024 * sw
+    lines = [f"kernel: {sym} ({phase}, 131072-token workload)",
+             f"source_digest: {source_digest(phase)}",
+             *[f"command: {c}" for c in commands],
+             f"FETCH_SIZE_KiB_per_dispatch: {f_kib:.1f} (mean of {nf} dispatches)",
+             f"WRITE_SIZE_KiB_per_dispatch: {w_kib:.1f} (mean of {nw} dispatches)",
+             f"copy_probe_bytes: {COPY_PROBE_BYTES}",
+             f"copy_FETCH_SIZE_KiB: {cf_kib:.1f}",
+             f"copy_WRITE_SIZE_KiB: {cw_kib:.1f}",
+             f"elementwise_copy_FETCH_SIZE_KiB: {ef_kib:.1f}",
+             f"elementwise_copy_WRITE_SIZE_KiB: {ew_kib:.1f}",
+             f"fetch_scale: {sf:.4f}",
+             f"write_scale: {sw:.4f}",
+             f"hbm_read_bytes_per_launch: {fb:.4e}",
+             f"hbm_write_bytes_per_launch: {wb:.4e}",
+             f"hbm_bytes_per_launch: {fb + wb:.6e}"]
+    return "\n".join(lines) + "\n"
+
+
+def copy_probe():
+    """The calibration runs for the FETCH_SIZE / WRITE_SIZE counters, three of each:
+    (1) a runtime device-to-device copy of COPY_PROBE_BYTES (hipMemcpy's blit kernel);
+    (2) torch's elementwise copy kernel over the same number of bf16 bytes, made to run
+    by copying between two strided views (rows of 8 KiB, every other row), which moves
+    16 bytes per lane like the attention kernels do."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    rows, cols = COPY_PROBE_BYTES // 8192, 4096          # bf16 elements per row
+    a = torch.ones((rows, 2 * cols), dtype=torch.bfloat16, device="cuda:0")
+    b = torch.zeros_like(a)
+    for _ in range(3):
+        b[:, :cols].copy_(a[:, :cols])
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "ok": bool(dst[-1].item() == 1)
+                      and bool(b[-1, cols - 1].item() == 1)}), flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run the copy that calibrates the HBM byte counters")
+    ap.add_argument("--pmc-summary", nargs=5, metavar=("PHASE", "FETCH_CSV", "WRITE_CSV",
+                                                       "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="print the traffic record of PHASE from four counter-collection CSVs")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --pmc-summary: a command that produced the CSVs (repeatable)")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=48,
+    ap.add_argument("--cpu-rows", type=int, default=320,
                     help="query rows of the 128K forward the oracle times (all 40 heads)")
     return ap.parse_args()
 
@@ -67,6 +187,13 @@ def cpu_baseline(q, k, v, ow, rows):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        phase, *csvs = args.pmc_summary
+        sys.stdout.write(pmc_summary(phase, *csvs, args.command))
+        return
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the operator shards by "
                                    "KV head with no exchange, see the design notes",
@@ -158,11 +285,13 @@ def main():
     if bound == "mfma":
         achieved = amount / (ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": traffic_from_profile(dom), "traffic_unit": "HBM bytes per launch"}
     else:
         achieved = amount / (ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None}
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                "traffic": traffic_from_profile(dom), "traffic_unit": "HBM bytes per launch"}
 
     out = {
         "metric": "CoWA fwd+bwd ms & attended-edge TFLOP/s at 128K; decode us/token at 128K KV",
