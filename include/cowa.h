@@ -111,8 +111,10 @@ typedef struct cowa_plan_info {
  *   row_order [Hkv * nqb]      row item ids in launch order (a permutation)
  *   col_order [Hkv * nkb]      column item ids in launch order (a permutation)
  * The launch orders are built for MI355X's 8 XCDs, whose L2 caches are separate and to
- * which work groups are dealt round-robin: the items dealt to one XCD are contiguous
- * blocks of one KV head at a time, so concurrently running items share K/V tiles.
+ * which work groups are dealt round-robin.  Items whose list is longer than twice the
+ * mean (the columns that hold the prefix sink) come first, longest first, so none starts
+ * late; after them, the items dealt to one XCD are contiguous blocks of one KV head at a
+ * time, so concurrently running items share K/V (or Q/dO) tiles.
  * The arrays must be either all NULL or all non-NULL.  Every list (within an item) is
  * sorted ascending; entries use COWA_ENT_BLOCK / COWA_ENT_PARTIAL.
  * Errors: INVALID_ARG for NULL info/window, a non-positive size or a negative width;

@@ -30,7 +30,27 @@ constexpr int D = 128;
 constexpr int ROWS = kBwdRows;  // 128 query rows per q-block
 constexpr int BK = kBwdBk;      // 128 keys per k-block
 constexpr int SUB = 64;         // keys staged per LDS sub-tile in the dq kernel
-constexpr int PITCH = D + 16;
+
+// x -> (hi, lo) with hi = bf16(x), lo = bf16(x - hi): about 16 significant bits as two
+// bf16 MFMA operands.  Done for 8 values at once with packed conversions; hi is widened
+// back to fp32 exactly by bit shifts.
+__device__ __forceinline__ void split_hi_lo(const float* x, bf16x8& hi, bf16x8& lo) {
+  u32x4 wh, wl;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16x2 h = {(__bf16)x[2 * k], (__bf16)x[2 * k + 1]};
+    const unsigned w = __builtin_bit_cast(unsigned, h);
+    // (w << 16 as a byte permute: written as a shift, it gets re-derived from a second
+    // conversion)
+    const float h0 = __uint_as_float(__builtin_amdgcn_perm(w, w, 0x01000c0cu));
+    const float h1 = __uint_as_float(w & 0xffff0000u);
+    const bf16x2 l = {(__bf16)(x[2 * k] - h0), (__bf16)(x[2 * k + 1] - h1)};
+    wh[k] = w;
+    wl[k] = __builtin_bit_cast(unsigned, l);
+  }
+  hi = __builtin_bit_cast(bf16x8, wh);
+  lo = __builtin_bit_cast(bf16x8, wl);
+}
 
 // ------------------------------------------------------------------------ Delta
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
@@ -62,8 +82,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------------ dQ
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 sK[SUB * PITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[SUB * PITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[SUB * D];  // swizzled rows (lds_swz)
+  __shared__ __attribute__((aligned(16))) __bf16 sV[SUB * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -150,8 +170,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     for (int u = 0; u < 4; ++u) {
       const int id = tid + 256 * u;
       const int row = id >> 4, cc = id & 15;
-      *(u32x4*)(sK + row * PITCH + 8 * cc) = pk[u];
-      *(u32x4*)(sV + row * PITCH + 8 * cc) = pv[u];
+      *(u32x4*)(sK + lds_swz(row, 8 * cc)) = pk[u];
+      *(u32x4*)(sV + lds_swz(row, 8 * cc)) = pv[u];
     }
     __syncthreads();
     if (sidx + 1 < n_sub) fetch(sidx + 1);
@@ -166,8 +186,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     for (int dd = 0; dd < 8; ++dd)
 #pragma unroll
       for (int k2 = 0; k2 < SUB / 32; ++k2) {
-        const bf16x8 kf = load16(sK + (32 * k2 + n) * PITCH + 16 * dd + 8 * h2);
-        const bf16x8 vf = load16(sV + (32 * k2 + n) * PITCH + 16 * dd + 8 * h2);
+        const bf16x8 kf = load16(sK + lds_swz(32 * k2 + n, 16 * dd + 8 * h2));
+        const bf16x8 vf = load16(sV + lds_swz(32 * k2 + n, 16 * dd + 8 * h2));
         s2[k2] = mfma32x32x16(kf, qf[dd], s2[k2]);
         dp2[k2] = mfma32x32x16(vf, df[dd], dp2[k2]);
       }
@@ -193,8 +213,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
                                 to_bf16x4(ds[8 * hf + 4], ds[8 * hf + 5], ds[8 * hf + 6], ds[8 * hf + 7]));
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const __bf16* kp = sK + (32 * k2 + 16 * hf + vrow) * PITCH + 32 * db + vcol;
-          const bf16x8 ktf = join(lds_read_tr4(kp), lds_read_tr4(kp + 8 * PITCH));
+          const int r0 = 32 * k2 + 16 * hf + vrow, col = 32 * db + vcol;
+          const bf16x8 ktf = join(lds_read_tr4(sK + lds_swz(r0, col)), lds_read_tr4(sK + lds_swz(r0 + 8, col)));
           acc[db] = mfma32x32x16(ktf, dsf, acc[db]);
         }
       }
@@ -216,8 +236,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------------ dK, dV
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[ROWS * PITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 sD[ROWS * PITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[ROWS * D];  // swizzled rows (lds_swz)
+  __shared__ __attribute__((aligned(16))) __bf16 sD[ROWS * D];
   __shared__ __attribute__((aligned(16))) float sL[ROWS];
   __shared__ __attribute__((aligned(16))) float sT[ROWS];
   __shared__ int sTok[ROWS];
@@ -309,8 +329,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for (int u = 0; u < 8; ++u) {
       const int id = tid + 256 * u;
       const int row = id >> 4, cc = id & 15;
-      *(u32x4*)(sQ + row * PITCH + 8 * cc) = pq[u];
-      *(u32x4*)(sD + row * PITCH + 8 * cc) = pd[u];
+      *(u32x4*)(sQ + lds_swz(row, 8 * cc)) = pq[u];
+      *(u32x4*)(sD + lds_swz(row, 8 * cc)) = pd[u];
     }
     if (tid < ROWS) {
       sL[tid] = plse;
@@ -327,8 +347,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
-        const bf16x8 qa = load16(sQ + (32 * rb + n) * PITCH + 16 * dd + 8 * h2);
-        const bf16x8 da = load16(sD + (32 * rb + n) * PITCH + 16 * dd + 8 * h2);
+        const bf16x8 qa = load16(sQ + lds_swz(32 * rb + n, 16 * dd + 8 * h2));
+        const bf16x8 da = load16(sD + lds_swz(32 * rb + n, 16 * dd + 8 * h2));
         s = mfma32x32x16(qa, kf[dd], s);
         dp = mfma32x32x16(da, vf[dd], dp);
       }
@@ -364,23 +384,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         // P and dS as bf16 pairs hi + lo (~16 mantissa bits): dV and dK sum them over many
         // rows with strong cancellation, so a single bf16 rounding would dominate the error
         bf16x8 pa, pl, sa, sl;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const __bf16 ph = (__bf16)pr[8 * hf + x];
-          pa[x] = ph;
-          pl[x] = (__bf16)(pr[8 * hf + x] - (float)ph);
-          const __bf16 sh = (__bf16)ds[8 * hf + x];
-          sa[x] = sh;
-          sl[x] = (__bf16)(ds[8 * hf + x] - (float)sh);
-        }
+        split_hi_lo(pr + 8 * hf, pa, pl);
+        split_hi_lo(ds + 8 * hf, sa, sl);
         // hi products for all 4 column blocks, then the lo ones: an accumulator is next
         // updated only after 7 independent MFMAs
         bf16x8 dt[4], qt[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const int ro = (32 * rb + 16 * hf + vrow) * PITCH + 32 * db + vcol;
-          dt[db] = join(lds_read_tr4(sD + ro), lds_read_tr4(sD + ro + 8 * PITCH));
-          qt[db] = join(lds_read_tr4(sQ + ro), lds_read_tr4(sQ + ro + 8 * PITCH));
+          const int r0 = 32 * rb + 16 * hf + vrow, col = 32 * db + vcol;
+          dt[db] = join(lds_read_tr4(sD + lds_swz(r0, col)), lds_read_tr4(sD + lds_swz(r0 + 8, col)));
+          qt[db] = join(lds_read_tr4(sQ + lds_swz(r0, col)), lds_read_tr4(sQ + lds_swz(r0 + 8, col)));
           accV[db] = mfma32x32x16(pa, dt[db], accV[db]);
           accK[db] = mfma32x32x16(sa, qt[db], accK[db]);
         }

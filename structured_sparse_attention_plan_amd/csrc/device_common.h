@@ -22,6 +22,7 @@ namespace cowa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -46,6 +47,21 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
   const lds_i16x4* lp = (const lds_i16x4*)(__attribute__((address_space(3))) const void*)(p);
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lp);
   return __builtin_bit_cast(bf16x4, v);
+}
+
+// LDS tiles of 128 bf16 columns use 256-byte rows (every row starts at bank 0) with the
+// 16-byte chunks of row r permuted by XOR with lds_sw(r), which is conflict-free for both
+// read patterns of the kernels (64 banks of 4 bytes; 16 lanes per cycle for 16-byte
+// reads, 32 lanes per cycle for 8-byte reads):
+//   * 16-byte operand reads, one chunk of 16 consecutive rows: lds_sw takes 16 distinct
+//     values on any 16 consecutive rows;
+//   * ds_read_b64_tr_b16, 4 aligned rows x 4 aligned chunks: bits 2-3 of lds_sw(r) are
+//     r % 4 and bits 0-1 depend only on r / 4, so the 16 (row, chunk) pairs land on 16
+//     distinct chunks.
+__device__ __forceinline__ int lds_sw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Element offset of (row r, column e) in such a tile.
+__device__ __forceinline__ int lds_swz(int r, int e) {
+  return r * 128 + ((((e >> 3) ^ lds_sw(r)) & 15) << 3) + (e & 7);
 }
 
 __device__ __forceinline__ bf16x8 join(const bf16x4& lo, const bf16x4& hi) {

@@ -28,7 +28,8 @@
 // global->LDS loads (global_load_lds_dwordx4, no staging registers); the loads of K(t+2)
 // and V(t+1) are issued right after the single barrier of iteration t and waited for at
 // the next one.  LDS rows are 256 bytes with the 16-byte chunks XOR-swizzled by a function
-// of the row, so the row-wise operand reads and the transposed V reads hit distinct banks.
+// of the row, so both the row-wise operand reads and the transposed V reads are free of
+// bank conflicts.
 // Output: O / l in bf16 and LSE = ln 2 * (m + log2 l) in fp32.
 //
 // MFMA lane layouts of v_mfma_f32_32x32x16_bf16 (n = lane % 32, h2 = lane / 32):
@@ -50,13 +51,9 @@ constexpr int KB2 = BK / 32;         // 2 key blocks of 32
 constexpr int TILE = BK * D;         // elements per K or V tile
 constexpr float kRescaleThreshold = 8.0f;
 
-// LDS rows are 256 bytes, so every row starts at bank 0; the 16-byte chunks of row r are
-// permuted by XOR with sw(r).  sw takes 16 distinct values over any 16 consecutive rows
-// (row-wise operand reads: one chunk of 16 rows) and maps 4 aligned rows x 2 adjacent
-// chunks to 8 distinct chunks (the transposed reads).
-__device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-// Element offset of (row r, column e) in a swizzled 128-column LDS tile.
-__device__ __forceinline__ int swz(int r, int e) { return r * D + ((((e >> 3) ^ sw(r)) & 15) << 3) + (e & 7); }
+// LDS tiles: 256-byte rows with XOR-swizzled 16-byte chunks (lds_sw / lds_swz).
+__device__ __forceinline__ int sw(int r) { return lds_sw(r); }
+__device__ __forceinline__ int swz(int r, int e) { return lds_swz(r, e); }
 
 // x * alpha for a value held in an accumulation register, done in place: read to a VGPR,
 // multiply, write back.  Only used on the rare rescale path, long after the MFMA that

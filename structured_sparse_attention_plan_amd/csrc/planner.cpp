@@ -187,23 +187,41 @@ extern "C" int cowa_plan_blocks(int32_t Lq, int32_t Lk, int32_t Hkv, int32_t Bq,
       }
     }
 
-  // XCD-aware work orders.  Work groups are dispatched round-robin over the 8 XCDs
-  // (work group b runs on XCD b % 8) and each XCD has its own L2.  Stream x (one per XCD)
-  // takes, for every KV head, one contiguous part of that head's blocks, so the items an
-  // XCD runs together have neighbouring windows and read the same K/V (or Q/dO) tiles from
-  // its L2.  Parts are snaked across heads (part x for even heads, part 7 - x for odd
-  // ones) so that workloads whose lists grow along the sequence stay balanced; the
-  // streams are then merged round-robin.
-  auto xcd_order = [&](int32_t nblk, int32_t* order) {
+  // Launch orders.  Work groups are dispatched in launch order, round-robin over the 8
+  // XCDs (work group b runs on XCD b % 8), and each XCD has its own L2.
+  //  1. Heavy items first: an item whose list is more than twice the mean length (the
+  //     columns holding the prefix sink are seen by every row) goes first, longest first,
+  //     so that it does not start late and run alone at the end of the launch.
+  //  2. The rest in XCD streams: stream x (one per XCD) takes, for every KV head, one
+  //     contiguous part of that head's blocks, so the items an XCD runs together have
+  //     neighbouring windows and read the same K/V (or Q/dO) tiles from its L2.  Parts are
+  //     snaked across heads (part x for even heads, part 7 - x for odd ones) so that
+  //     workloads whose lists grow along the sequence stay balanced; the streams are then
+  //     merged round-robin.
+  auto xcd_order = [&](int32_t nblk, const int32_t* ptr, int32_t* order) {
     constexpr int X = 8;
+    const int64_t nitem = (int64_t)Hkv * nblk;
+    const double mean = (double)ptr[nitem] / (double)nitem;
+    std::vector<int32_t> heavy;
+    for (int64_t it = 0; it < nitem; ++it)
+      if (ptr[it + 1] - ptr[it] > 2.0 * mean) heavy.push_back((int32_t)it);
+    std::stable_sort(heavy.begin(), heavy.end(), [&](int32_t x, int32_t y) {
+      return ptr[x + 1] - ptr[x] > ptr[y + 1] - ptr[y];
+    });
+    std::vector<char> is_heavy((size_t)nitem, 0);
+    for (int32_t it : heavy) is_heavy[it] = 1;
+    size_t pos = 0;
+    for (int32_t it : heavy) order[pos++] = it;
     std::vector<std::vector<int32_t>> stream(X);
     for (int32_t hh = 0; hh < Hkv; ++hh)
       for (int x = 0; x < X; ++x) {
         const int part = (hh & 1) ? (X - 1 - x) : x;
         const int64_t lo = (int64_t)part * nblk / X, hi = (int64_t)(part + 1) * nblk / X;
-        for (int64_t blk = lo; blk < hi; ++blk) stream[x].push_back((int32_t)(hh * (int64_t)nblk + blk));
+        for (int64_t blk = lo; blk < hi; ++blk) {
+          const int64_t it = hh * (int64_t)nblk + blk;
+          if (!is_heavy[it]) stream[x].push_back((int32_t)it);
+        }
       }
-    size_t pos = 0;
     std::vector<size_t> next(X, 0);
     for (bool any = true; any;) {
       any = false;
@@ -214,7 +232,7 @@ extern "C" int cowa_plan_blocks(int32_t Lq, int32_t Lk, int32_t Hkv, int32_t Bq,
         }
     }
   };
-  xcd_order(nqb, row_order);
-  xcd_order(nkb, col_order);
+  xcd_order(nqb, row_ptr, row_order);
+  xcd_order(nkb, col_ptr, col_order);
   return COWA_OK;
 }
