@@ -20,6 +20,8 @@
 // Rows of a q-block are token-major (row r = token * G + head-in-group); rows beyond
 // G * Bq or Lq carry LSE = +inf and Delta = 0 so that they contribute nothing.
 
+#include <type_traits>
+
 #include "cowa.h"
 #include "device_common.h"
 
@@ -30,27 +32,6 @@ constexpr int D = 128;
 constexpr int ROWS = kBwdRows;  // 128 query rows per q-block
 constexpr int BK = kBwdBk;      // 128 keys per k-block
 constexpr int SUB = 64;         // keys staged per LDS sub-tile in the dq kernel
-
-// x -> (hi, lo) with hi = bf16(x), lo = bf16(x - hi): about 16 significant bits as two
-// bf16 MFMA operands.  Done for 8 values at once with packed conversions; hi is widened
-// back to fp32 exactly by bit shifts.
-__device__ __forceinline__ void split_hi_lo(const float* x, bf16x8& hi, bf16x8& lo) {
-  u32x4 wh, wl;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const bf16x2 h = {(__bf16)x[2 * k], (__bf16)x[2 * k + 1]};
-    const unsigned w = __builtin_bit_cast(unsigned, h);
-    // (w << 16 as a byte permute: written as a shift, it gets re-derived from a second
-    // conversion)
-    const float h0 = __uint_as_float(__builtin_amdgcn_perm(w, w, 0x01000c0cu));
-    const float h1 = __uint_as_float(w & 0xffff0000u);
-    const bf16x2 l = {(__bf16)(x[2 * k] - h0), (__bf16)(x[2 * k + 1] - h1)};
-    wh[k] = w;
-    wl[k] = __builtin_bit_cast(unsigned, l);
-  }
-  hi = __builtin_bit_cast(bf16x8, wh);
-  lo = __builtin_bit_cast(bf16x8, wl);
-}
 
 // ------------------------------------------------------------------------ Delta
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
@@ -235,19 +216,48 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------ dK, dV
+// Software pipeline over the 32-row blocks g of the item's column list (4 per q-block):
+// step g issues S, dP of block g + 1 (16 MFMAs, phase 1), then dV, dK of block g
+// (32 MFMAs, phase 2) with the VALU work of block g + 1 (P, dS and their hi/lo split)
+// placed between those MFMAs by scheduling fences, so the matrix core and the VALU run
+// at the same time.  The Q and dO tiles of a q-block are double-buffered in LDS and
+// filled by direct global->LDS copies issued one q-block ahead.
+constexpr int QTILE = ROWS * D;  // one q-block of Q (or dO) in LDS
+
+// Returns x unchanged, but the value is taken at this point of the program: computations
+// that use the result cannot be hoisted above it (it pins VALU work to its pipeline slot).
+__device__ __forceinline__ float pin(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ void pin_out(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin_out(float& x) { asm volatile("" : "+v"(x)); }
+
+// One pair of the hi/lo split: (x0, x1) -> bf16 pair hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = {(__bf16)x0, (__bf16)x1};
+  const uint32_t w = __builtin_bit_cast(uint32_t, h);
+  const float h0 = __uint_as_float(__builtin_amdgcn_perm(w, w, 0x01000c0cu));  // w << 16
+  const float h1 = __uint_as_float(w & 0xffff0000u);
+  const bf16x2 l = {(__bf16)(x0 - h0), (__bf16)(x1 - h1)};
+  hi = w;
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[ROWS * D];  // swizzled rows (lds_swz)
-  __shared__ __attribute__((aligned(16))) __bf16 sD[ROWS * D];
-  __shared__ __attribute__((aligned(16))) float sL[ROWS];
-  __shared__ __attribute__((aligned(16))) float sT[ROWS];
-  __shared__ int sTok[ROWS];
+  // [buffer][Q, dO][rows]: swizzled 256-byte rows (lds_swz); the dO tile of a buffer sits
+  // at a fixed distance from its Q tile, so one address serves both
+  __shared__ __attribute__((aligned(1024))) __bf16 sQD[4 * QTILE];
+  __shared__ __attribute__((aligned(16))) float sLT[4 * ROWS];  // [buffer][LSE*log2e, Delta]
+  __shared__ int sRt[ROWS];                                     // row -> token in the q-block
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int n = lane & 31;
   const int h2 = lane >> 5;
-  const int item = a.col_order[blockIdx.x];
+  const int item = load_uniform(a.col_order, blockIdx.x);
   const int b = blockIdx.y;
   const int h = item / a.nkb;
   const int kb = item - h * a.nkb;
@@ -259,6 +269,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const __bf16* K = (const __bf16*)a.k;
   const __bf16* V = (const __bf16*)a.v;
   const __bf16* dO = (const __bf16*)a.dout;
+
+  if (tid < ROWS) sRt[tid] = tid / G;
 
   // this lane's key (column of S and dP)
   const int j = kb * BK + wave * 32 + n;
@@ -279,131 +291,292 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) accK[db][i] = accV[db][i] = 0.f;
 
+  // Per-lane LDS offsets inside a 32-row block (the swizzle depends on row % 16 only, so
+  // row block rb adds 32 rb rows and half hf adds 16 rows to these):
+  //   operand reads (S, dP): row n, columns 16 dd + 8 h2;
+  //   transposed reads (dV, dK): rows vrow (+8), columns 32 db + vcol.
   const int gg = lane >> 4, j16 = lane & 15;
   const int vrow = 4 * (gg >> 1) + (j16 >> 2);
   const int vcol = 16 * (gg & 1) + 4 * (j16 & 3);
-
-  const int e0 = a.col_ptr[item], e1 = a.col_ptr[item + 1];
-  // staging of one q-block: Q and dO rows, chunks tid + 256 u (u < 8), row id / 16
-  u32x4 pq[8], pd[8];
-  float plse = INFINITY, pdel = 0.f;
-  int ptok = 0x40000000;
-  auto fetch = [&](int e) {
-    const int qb = a.col_ent[e] >> 1;
+  int ofs_a[8], ofs_t[2][4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int id = tid + 256 * u;
-      const int row = id >> 4, cc = id & 15;
-      const int rt = row / G;
-      const int t = qb * Bq + rt;
-      if (rt < Bq && t < a.Lq) {
-        const int64_t o = (((int64_t)b * a.Lq + t) * a.Hq + h * G + (row - rt * G)) * D + 8 * cc;
-        pq[u] = *(const u32x4*)(Q + o);
-        pd[u] = *(const u32x4*)(dO + o);
-      } else {
-        pq[u] = u32x4{0, 0, 0, 0};
-        pd[u] = u32x4{0, 0, 0, 0};
+  for (int dd = 0; dd < 8; ++dd) ofs_a[dd] = lds_swz(n, 16 * dd + 8 * h2);
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) ofs_t[p][db] = lds_swz(vrow + 8 * p, 32 * db + vcol);
+
+  // Direct copies: wave w fills rows 32 w .. 32 w + 31 of a tile, 4 rows per copy; lane L
+  // of copy u fills row r = 32 w + 4 u + L / 16, physical chunk L % 16, i.e. logical chunk
+  // (L % 16) ^ lds_sw(r) of that row.  off_u[u] is that chunk's element offset from the
+  // q-block's first token: token tk = r / G (rows past the q-block take its last token;
+  // their LSE is +inf, so they contribute nothing) times Hq * D, plus the head's columns.
+  const int HqD = a.Hq * D;
+  int off_u[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int r = wave * 32 + 4 * u + (lane >> 4);
+    int rt = r / G, g = r - rt * G;
+    if (rt >= Bq) {
+      rt = Bq - 1;
+      g = 0;
+    }
+    off_u[u] = rt * HqD + (h * G + g) * D + 8 * ((lane & 15) ^ lds_sw(r));
+  }
+  // LSE / Delta staging: thread tid < ROWS owns row tid of the next q-block.  The raw
+  // loaded values are only touched when stored to LDS (after the wait that precedes the
+  // q-block's first use), so the loads do not stall the wave when they are issued.
+  const int my_rt = tid / G, my_g = tid - my_rt * G;
+  float plse = 0.f, pdel = 0.f;
+  bool pvalid = false;
+
+  const int e0 = load_uniform(a.col_ptr, item);
+  const int n_ent = load_uniform(a.col_ptr, item + 1) - e0;
+
+  auto load_entry = [&](int qb, int buf) {
+    const int t0 = qb * Bq;
+    const int64_t base = ((int64_t)b * a.Lq + t0) * HqD;
+    __bf16* dq_ = sQD + 2 * buf * QTILE + wave * 32 * D;
+    if (t0 + Bq <= a.Lq) {
+      // uniform base + unsigned 32-bit byte offset: the scalar-base form of the copy
+      const char* qs = (const char*)(Q + base);
+      const char* ds_ = (const char*)(dO + base);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        g2lds(qs + (uint32_t)(2 * off_u[u]), dq_ + 4 * u * D);
+        g2lds(ds_ + (uint32_t)(2 * off_u[u]), dq_ + QTILE + 4 * u * D);
+      }
+    } else {  // last q-block: tokens past Lq read token Lq - 1
+      const int last = a.Lq - 1 - t0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int tk = off_u[u] / HqD;
+        const int o = min(tk, last) * HqD + (off_u[u] - tk * HqD);
+        g2lds(Q + base + o, dq_ + 4 * u * D);
+        g2lds(dO + base + o, dq_ + QTILE + 4 * u * D);
       }
     }
     if (tid < ROWS) {
-      const int rt = tid / G;
-      const int t = qb * Bq + rt;
-      plse = INFINITY;
-      pdel = 0.f;
-      ptok = 0x40000000;
-      if (rt < Bq && t < a.Lq) {
-        const int64_t si = ((int64_t)b * a.Hq + h * G + (tid - rt * G)) * a.Lq + t;
-        const float lv = a.lse[si];
-        plse = lv == -INFINITY ? INFINITY : lv * kLog2e;
-        pdel = a.delta[si];
-        ptok = t;
+      const int t = t0 + my_rt;
+      pvalid = my_rt < Bq && t < a.Lq;
+      const int64_t si = ((int64_t)b * a.Hq + h * G + my_g) * a.Lq + (pvalid ? t : 0);
+      plse = a.lse[si];
+      pdel = a.delta[si];
+    }
+  };
+  // rows with no token or no visible key: LSE +inf (P = 0) and Delta 0
+  auto store_lse = [&](int buf) {
+    if (tid < ROWS) {
+      sLT[2 * buf * ROWS + tid] = (pvalid && plse != -INFINITY) ? plse * kLog2e : INFINITY;
+      sLT[(2 * buf + 1) * ROWS + tid] = pvalid ? pdel : 0.f;
+    }
+  };
+
+  // S, dP of row block rb (32 rows) of buffer buf: 16 MFMAs, operands one dd ahead
+  auto scores = [&](int buf, int rb, f32x16& s, f32x16& dp) {
+    const __bf16* qt = sQD + 2 * buf * QTILE + 4096 * rb;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+    bf16x8 qa[2], da[2];
+    qa[0] = load16(qt + ofs_a[0]);
+    da[0] = load16(qt + QTILE + ofs_a[0]);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      if (dd + 1 < 8) {
+        qa[(dd + 1) & 1] = load16(qt + ofs_a[dd + 1]);
+        da[(dd + 1) & 1] = load16(qt + QTILE + ofs_a[dd + 1]);
+      }
+      s = mfma32x32x16(qa[dd & 1], kf[dd], s);
+      dp = mfma32x32x16(da[dd & 1], vf[dd], dp);
+    }
+  };
+  // boundary q-block: the window predicate per element (S = -inf where hidden)
+  auto mask = [&](f32x16& s, int rb, int qb) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int rr = 32 * rb + 8 * i4 + 4 * h2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = qb * Bq + sRt[rr + i];
+        const bool vis = kvalid & visible(t + off, j, a.Lk, a.win.sink, a.win.near_w, band);
+        s[4 * i4 + i] = vis ? s[4 * i4 + i] : -INFINITY;
       }
     }
   };
-  if (e0 < e1) fetch(e0);
 
-  for (int e = e0; e < e1; ++e) {
-    const bool partial = a.col_ent[e] & 1;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int id = tid + 256 * u;
-      const int row = id >> 4, cc = id & 15;
-      *(u32x4*)(sQ + lds_swz(row, 8 * cc)) = pq[u];
-      *(u32x4*)(sD + lds_swz(row, 8 * cc)) = pd[u];
-    }
-    if (tid < ROWS) {
-      sL[tid] = plse;
-      sT[tid] = pdel;
-      sTok[tid] = ptok;
-    }
-    __syncthreads();
-    if (e + 1 < e1) fetch(e + 1);
+  // Carried from one step to the next: P of the block as packed bf16 hi and lo (2 halves
+  // x 4 words), and dS in fp32 (split in the next step's phase 1).
+  struct Carry {
+    uint32_t pa[2][4], pl[2][4];
+    float ds[16];
+  };
+  auto as_bf16x8 = [](const uint32_t (&w)[4]) { return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]}); };
 
-#pragma unroll
-    for (int rb = 0; rb < ROWS / 32; ++rb) {
+  if (n_ent > 0) {
+    int ent_c = load_uniform(a.col_ent, e0);  // entry of the current block g
+    // entry of q-block e + 1, read one q-block before it is needed
+    int ent_ahead = n_ent > 1 ? load_uniform(a.col_ent, e0 + 1) : 0;
+    load_entry(ent_c >> 1, 0);
+    wait_loads_and_barrier();
+    store_lse(0);
+    __syncthreads();
+
+    Carry wA, wB;
+    {  // prologue: S, dP, P (split) and dS of block 0
       f32x16 s, dp;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const bf16x8 qa = load16(sQ + lds_swz(32 * rb + n, 16 * dd + 8 * h2));
-        const bf16x8 da = load16(sD + lds_swz(32 * rb + n, 16 * dd + 8 * h2));
-        s = mfma32x32x16(qa, kf[dd], s);
-        dp = mfma32x32x16(da, vf[dd], dp);
-      }
-      // element i: row 32 rb + 8 (i / 4) + 4 h2 + i % 4, key j
-      float pr[16], ds[16];
+      scores(0, 0, s, dp);
+      if (ent_c & 1) mask(s, 0, ent_c >> 1);
+      float pr[16];
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int rr = 32 * rb + 8 * i4 + 4 * h2;
-        const f32x4 l4 = *(const f32x4*)(sL + rr);
+        const f32x4 l4 = *(const f32x4*)(sLT + 8 * i4 + 4 * h2);
+        const f32x4 t4 = *(const f32x4*)(sLT + ROWS + 8 * i4 + 4 * h2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
           pr[4 * i4 + i] = __builtin_amdgcn_exp2f(fmaf(s[4 * i4 + i], a.scale_log2, -l4[i]));
+          wA.ds[4 * i4 + i] = pr[4 * i4 + i] * (dp[4 * i4 + i] - t4[i]);
+        }
       }
-      if (partial) {  // one uniform branch; the predicate per element, branch-free
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int rr = 32 * rb + 8 * i4 + 4 * h2;
+      for (int k = 0; k < 8; ++k) split_pair(pr[2 * k], pr[2 * k + 1], wA.pa[k >> 2][k & 3], wA.pl[k >> 2][k & 3]);
+    }
+
+    int ent_n = ent_c;  // entry of block g + 1 once it starts a new q-block
+    const int ng = 4 * n_ent;
+    // One pipeline step.  Phase 1: S, dP of block g + 1 (16 MFMAs) with the hi/lo split of
+    // dS(g) between them.  Phase 2: dV, dK of block g (32 MFMAs) with P, dS of block g + 1
+    // and the split of P(g + 1) between them.  has_next (compile time) is false only for
+    // the last block.
+    auto step = [&](const int g, auto has_next_c, const Carry& cur, Carry& nxt) {
+      constexpr bool has_next = decltype(has_next_c)::value;
+      const int rb = g & 3;
+      const int e = g >> 2;
+      const int buf = e & 1;
+      if (rb == 0) {
+        // every wave is done with q-block e - 1: its buffer takes q-block e + 1
+        __syncthreads();
+        if (e + 1 < n_ent) {
+          ent_n = ent_ahead;
+          load_entry(ent_n >> 1, buf ^ 1);
+          if (e + 2 < n_ent) ent_ahead = load_uniform(a.col_ent, e0 + e + 2);
+        }
+      }
+      const int ent_g1 = (rb == 3) ? ent_n : ent_c;  // entry of block g + 1
+      const int buf1 = (rb == 3) ? buf ^ 1 : buf;
+      const int rb1 = (rb + 1) & 3;
+      if (rb == 3 && has_next) {  // q-block e + 1 resident
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        store_lse(buf1);
+        __syncthreads();
+      }
+
+      // ---- phase 1
+      const __bf16* tg = sQD + 2 * buf * QTILE + 4096 * rb;     // Q rows of block g (dO: + QTILE)
+      const __bf16* t1 = sQD + 2 * buf1 * QTILE + 4096 * rb1;  // Q rows of block g + 1
+      bf16x8 qa[8], da[8];
+      if constexpr (has_next) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool vis = kvalid & visible(sTok[rr + i] + off, j, a.Lk, a.win.sink, a.win.near_w, band);
-            pr[4 * i4 + i] = vis ? pr[4 * i4 + i] : 0.f;
+        for (int dd = 0; dd < 8; ++dd) {
+          qa[dd] = load16(t1 + ofs_a[dd]);
+          da[dd] = load16(t1 + QTILE + ofs_a[dd]);
+        }
+      }
+      bf16x8 dt[2][4], qt[2][4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        dt[0][db] = join(lds_read_tr4(tg + QTILE + ofs_t[0][db]), lds_read_tr4(tg + QTILE + ofs_t[1][db]));
+        qt[0][db] = join(lds_read_tr4(tg + ofs_t[0][db]), lds_read_tr4(tg + ofs_t[1][db]));
+      }
+      f32x16 sn, dpn;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sn[i] = dpn[i] = 0.f;
+      uint32_t wsa[2][4], wsl[2][4];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        if constexpr (has_next) {
+          const int dd = x >> 1;
+          if (x & 1) dpn = mfma32x32x16(da[dd], vf[dd], dpn);
+          else sn = mfma32x32x16(qa[dd], kf[dd], sn);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if ((x & 1) == 0) {
+          const int q = x >> 1;
+          split_pair(pin(cur.ds[2 * q]), pin(cur.ds[2 * q + 1]), wsa[q >> 2][q & 3], wsl[q >> 2][q & 3]);
+          pin_out(wsa[q >> 2][q & 3]);
+          pin_out(wsl[q >> 2][q & 3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (has_next) {
+        if (ent_g1 & 1) mask(sn, rb1, ent_g1 >> 1);
+      }
+
+      // ---- phase 2: dV, dK of block g, interleaved with P, dS of block g + 1
+      const float* lt = sLT + 2 * buf1 * ROWS + 32 * rb1 + 4 * h2;  // LSE; Delta at + ROWS
+      f32x4 l4[4], t4[4];
+      float pr[16];
+      if constexpr (has_next) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) l4[i4] = *(const f32x4*)(lt + 8 * i4);
+      }
+      const bf16x8 pa[2] = {as_bf16x8(cur.pa[0]), as_bf16x8(cur.pa[1])};
+      const bf16x8 pl[2] = {as_bf16x8(cur.pl[0]), as_bf16x8(cur.pl[1])};
+      const bf16x8 sa[2] = {as_bf16x8(wsa[0]), as_bf16x8(wsa[1])};
+      const bf16x8 sl[2] = {as_bf16x8(wsl[0]), as_bf16x8(wsl[1])};
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int x = 0; x < 32; ++x) {
+        // MFMA x: half hf, hi products (k < 8) then lo products, V and K alternating
+        const int hf = x >> 4, k = x & 15, db = (k & 7) >> 1;
+        if (k < 8) {
+          if (k & 1) accK[db] = mfma32x32x16(sa[hf], qt[hf][db], accK[db]);
+          else accV[db] = mfma32x32x16(pa[hf], dt[hf][db], accV[db]);
+        } else {
+          if (k & 1) accK[db] = mfma32x32x16(sl[hf], qt[hf][db], accK[db]);
+          else accV[db] = mfma32x32x16(pl[hf], dt[hf][db], accV[db]);
+        }
+        // transposed operands of half 1, each read right after its half-0 register is
+        // last used (MFMA 8 + 2 db for dO, 9 + 2 db for Q), 7 MFMAs before its own use
+        if (x >= 9 && x <= 16) {
+          const int db1 = (x - 9) >> 1;
+          const __bf16* th = tg + 2048 + (((x - 9) & 1) ? 0 : QTILE);
+          const bf16x8 v = join(lds_read_tr4(th + ofs_t[0][db1]), lds_read_tr4(th + ofs_t[1][db1]));
+          if ((x - 9) & 1) qt[1][db1] = v;
+          else dt[1][db1] = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (has_next) {
+          // P (exp) in steps 0..15, dS 4 steps behind, the split of P pair q in step 2q + 17
+          if (x < 16) {
+            pr[x] = __builtin_amdgcn_exp2f(fmaf(pin(sn[x]), a.scale_log2, -l4[x >> 2][x & 3]));
+            pin_out(pr[x]);
+          }
+          if ((x & 3) == 0 && x < 16) t4[x >> 2] = *(const f32x4*)(lt + ROWS + 2 * x);
+          if (x >= 4 && x < 20) {
+            const int i = x - 4;
+            nxt.ds[i] = pr[i] * (pin(dpn[i]) - t4[i >> 2][i & 3]);
+            pin_out(nxt.ds[i]);
+          }
+          if (x >= 16 && (x & 1)) {
+            const int q = (x - 17) >> 1;
+            split_pair(pin(pr[2 * q]), pin(pr[2 * q + 1]), nxt.pa[q >> 2][q & 3], nxt.pl[q >> 2][q & 3]);
+            pin_out(nxt.pa[q >> 2][q & 3]);
+            pin_out(nxt.pl[q >> 2][q & 3]);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 t4 = *(const f32x4*)(sT + 32 * rb + 8 * i4 + 4 * h2);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ds[4 * i4 + i] = pr[4 * i4 + i] * (dp[4 * i4 + i] - t4[i]);
-      }
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        // P and dS as bf16 pairs hi + lo (~16 mantissa bits): dV and dK sum them over many
-        // rows with strong cancellation, so a single bf16 rounding would dominate the error
-        bf16x8 pa, pl, sa, sl;
-        split_hi_lo(pr + 8 * hf, pa, pl);
-        split_hi_lo(ds + 8 * hf, sa, sl);
-        // hi products for all 4 column blocks, then the lo ones: an accumulator is next
-        // updated only after 7 independent MFMAs
-        bf16x8 dt[4], qt[4];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int r0 = 32 * rb + 16 * hf + vrow, col = 32 * db + vcol;
-          dt[db] = join(lds_read_tr4(sD + lds_swz(r0, col)), lds_read_tr4(sD + lds_swz(r0 + 8, col)));
-          qt[db] = join(lds_read_tr4(sQ + lds_swz(r0, col)), lds_read_tr4(sQ + lds_swz(r0 + 8, col)));
-          accV[db] = mfma32x32x16(pa, dt[db], accV[db]);
-          accK[db] = mfma32x32x16(sa, qt[db], accK[db]);
-        }
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          accV[db] = mfma32x32x16(pl, dt[db], accV[db]);
-          accK[db] = mfma32x32x16(sl, qt[db], accK[db]);
-        }
-      }
+      if (rb == 3) ent_c = ent_n;
+    };
+    // steps in pairs, the carried values alternating between wA and wB
+    int g = 0;
+    for (; g + 2 < ng; g += 2) {
+      step(g, std::true_type{}, wA, wB);
+      step(g + 1, std::true_type{}, wB, wA);
     }
+    step(g, std::true_type{}, wA, wB);
+    step(g + 1, std::false_type{}, wB, wA);
   }
 
   // element i of accK[db] / accV[db]: key 32 wave + 8 (i / 4) + 4 h2 + i % 4, dim 32 db + n

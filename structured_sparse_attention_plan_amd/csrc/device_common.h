@@ -64,6 +64,26 @@ __device__ __forceinline__ int lds_swz(int r, int e) {
   return r * 128 + ((((e >> 3) ^ lds_sw(r)) & 15) << 3) + (e & 7);
 }
 
+// Read-only plan data with a wave-uniform index, read through the constant address space
+// so that it becomes a scalar load (tracked apart from the vector-memory counter that the
+// direct LDS copies use).
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+// One 1 KB direct global->LDS copy per wave: lane L moves the 16 bytes at src (its own
+// address) to lds + 16 L (lds is wave-uniform).
+__device__ __forceinline__ void g2lds(const void* src, __bf16* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Wait for every outstanding vector-memory load of this wave (direct LDS copies
+// included), then the work-group barrier.
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __syncthreads();
+}
+
 __device__ __forceinline__ bf16x8 join(const bf16x4& lo, const bf16x4& hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }

@@ -67,16 +67,6 @@ __device__ __forceinline__ float agpr_scale(float x, float alpha) {
   return r;
 }
 
-// One 1 KB direct global->LDS copy per wave: lane L moves 16 bytes to lds + 16 L.
-__device__ __forceinline__ void g2lds(const void* src, __bf16* lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
-
-__device__ __forceinline__ void wait_loads_and_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  __syncthreads();
-}
-
 __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 sQ[ROWS * D];
   __shared__ __attribute__((aligned(1024))) __bf16 sK[2 * TILE];
