@@ -159,6 +159,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the secondary workloads (32K forward, coverage ablation, dense "
+                         "ratios, fp32 1K forward)")
     ap.add_argument("--cpu-rows", type=int, default=320,
                     help="query rows of the 128K forward the oracle times (all 40 heads)")
     return ap.parse_args()
@@ -178,11 +181,117 @@ def cpu_baseline(q, k, v, ow, rows):
     edges = sum(int(row_counts(rows, L, L, h, ow.sink, ow.near, ow.gap, ow.lr, ow.mode).sum()) * G
                 for h in range(HKV))
     cores = len(os.sched_getaffinity(0))
-    return {"value": 4 * D * edges / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((p.get("num_threads", 0) for p in threadpool_info()), default=None)
+    except Exception:
+        blas_threads = None
+    rate = 4 * D * edges / dt
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "blas_threads": blas_threads,
             "sample": f"float64 NumPy oracle forward on {len(rows)} seeded query rows x {HQ} heads "
                       f"of the 131072-token workload ({edges} attended edges, {dt:.1f} s, "
-                      f"attended-edge forward flops {4 * D * edges:.3e})"}
+                      f"attended-edge forward flops {4 * D * edges:.3e})",
+            "per_row_head_ms": dt * 1e3 / (len(rows) * HQ),
+            "extrapolated_full_fwd_s": None}
+
+
+def _events_ms(fn, steps, warmup):
+    """Mean ms of fn() over `steps` runs after `warmup`, HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(sum(a.elapsed_time(b) for a, b in ts) / len(ts))
+
+
+def extras(seed, main_fb_ms, main_fwd_ms, main_bwd_ms, main_dec_ms, main_E, main_dec_bytes):
+    """Secondary workloads timed with the same kernels: the 32K forward, the 32K coverage
+    ablation (complementary / duplicated / dense bands, forward + backward), dense causal
+    attention at 128K (forward + backward and decode) for the CoWA-vs-dense ratios, and the
+    fp32 1K forward."""
+    import torch
+    from structured_sparse_attention_plan_amd import api, inputs
+    from structured_sparse_attention_plan_amd import _cowa as C
+    dev = "cuda:0"
+    out = {}
+
+    def fwd_bwd(L, near, mode, dtype=torch.bfloat16, hq=HQ, hkv=HKV, d=D, sink=SINK, bwd=True,
+                steps=5, warmup=2):
+        win = api.make_window(L, hkv, sink, near, 0, mode)
+        scale = d ** -0.5
+        pf = api.problem(1, L, L, hq, hkv, d, dtype, scale, win)
+        plan_f = api.build_plan("fwd", pf, dev)
+        q, k, v, do = inputs.attention_inputs(1, L, L, hq, hkv, d, seed=seed, device=dev,
+                                              dtype=dtype, with_dout=True)
+        o = torch.empty_like(q)
+        lse = torch.empty((1, hq, L), dtype=torch.float32, device=dev)
+        E = plan_f.info.edges * (hq // hkv)
+        r = {"edges": E, "window": {"sink": win.sink, "near": win.near_w, "band_width": win.lr,
+                                    "bands": mode}}
+        r["fwd_ms"] = _events_ms(lambda: api.fwd(q, k, v, win, scale, plan=plan_f, out=o, lse=lse),
+                                 steps, warmup)
+        r["fwd_tflops"] = 4 * d * E / (r["fwd_ms"] * 1e-3) / 1e12
+        if bwd:
+            plan_b = api.build_plan("bwd", pf, dev)
+            grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+            ws = torch.empty(api.workspace_size("bwd", pf), dtype=torch.uint8, device=dev)
+            r["bwd_ms"] = _events_ms(lambda: api.bwd(q, k, v, o, lse, do, win, scale, plan=plan_b,
+                                                     grads=grads, workspace=ws), steps, warmup)
+            r["bwd_tflops"] = 10 * d * E / (r["bwd_ms"] * 1e-3) / 1e12
+            r["fwd_bwd_ms"] = r["fwd_ms"] + r["bwd_ms"]
+        del q, k, v, do, o, lse
+        torch.cuda.empty_cache()
+        return r
+
+    # fp32 forward, L=1024, Hq=4, Hkv=2, D=64, sink 64, near 128, 64x64 tiles
+    out["fwd_f32_1k"] = fwd_bwd(1024, 128, "complementary", dtype=torch.float32, hq=4, hkv=2, d=64,
+                                sink=64, bwd=False, steps=20, warmup=5)
+    # 32K prefill forward
+    out["fwd_32k"] = fwd_bwd(32768, 2048, "complementary", bwd=False, steps=10, warmup=3)
+    out["fwd_32k"]["frac_of_mfma_peak"] = out["fwd_32k"]["fwd_tflops"] / MFMA_BF16_PEAK_TFLOPS
+    # coverage ablation at 32K, forward + backward
+    abl = {m: fwd_bwd(32768, 2048, m, steps=5, warmup=2)
+           for m in ("complementary", "duplicated", "dense")}
+    for m in ("complementary", "duplicated"):
+        abl[m]["dense_over_this_ms"] = abl["dense"]["fwd_bwd_ms"] / abl[m]["fwd_bwd_ms"]
+        abl[m]["dense_over_this_edges"] = abl["dense"]["edges"] / abl[m]["edges"]
+    out["ablation_32k"] = abl
+    # dense causal at 128K with the same kernels: forward + backward, and decode
+    dense = fwd_bwd(L, NEAR, "dense", steps=2, warmup=1)
+    win_d = api.make_window(L, HKV, SINK, NEAR, 0, "dense")
+    pdd = api.problem(DEC_B, 1, L, HQ, HKV, D, torch.bfloat16, D ** -0.5, win_d)
+    plan_dd = api.build_plan("decode", pdd, dev)
+    qd, kc, vc = inputs.attention_inputs(DEC_B, 1, L, HQ, HKV, D, seed=seed + 10, device=dev)
+    wsd = torch.empty(api.workspace_size("decode", pdd), dtype=torch.uint8, device=dev)
+    od = torch.empty_like(qd)
+    lsed = torch.empty((DEC_B, HQ), dtype=torch.float32, device=dev)
+    dense["decode_us_per_step"] = 1e3 * _events_ms(
+        lambda: api.decode(qd, kc, vc, win_d, D ** -0.5, plan=plan_dd, out=od, lse=lsed, workspace=wsd),
+        10, 3)
+    dense_dec_bytes = plan_dd.info.edges * DEC_B * 2 * D * 2
+    out["dense_128k"] = dense
+    out["cowa_vs_dense_128k"] = {
+        "fwd_speedup": dense["fwd_ms"] / main_fwd_ms,
+        "bwd_speedup": dense["bwd_ms"] / main_bwd_ms,
+        "fwd_bwd_speedup": dense["fwd_bwd_ms"] / main_fb_ms,
+        "decode_speedup": dense["decode_us_per_step"] / (main_dec_ms * 1e3),
+        "ideal_edge_ratio": dense["edges"] / main_E,
+        "ideal_decode_byte_ratio": dense_dec_bytes / main_dec_bytes,
+        "pages_context": "the pages report 7.4x forward, 8.6x backward and 3.0x decode over "
+                         "dense attention at 128K on 8 H100 with tensor parallelism 8, at a "
+                         "window geometry they do not state; context only",
+    }
+    return out
 
 
 def main():
@@ -317,12 +426,19 @@ def main():
         "planner_ms": planner_ms,
         "roofline": roof,
     }
+    if not args.no_extras:
+        out["extras"] = extras(args.seed, fb_ms, ms["fwd"],
+                               ms["bwd_delta"] + ms["bwd_dq"] + ms["bwd_dkdv"], ms["decode"], E,
+                               dec_bytes)
     if not args.no_cpu_baseline:
         import oracle
         rng = np.random.default_rng(args.seed + 100)
         rows = np.sort(rng.choice(L, size=args.cpu_rows, replace=False))
         ow = oracle.Window(win.sink, win.near_w, win.gap, win.lr, oracle.COMPLEMENTARY)
         out["cpu_baseline"] = cpu_baseline(q, k, v, ow, rows)
+        # extrapolated (not measured): the whole 128K forward at the sample's edge rate
+        out["cpu_baseline"]["extrapolated_full_fwd_s"] = (
+            4 * D * E / (out["cpu_baseline"]["value"] * 1e12))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
