@@ -245,12 +245,27 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
+template <int V>
+using IC = std::integral_constant<int, V>;
+
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  // [buffer][Q, dO][rows]: swizzled 256-byte rows (lds_swz); the dO tile of a buffer sits
-  // at a fixed distance from its Q tile, so one address serves both
-  __shared__ __attribute__((aligned(1024))) __bf16 sQD[4 * QTILE];
-  __shared__ __attribute__((aligned(16))) float sLT[4 * ROWS];  // [buffer][LSE*log2e, Delta]
-  __shared__ int sRt[ROWS];                                     // row -> token in the q-block
+  // Q and dO of a q-block, [Q, dO][rows] with swizzled 256-byte rows (lds_swz); dO sits at
+  // a fixed distance from Q, so one address serves both.  Two separate arrays (not one
+  // indexed by the buffer): every read names the array it reads, so the compiler can tell
+  // it apart from the copies in flight into the other one and does not wait for them.
+  __shared__ __attribute__((aligned(1024))) __bf16 sQD0[2 * QTILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQD1[2 * QTILE];
+  __shared__ __attribute__((aligned(16))) float sLT0[2 * ROWS];  // [LSE * log2 e, Delta][rows]
+  __shared__ __attribute__((aligned(16))) float sLT1[2 * ROWS];
+  __shared__ int sRt[ROWS];  // row -> token in the q-block
+  auto tiles = [&](auto bufc) -> __bf16* {
+    if constexpr (decltype(bufc)::value == 0) return sQD0;
+    else return sQD1;
+  };
+  auto lts = [&](auto bufc) -> float* {
+    if constexpr (decltype(bufc)::value == 0) return sLT0;
+    else return sLT1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -271,6 +286,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const __bf16* dO = (const __bf16*)a.dout;
 
   if (tid < ROWS) sRt[tid] = tid / G;
+  // Rows of the last q-block past Lq are outside the copies' range: their LDS keeps what
+  // it held.  Cleared once here, it only ever holds zeros or earlier finite rows, which
+  // the row's LSE of +inf turns into P = 0.
+#pragma unroll
+  for (int i = 0; i < 2 * QTILE / (256 * 8); ++i) {
+    store16(sQD0 + 8 * (tid + 256 * i), zero_bf16x8());
+    store16(sQD1 + 8 * (tid + 256 * i), zero_bf16x8());
+  }
+  __syncthreads();  // cleared before any copy lands
 
   // this lane's key (column of S and dP)
   const int j = kb * BK + wave * 32 + n;
@@ -282,6 +306,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for (int dd = 0; dd < 8; ++dd) {
       kf[dd] = kvalid ? load16(K + ko + 16 * dd) : zero_bf16x8();
       vf[dd] = kvalid ? load16(V + ko + 16 * dd) : zero_bf16x8();
+      // held in AGPRs (MFMA reads its A/B operands from either file): leaves the VGPRs
+      // to the pipeline's temporaries
+      asm volatile("" : "+a"(kf[dd]));
+      asm volatile("" : "+a"(vf[dd]));
     }
   }
 
@@ -295,24 +323,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // row block rb adds 32 rb rows and half hf adds 16 rows to these):
   //   operand reads (S, dP): row n, columns 16 dd + 8 h2;
   //   transposed reads (dV, dK): rows vrow (+8), columns 32 db + vcol.
+  // Under the XOR swizzle the element offset for dd (resp. db) is the dd = 0 (db = 0)
+  // offset with bits 4-6 (5-6) XORed by dd (db), so three registers hold them all.
   const int gg = lane >> 4, j16 = lane & 15;
   const int vrow = 4 * (gg >> 1) + (j16 >> 2);
   const int vcol = 16 * (gg & 1) + 4 * (j16 & 3);
-  int ofs_a[8], ofs_t[2][4];
-#pragma unroll
-  for (int dd = 0; dd < 8; ++dd) ofs_a[dd] = lds_swz(n, 16 * dd + 8 * h2);
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) ofs_t[p][db] = lds_swz(vrow + 8 * p, 32 * db + vcol);
+  int ofs_a0 = lds_swz(n, 8 * h2);
+  int ofs_t0[2] = {lds_swz(vrow, vcol), lds_swz(vrow + 8, vcol)};
+  auto ofs_a = [&](int dd) { return ofs_a0 ^ (dd << 4); };
+  auto ofs_t = [&](int p, int db) { return ofs_t0[p] ^ (db << 5); };
 
   // Direct copies: wave w fills rows 32 w .. 32 w + 31 of a tile, 4 rows per copy; lane L
   // of copy u fills row r = 32 w + 4 u + L / 16, physical chunk L % 16, i.e. logical chunk
-  // (L % 16) ^ lds_sw(r) of that row.  off_u[u] is that chunk's element offset from the
+  // (L % 16) ^ lds_sw(r) of that row.  voff_u[u] is that chunk's byte offset from the
   // q-block's first token: token tk = r / G (rows past the q-block take its last token;
-  // their LSE is +inf, so they contribute nothing) times Hq * D, plus the head's columns.
+  // their LSE is +inf) times Hq * D, plus the head's columns.
   const int HqD = a.Hq * D;
-  int off_u[8];
+  uint32_t voff_u[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int r = wave * 32 + 4 * u + (lane >> 4);
@@ -321,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       rt = Bq - 1;
       g = 0;
     }
-    off_u[u] = rt * HqD + (h * G + g) * D + 8 * ((lane & 15) ^ lds_sw(r));
+    voff_u[u] = 2u * (uint32_t)(rt * HqD + (h * G + g) * D + 8 * ((lane & 15) ^ lds_sw(r)));
   }
   // LSE / Delta staging: thread tid < ROWS owns row tid of the next q-block.  The raw
   // loaded values are only touched when stored to LDS (after the wait that precedes the
@@ -329,65 +356,44 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int my_rt = tid / G, my_g = tid - my_rt * G;
   float plse = 0.f, pdel = 0.f;
   bool pvalid = false;
+  // LSE and Delta rows of this KV head's G query heads, [G, Lq] each
+  const int64_t lt_base = ((int64_t)b * a.Hq + h * G) * a.Lq;
+  const __amdgpu_buffer_rsrc_t r_lse = make_rsrc(a.lse + lt_base, (int64_t)G * a.Lq * 4);
+  const __amdgpu_buffer_rsrc_t r_del = make_rsrc(a.delta + lt_base, (int64_t)G * a.Lq * 4);
 
   const int e0 = load_uniform(a.col_ptr, item);
   const int n_ent = load_uniform(a.col_ptr, item + 1) - e0;
 
-  auto load_entry = [&](int qb, int buf) {
+  // Copies of q-block qb's Q and dO rows: prepare_entry builds the two buffer resources
+  // (scalar; the range ends at token Lq, so rows past Lq read zeros; an empty range when
+  // there is no next q-block, so the copies then touch no memory) and loads the LSE /
+  // Delta of its rows into registers; copy(i) issues copy i of 16 (u = i / 2, Q then dO)
+  // into buffer bufc, so the copies can be spread over MFMA slots.
+  __amdgpu_buffer_rsrc_t rq_n, rd_n;
+  auto prepare_entry = [&](int qb, bool real) {
     const int t0 = qb * Bq;
     const int64_t base = ((int64_t)b * a.Lq + t0) * HqD;
-    __bf16* dq_ = sQD + 2 * buf * QTILE + wave * 32 * D;
-    if (t0 + Bq <= a.Lq) {
-      // uniform base + unsigned 32-bit byte offset: the scalar-base form of the copy
-      const char* qs = (const char*)(Q + base);
-      const char* ds_ = (const char*)(dO + base);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        g2lds(qs + (uint32_t)(2 * off_u[u]), dq_ + 4 * u * D);
-        g2lds(ds_ + (uint32_t)(2 * off_u[u]), dq_ + QTILE + 4 * u * D);
-      }
-    } else {  // last q-block: tokens past Lq read token Lq - 1
-      const int last = a.Lq - 1 - t0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int tk = off_u[u] / HqD;
-        const int o = min(tk, last) * HqD + (off_u[u] - tk * HqD);
-        g2lds(Q + base + o, dq_ + 4 * u * D);
-        g2lds(dO + base + o, dq_ + QTILE + 4 * u * D);
-      }
-    }
+    const int64_t bytes = real ? (int64_t)(a.Lq - t0) * HqD * 2 : 0;
+    rq_n = make_rsrc(Q + base, bytes);
+    rd_n = make_rsrc(dO + base, bytes);
     if (tid < ROWS) {
-      const int t = t0 + my_rt;
-      pvalid = my_rt < Bq && t < a.Lq;
-      const int64_t si = ((int64_t)b * a.Hq + h * G + my_g) * a.Lq + (pvalid ? t : 0);
-      plse = a.lse[si];
-      pdel = a.delta[si];
+      pvalid = my_rt < Bq && t0 + my_rt < a.Lq;
+      // rows past Lq read row Lq - 1 (in bounds; discarded by pvalid)
+      const uint32_t vo = 4u * (uint32_t)(my_g * a.Lq + min(t0 + my_rt, a.Lq - 1));
+      plse = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_lse, vo, 0, 0));
+      pdel = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_del, vo, 0, 0));
     }
+  };
+  auto copy = [&](int i, auto bufc) {
+    __bf16* dst = tiles(bufc) + wave * 32 * D + 4 * (i >> 1) * D + ((i & 1) ? QTILE : 0);
+    buf2lds((i & 1) ? rd_n : rq_n, voff_u[i >> 1], dst);
   };
   // rows with no token or no visible key: LSE +inf (P = 0) and Delta 0
-  auto store_lse = [&](int buf) {
+  auto store_lse = [&](auto bufc) {
     if (tid < ROWS) {
-      sLT[2 * buf * ROWS + tid] = (pvalid && plse != -INFINITY) ? plse * kLog2e : INFINITY;
-      sLT[(2 * buf + 1) * ROWS + tid] = pvalid ? pdel : 0.f;
-    }
-  };
-
-  // S, dP of row block rb (32 rows) of buffer buf: 16 MFMAs, operands one dd ahead
-  auto scores = [&](int buf, int rb, f32x16& s, f32x16& dp) {
-    const __bf16* qt = sQD + 2 * buf * QTILE + 4096 * rb;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-    bf16x8 qa[2], da[2];
-    qa[0] = load16(qt + ofs_a[0]);
-    da[0] = load16(qt + QTILE + ofs_a[0]);
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      if (dd + 1 < 8) {
-        qa[(dd + 1) & 1] = load16(qt + ofs_a[dd + 1]);
-        da[(dd + 1) & 1] = load16(qt + QTILE + ofs_a[dd + 1]);
-      }
-      s = mfma32x32x16(qa[dd & 1], kf[dd], s);
-      dp = mfma32x32x16(da[dd & 1], vf[dd], dp);
+      float* lt = lts(bufc);
+      lt[tid] = (pvalid && plse != -INFINITY) ? plse * kLog2e : INFINITY;
+      lt[ROWS + tid] = pvalid ? pdel : 0.f;
     }
   };
   // boundary q-block: the window predicate per element (S = -inf where hidden)
@@ -413,24 +419,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   auto as_bf16x8 = [](const uint32_t (&w)[4]) { return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]}); };
 
   if (n_ent > 0) {
-    int ent_c = load_uniform(a.col_ent, e0);  // entry of the current block g
-    // entry of q-block e + 1, read one q-block before it is needed
+    int ent_c = load_uniform(a.col_ent, e0);  // entry of the current q-block
+    // entry of the next q-block, read one q-block before it is needed
     int ent_ahead = n_ent > 1 ? load_uniform(a.col_ent, e0 + 1) : 0;
-    load_entry(ent_c >> 1, 0);
+    int ent_n = ent_c;
+    prepare_entry(ent_c >> 1, true);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) copy(i, IC<0>{});
     wait_loads_and_barrier();
-    store_lse(0);
+    store_lse(IC<0>{});
     __syncthreads();
 
     Carry wA, wB;
     {  // prologue: S, dP, P (split) and dS of block 0
       f32x16 s, dp;
-      scores(0, 0, s, dp);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        s = mfma32x32x16(load16(sQD0 + ofs_a(dd)), kf[dd], s);
+        dp = mfma32x32x16(load16(sQD0 + QTILE + ofs_a(dd)), vf[dd], dp);
+      }
       if (ent_c & 1) mask(s, 0, ent_c >> 1);
       float pr[16];
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 l4 = *(const f32x4*)(sLT + 8 * i4 + 4 * h2);
-        const f32x4 t4 = *(const f32x4*)(sLT + ROWS + 8 * i4 + 4 * h2);
+        const f32x4 l4 = *(const f32x4*)(sLT0 + 8 * i4 + 4 * h2);
+        const f32x4 t4 = *(const f32x4*)(sLT0 + ROWS + 8 * i4 + 4 * h2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           pr[4 * i4 + i] = __builtin_amdgcn_exp2f(fmaf(s[4 * i4 + i], a.scale_log2, -l4[i]));
@@ -441,51 +456,54 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int k = 0; k < 8; ++k) split_pair(pr[2 * k], pr[2 * k + 1], wA.pa[k >> 2][k & 3], wA.pl[k >> 2][k & 3]);
     }
 
-    int ent_n = ent_c;  // entry of block g + 1 once it starts a new q-block
-    const int ng = 4 * n_ent;
-    // One pipeline step.  Phase 1: S, dP of block g + 1 (16 MFMAs) with the hi/lo split of
-    // dS(g) between them.  Phase 2: dV, dK of block g (32 MFMAs) with P, dS of block g + 1
-    // and the split of P(g + 1) between them.  has_next (compile time) is false only for
-    // the last block.
-    auto step = [&](const int g, auto has_next_c, const Carry& cur, Carry& nxt) {
-      constexpr bool has_next = decltype(has_next_c)::value;
-      const int rb = g & 3;
-      const int e = g >> 2;
-      const int buf = e & 1;
-      if (rb == 0) {
-        // every wave is done with q-block e - 1: its buffer takes q-block e + 1
+    // One pipeline step for row block RB of the q-block in buffer BUF (both compile-time).
+    // Phase 1: S, dP of the next block (16 MFMAs) with the hi/lo split of dS(g) between
+    // them.  Phase 2: dV, dK of block g (32 MFMAs) with P, dS of the next block and the
+    // split of its P between them.  After the item's last block the "next" block is the
+    // resident other buffer's first block: computed and discarded, so the step has no
+    // branches inside its interleaved parts.
+    auto step = [&](auto rbc, auto bufc, const int e, const Carry& cur, Carry& nxt) {
+      constexpr int RB = decltype(rbc)::value;
+      constexpr int BUF = decltype(bufc)::value;
+      constexpr int RB1 = (RB + 1) & 3;
+      constexpr int BUF1 = RB == 3 ? BUF ^ 1 : BUF;
+      const bool more = e + 1 < n_ent;  // a next q-block exists
+      // taken afresh each step, so the per-read XORs stay in the step instead of being
+      // hoisted into 16 long-lived registers
+      asm volatile("" : "+v"(ofs_a0), "+v"(ofs_t0[0]), "+v"(ofs_t0[1]));
+      if constexpr (RB == 0) {
+        // every wave is done with q-block e - 1: its buffer takes q-block e + 1, copied
+        // during the phase-2 MFMAs of this step and the next
         __syncthreads();
-        if (e + 1 < n_ent) {
-          ent_n = ent_ahead;
-          load_entry(ent_n >> 1, buf ^ 1);
-          if (e + 2 < n_ent) ent_ahead = load_uniform(a.col_ent, e0 + e + 2);
-        }
+        if (more) ent_n = ent_ahead;
+        prepare_entry(ent_n >> 1, more);
+        if (e + 2 < n_ent) ent_ahead = load_uniform(a.col_ent, e0 + e + 2);
       }
-      const int ent_g1 = (rb == 3) ? ent_n : ent_c;  // entry of block g + 1
-      const int buf1 = (rb == 3) ? buf ^ 1 : buf;
-      const int rb1 = (rb + 1) & 3;
-      if (rb == 3 && has_next) {  // q-block e + 1 resident
-        __builtin_amdgcn_s_waitcnt(0x0f70);
-        store_lse(buf1);
-        __syncthreads();
+      const int ent_g1 = RB == 3 ? ent_n : ent_c;  // entry of the next block
+      if constexpr (RB == 3) {
+        if (more) {  // q-block e + 1 resident
+          __builtin_amdgcn_s_waitcnt(0x0f70);
+          store_lse(IC<BUF ^ 1>{});
+          __syncthreads();
+        }
       }
 
       // ---- phase 1
-      const __bf16* tg = sQD + 2 * buf * QTILE + 4096 * rb;     // Q rows of block g (dO: + QTILE)
-      const __bf16* t1 = sQD + 2 * buf1 * QTILE + 4096 * rb1;  // Q rows of block g + 1
+      const __bf16* tg = tiles(bufc) + 4096 * RB;     // Q rows of block g (dO: + QTILE)
+      const __bf16* t1 = tiles(IC<BUF1>{}) + 4096 * RB1;  // Q rows of the next block
+      // operands of the next block's S, dP: four dd steps in flight, dd + 4 read when dd's
+      // pair of MFMAs has been issued
       bf16x8 qa[8], da[8];
-      if constexpr (has_next) {
 #pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          qa[dd] = load16(t1 + ofs_a[dd]);
-          da[dd] = load16(t1 + QTILE + ofs_a[dd]);
-        }
+      for (int dd = 0; dd < 4; ++dd) {
+        qa[dd] = load16(t1 + ofs_a(dd));
+        da[dd] = load16(t1 + QTILE + ofs_a(dd));
       }
       bf16x8 dt[2][4], qt[2][4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        dt[0][db] = join(lds_read_tr4(tg + QTILE + ofs_t[0][db]), lds_read_tr4(tg + QTILE + ofs_t[1][db]));
-        qt[0][db] = join(lds_read_tr4(tg + ofs_t[0][db]), lds_read_tr4(tg + ofs_t[1][db]));
+        dt[0][db] = join(lds_read_tr4(tg + QTILE + ofs_t(0, db)), lds_read_tr4(tg + QTILE + ofs_t(1, db)));
+        qt[0][db] = join(lds_read_tr4(tg + ofs_t(0, db)), lds_read_tr4(tg + ofs_t(1, db)));
       }
       f32x16 sn, dpn;
 #pragma unroll
@@ -494,10 +512,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        if constexpr (has_next) {
-          const int dd = x >> 1;
-          if (x & 1) dpn = mfma32x32x16(da[dd], vf[dd], dpn);
-          else sn = mfma32x32x16(qa[dd], kf[dd], sn);
+        const int dd = x >> 1;
+        if (x & 1) dpn = mfma32x32x16(da[dd], vf[dd], dpn);
+        else sn = mfma32x32x16(qa[dd], kf[dd], sn);
+        if ((x & 1) && dd + 4 < 8) {
+          qa[dd + 4] = load16(t1 + ofs_a(dd + 4));
+          da[dd + 4] = load16(t1 + QTILE + ofs_a(dd + 4));
         }
         __builtin_amdgcn_sched_barrier(0);
         if ((x & 1) == 0) {
@@ -508,18 +528,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (has_next) {
-        if (ent_g1 & 1) mask(sn, rb1, ent_g1 >> 1);
-      }
+      if (ent_g1 & 1) mask(sn, RB1, ent_g1 >> 1);
 
-      // ---- phase 2: dV, dK of block g, interleaved with P, dS of block g + 1
-      const float* lt = sLT + 2 * buf1 * ROWS + 32 * rb1 + 4 * h2;  // LSE; Delta at + ROWS
+      // ---- phase 2: dV, dK of block g, interleaved with P, dS of the next block
+      const float* lt = lts(IC<BUF1>{}) + 32 * RB1 + 4 * h2;  // LSE; Delta at + ROWS
       f32x4 l4[4], t4[4];
       float pr[16];
-      if constexpr (has_next) {
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) l4[i4] = *(const f32x4*)(lt + 8 * i4);
-      }
+      for (int i4 = 0; i4 < 4; ++i4) l4[i4] = *(const f32x4*)(lt + 8 * i4);
       const bf16x8 pa[2] = {as_bf16x8(cur.pa[0]), as_bf16x8(cur.pa[1])};
       const bf16x8 pl[2] = {as_bf16x8(cur.pl[0]), as_bf16x8(cur.pl[1])};
       const bf16x8 sa[2] = {as_bf16x8(wsa[0]), as_bf16x8(wsa[1])};
@@ -541,42 +557,49 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         if (x >= 9 && x <= 16) {
           const int db1 = (x - 9) >> 1;
           const __bf16* th = tg + 2048 + (((x - 9) & 1) ? 0 : QTILE);
-          const bf16x8 v = join(lds_read_tr4(th + ofs_t[0][db1]), lds_read_tr4(th + ofs_t[1][db1]));
+          const bf16x8 v = join(lds_read_tr4(th + ofs_t(0, db1)), lds_read_tr4(th + ofs_t(1, db1)));
           if ((x - 9) & 1) qt[1][db1] = v;
           else dt[1][db1] = v;
         }
+        // copies of the next q-block: 8 in each of the first two steps, one every 2 MFMAs
+        if constexpr (RB < 2)
+          if (x >= 17 && (x & 1)) copy(8 * RB + ((x - 17) >> 1), IC<BUF ^ 1>{});
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (has_next) {
-          // P (exp) in steps 0..15, dS 4 steps behind, the split of P pair q in step 2q + 17
-          if (x < 16) {
-            pr[x] = __builtin_amdgcn_exp2f(fmaf(pin(sn[x]), a.scale_log2, -l4[x >> 2][x & 3]));
-            pin_out(pr[x]);
-          }
-          if ((x & 3) == 0 && x < 16) t4[x >> 2] = *(const f32x4*)(lt + ROWS + 2 * x);
-          if (x >= 4 && x < 20) {
-            const int i = x - 4;
-            nxt.ds[i] = pr[i] * (pin(dpn[i]) - t4[i >> 2][i & 3]);
-            pin_out(nxt.ds[i]);
-          }
-          if (x >= 16 && (x & 1)) {
-            const int q = (x - 17) >> 1;
-            split_pair(pin(pr[2 * q]), pin(pr[2 * q + 1]), nxt.pa[q >> 2][q & 3], nxt.pl[q >> 2][q & 3]);
-            pin_out(nxt.pa[q >> 2][q & 3]);
-            pin_out(nxt.pl[q >> 2][q & 3]);
-          }
+        // P (exp) in steps 0..15, dS 4 steps behind, the split of P pair q in step 2q + 17
+        if (x < 16) {
+          pr[x] = __builtin_amdgcn_exp2f(fmaf(pin(sn[x]), a.scale_log2, -l4[x >> 2][x & 3]));
+          pin_out(pr[x]);
+        }
+        if ((x & 3) == 0 && x < 16) t4[x >> 2] = *(const f32x4*)(lt + ROWS + 2 * x);
+        if (x >= 4 && x < 20) {
+          const int i = x - 4;
+          nxt.ds[i] = pr[i] * (pin(dpn[i]) - t4[i >> 2][i & 3]);
+          pin_out(nxt.ds[i]);
+        }
+        if (x >= 16 && (x & 1)) {
+          const int q = (x - 17) >> 1;
+          split_pair(pin(pr[2 * q]), pin(pr[2 * q + 1]), nxt.pa[q >> 2][q & 3], nxt.pl[q >> 2][q & 3]);
+          pin_out(nxt.pa[q >> 2][q & 3]);
+          pin_out(nxt.pl[q >> 2][q & 3]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (rb == 3) ent_c = ent_n;
+      if constexpr (RB == 3) ent_c = ent_n;
     };
-    // steps in pairs, the carried values alternating between wA and wB
-    int g = 0;
-    for (; g + 2 < ng; g += 2) {
-      step(g, std::true_type{}, wA, wB);
-      step(g + 1, std::true_type{}, wB, wA);
+    auto entry = [&](auto bufc, const int e) {
+      step(IC<0>{}, bufc, e, wA, wB);
+      step(IC<1>{}, bufc, e, wB, wA);
+      step(IC<2>{}, bufc, e, wA, wB);
+      step(IC<3>{}, bufc, e, wB, wA);
+    };
+    // q-blocks alternate between the two buffers
+    for (int e = 0; e < n_ent; e += 2) {
+      entry(IC<0>{}, e);
+      if (e + 1 < n_ent) entry(IC<1>{}, e + 1);
     }
-    step(g, std::true_type{}, wA, wB);
-    step(g + 1, std::false_type{}, wB, wA);
+    // the last q-block's steps issued copies with an empty range: let them retire before
+    // the work group's LDS can be handed on
+    __builtin_amdgcn_s_waitcnt(0x0f70);
   }
 
   // element i of accK[db] / accV[db]: key 32 wave + 8 (i / 4) + 4 h2 + i % 4, dim 32 db + n

@@ -71,6 +71,31 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p, int64_t i) {
   return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
+// A pointer the compiler can prove wave-uniform (held in scalar registers), so that
+// uniform + 32-bit per-lane offset addressing uses the scalar-base form of the load.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T*)(((uint64_t)hi << 32) | lo);
+}
+
+// Raw buffer resource over [base, base + bytes): loads through it take a 32-bit per-lane
+// byte offset (plus a scalar one) and return zeros past `bytes`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes < 0x7fffffff ? (int)bytes : 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr((const char*)base), (short)0, n,
+                                           0x00020000);
+}
+
+// One 1 KB direct buffer->LDS copy per wave: lane L moves the 16 bytes at byte offset
+// voff of the resource to lds + 16 L (lds is wave-uniform).
+__device__ __forceinline__ void buf2lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, __bf16* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           (int)voff, 0, 0, 0);
+}
+
 // One 1 KB direct global->LDS copy per wave: lane L moves the 16 bytes at src (its own
 // address) to lds + 16 L (lds is wave-uniform).
 __device__ __forceinline__ void g2lds(const void* src, __bf16* lds) {
