@@ -509,6 +509,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sn[i] = dpn[i] = 0.f;
       uint32_t wsa[2][4], wsl[2][4];
+      float dsv[16];
+      dsv[0] = pin(cur.ds[0]);
+      dsv[1] = pin(cur.ds[1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
@@ -520,9 +523,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           da[dd + 4] = load16(t1 + QTILE + ofs_a(dd + 4));
         }
         __builtin_amdgcn_sched_barrier(0);
+        // pair q split in step 2q; its inputs are taken one step earlier and its outputs
+        // fenced one step later, so nothing waits on a result in its own step
         if ((x & 1) == 0) {
           const int q = x >> 1;
-          split_pair(pin(cur.ds[2 * q]), pin(cur.ds[2 * q + 1]), wsa[q >> 2][q & 3], wsl[q >> 2][q & 3]);
+          split_pair(dsv[2 * q], dsv[2 * q + 1], wsa[q >> 2][q & 3], wsl[q >> 2][q & 3]);
+        }
+        if ((x & 1) && x < 15) {
+          const int q = (x + 1) >> 1;
+          dsv[2 * q] = pin(cur.ds[2 * q]);
+          dsv[2 * q + 1] = pin(cur.ds[2 * q + 1]);
+        }
+        if (x & 1) {
+          const int q = x >> 1;
           pin_out(wsa[q >> 2][q & 3]);
           pin_out(wsl[q >> 2][q & 3]);
         }
@@ -540,6 +553,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const bf16x8 pl[2] = {as_bf16x8(cur.pl[0]), as_bf16x8(cur.pl[1])};
       const bf16x8 sa[2] = {as_bf16x8(wsa[0]), as_bf16x8(wsa[1])};
       const bf16x8 sl[2] = {as_bf16x8(wsl[0]), as_bf16x8(wsl[1])};
+      float snv[2], dpv[2];
+      snv[0] = pin(sn[0]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int x = 0; x < 32; ++x) {
@@ -565,25 +580,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         if constexpr (RB < 2)
           if (x >= 17 && (x & 1)) copy(8 * RB + ((x - 17) >> 1), IC<BUF ^ 1>{});
         __builtin_amdgcn_sched_barrier(0);
-        // P (exp) in steps 0..15, dS 4 steps behind, the split of P pair q in step 2q + 17
-        if (x < 16) {
-          pr[x] = __builtin_amdgcn_exp2f(fmaf(pin(sn[x]), a.scale_log2, -l4[x >> 2][x & 3]));
-          pin_out(pr[x]);
-        }
+        // P (exp) in steps 0..15, dS 4 steps behind, the split of P pair q in step 2q + 17.
+        // Inputs are taken (pin) one step before use and results fenced (pin_out) one step
+        // after they are made: each piece stays in its slot without stalling on itself.
+        if (x < 16) pr[x] = __builtin_amdgcn_exp2f(fmaf(snv[x & 1], a.scale_log2, -l4[x >> 2][x & 3]));
+        if (x + 1 < 16) snv[(x + 1) & 1] = pin(sn[x + 1]);
+        if (x >= 1 && x <= 16) pin_out(pr[x - 1]);
         if ((x & 3) == 0 && x < 16) t4[x >> 2] = *(const f32x4*)(lt + ROWS + 2 * x);
         if (x >= 4 && x < 20) {
           const int i = x - 4;
-          nxt.ds[i] = pr[i] * (pin(dpn[i]) - t4[i >> 2][i & 3]);
-          pin_out(nxt.ds[i]);
+          nxt.ds[i] = pr[i] * (dpv[i & 1] - t4[i >> 2][i & 3]);
         }
+        if (x >= 3 && x < 19) dpv[(x - 3) & 1] = pin(dpn[x - 3]);
+        if (x >= 5 && x <= 20) pin_out(nxt.ds[x - 5]);
         if (x >= 16 && (x & 1)) {
           const int q = (x - 17) >> 1;
-          split_pair(pin(pr[2 * q]), pin(pr[2 * q + 1]), nxt.pa[q >> 2][q & 3], nxt.pl[q >> 2][q & 3]);
+          split_pair(pr[2 * q], pr[2 * q + 1], nxt.pa[q >> 2][q & 3], nxt.pl[q >> 2][q & 3]);
+        }
+        if (x >= 18 && !(x & 1)) {
+          const int q = (x - 18) >> 1;
           pin_out(nxt.pa[q >> 2][q & 3]);
           pin_out(nxt.pl[q >> 2][q & 3]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      pin_out(nxt.pa[1][3]);
+      pin_out(nxt.pl[1][3]);
       if constexpr (RB == 3) ent_c = ent_n;
     };
     auto entry = [&](auto bufc, const int e) {
