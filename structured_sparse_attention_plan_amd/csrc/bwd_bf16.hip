@@ -31,7 +31,16 @@ namespace {
 constexpr int D = 128;
 constexpr int ROWS = kBwdRows;  // 128 query rows per q-block
 constexpr int BK = kBwdBk;      // 128 keys per k-block
-constexpr int SUB = 64;         // keys staged per LDS sub-tile in the dq kernel
+
+// Returns x unchanged, but the value is taken at this point of the program: computations
+// that use the result cannot be hoisted above it (it pins VALU work to its pipeline slot).
+__device__ __forceinline__ float pin(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ void pin_out(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin_out(float& x) { asm volatile("" : "+v"(x)); }
 
 // ------------------------------------------------------------------------ Delta
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
@@ -61,17 +70,48 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   }
 }
 
+template <int V>
+using IC = std::integral_constant<int, V>;
+
 // ------------------------------------------------------------------------ dQ
+// One work item = (KV head, q-block of 128 rows), 4 waves x 32 rows; each lane owns one
+// query row (column of the transposed products) and keeps its Q and dO fragments in
+// registers.  The item walks its row list as 64-key tiles t (two per listed 128-key
+// block).  Iteration t is one block of 48 MFMAs, the dQ^T += K^T dS^T products of tile
+// t-1 (16) then S^T = K Q^T and dP^T = V dO^T of tile t+1 (32), with the VALU work of
+// tile t (P, dS and their bf16 packing) spread between them by scheduling fences.  K
+// and V tiles are copied straight into LDS two tiles ahead: four K buffers (tiles t-1,
+// t+1 read, t+2 arriving) and two V buffers (t+1 read, t+2 arriving), each its own
+// array, indexed at compile time (the tile loop is unrolled by 4), so the compiler can
+// tell the reads from the copies in flight.
+constexpr int QBK = 64;          // keys per tile
+constexpr int QTL = QBK * D;     // elements per K or V tile (16 KB)
+
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 sK[SUB * D];  // swizzled rows (lds_swz)
-  __shared__ __attribute__((aligned(16))) __bf16 sV[SUB * D];
+  __shared__ __attribute__((aligned(16384))) __bf16 sK0[QTL];
+  __shared__ __attribute__((aligned(16384))) __bf16 sK1[QTL];
+  __shared__ __attribute__((aligned(16384))) __bf16 sK2[QTL];
+  __shared__ __attribute__((aligned(16384))) __bf16 sK3[QTL];
+  __shared__ __attribute__((aligned(16384))) __bf16 sV0[QTL];
+  __shared__ __attribute__((aligned(16384))) __bf16 sV1[QTL];
+  auto kbuf = [&](auto c) -> __bf16* {
+    constexpr int i = decltype(c)::value & 3;
+    if constexpr (i == 0) return sK0;
+    else if constexpr (i == 1) return sK1;
+    else if constexpr (i == 2) return sK2;
+    else return sK3;
+  };
+  auto vbuf = [&](auto c) -> __bf16* {
+    if constexpr ((decltype(c)::value & 1) == 0) return sV0;
+    else return sV1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int n = lane & 31;
   const int h2 = lane >> 5;
-  const int item = a.row_order[blockIdx.x];
+  const int item = load_uniform(a.row_order, blockIdx.x);
   const int b = blockIdx.y;
   const int h = item / a.nqb;
   const int qb = item - h * a.nqb;
@@ -84,7 +124,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   const __bf16* V = (const __bf16*)a.v;
   const __bf16* dO = (const __bf16*)a.dout;
 
-  // this lane's query row (column of the transposed products)
+  // Key rows past Lk are outside the copies' range: their LDS keeps what it held.  Cleared
+  // once here, it only ever holds zeros or earlier finite rows, which the mask hides.
+#pragma unroll
+  for (int i = 0; i < QTL / (256 * 8); ++i) {
+    const int o = 8 * (tid + 256 * i);
+    store16(sK0 + o, zero_bf16x8());
+    store16(sK1 + o, zero_bf16x8());
+    store16(sK2 + o, zero_bf16x8());
+    store16(sK3 + o, zero_bf16x8());
+    store16(sV0 + o, zero_bf16x8());
+    store16(sV1 + o, zero_bf16x8());
+  }
+  __syncthreads();  // cleared before any copy lands
+
+  // this lane's query row
   const int r = wave * 32 + n;
   const int rt = r / G;
   const int t = qb * Bq + rt;
@@ -114,91 +168,201 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
+  // LDS offsets (elements) inside a tile, as in the dK/dV kernel: operand reads of key row
+  // 32 k2 + n, columns 16 dd + 8 h2 (base XOR dd << 4); transposed reads of key rows
+  // 16 (2 k2 + hf) + vrow (+8), columns 32 db + vcol (base XOR db << 5).
   const int gg = lane >> 4, j16 = lane & 15;
   const int vrow = 4 * (gg >> 1) + (j16 >> 2);
   const int vcol = 16 * (gg & 1) + 4 * (j16 & 3);
+  int ofs_a0 = lds_swz(n, 8 * h2);
+  int ofs_t0[2] = {lds_swz(vrow, vcol), lds_swz(vrow + 8, vcol)};
+  auto ofs_a = [&](int k2, int dd) { return 4096 * k2 + (ofs_a0 ^ (dd << 4)); };
+  auto ofs_t = [&](int k2, int hf, int pp, int db) { return 2048 * (2 * k2 + hf) + (ofs_t0[pp] ^ (db << 5)); };
 
-  // staging of one 64-key sub-tile: chunks tid + 256 u (u < 4), row id / 16, col id % 16
-  const int e0 = a.row_ptr[item], e1 = a.row_ptr[item + 1];
-  const int n_sub = 2 * (e1 - e0);
-  u32x4 pk[4], pv[4];
-  auto fetch = [&](int sidx) {
-    const int kb = a.row_ent[e0 + (sidx >> 1)] >> 1;
-    const int jb = kb * BK + (sidx & 1) * SUB;
+  // Copies of a tile: wave w fills key rows 16 w .. 16 w + 15, 4 rows per copy; lane L of
+  // copy u fills row kr = 16 w + 4 u + L / 16, physical chunk L % 16 (logical chunk
+  // (L % 16) ^ lds_sw(kr)).  voff[u]: its byte offset from the tile's first key.
+  const int HkvD = a.Hkv * D;
+  uint32_t voff[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int id = tid + 256 * u;
-      const int row = id >> 4, cc = id & 15;
-      const int j = jb + row;
-      if (j < a.Lk) {
-        const int64_t o = (((int64_t)b * a.Lk + j) * a.Hkv + h) * D + 8 * cc;
-        pk[u] = *(const u32x4*)(K + o);
-        pv[u] = *(const u32x4*)(V + o);
-      } else {
-        pk[u] = u32x4{0, 0, 0, 0};
-        pv[u] = u32x4{0, 0, 0, 0};
-      }
-    }
+  for (int u = 0; u < 4; ++u) {
+    const int kr = 16 * wave + 4 * u + (lane >> 4);
+    voff[u] = 2u * (uint32_t)(kr * HkvD + h * D + 8 * ((lane & 15) ^ lds_sw(kr)));
+  }
+
+  const int e0 = load_uniform(a.row_ptr, item);
+  const int n_ent = load_uniform(a.row_ptr, item + 1) - e0;
+  const int ntile = 2 * n_ent;
+  // first key of tile tt, and its entry; tiles past the list get an empty copy range
+  auto tile_j0 = [&](int ent, int tt) { return (ent >> 1) * BK + (tt & 1) * QBK; };
+  __amdgpu_buffer_rsrc_t rk, rv;
+  auto prepare_copy = [&](int ent, int tt, bool real) {
+    const int j0 = tile_j0(ent, tt);
+    const int64_t base = ((int64_t)b * a.Lk + j0) * HkvD;
+    const int64_t bytes = real ? (int64_t)(a.Lk - j0) * HkvD * 2 : 0;
+    rk = make_rsrc(K + base, bytes);
+    rv = make_rsrc(V + base, bytes);
   };
-  if (n_sub > 0) fetch(0);
-
-  for (int sidx = 0; sidx < n_sub; ++sidx) {
-    const int ent = a.row_ent[e0 + (sidx >> 1)];
-    const int jb = (ent >> 1) * BK + (sidx & 1) * SUB;
-    const bool partial = ent & 1;
-    __syncthreads();
+  auto copy = [&](int i, __bf16* kd, __bf16* vd) {  // copy i of 8 (u = i / 2, K then V)
+    const int u = i >> 1;
+    buf2lds((i & 1) ? rv : rk, voff[u], ((i & 1) ? vd : kd) + (16 * wave + 4 * u) * D);
+  };
+  // masked element: S = -inf where the key is hidden from the row
+  auto mask = [&](f32x16 (&s)[2], int j0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int id = tid + 256 * u;
-      const int row = id >> 4, cc = id & 15;
-      *(u32x4*)(sK + lds_swz(row, 8 * cc)) = pk[u];
-      *(u32x4*)(sV + lds_swz(row, 8 * cc)) = pv[u];
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = j0 + 32 * k2 + 8 * (i >> 2) + 4 * h2 + (i & 3);
+        s[k2][i] = (rvalid & visible(p, j, a.Lk, a.win.sink, a.win.near_w, band)) ? s[k2][i] : -INFINITY;
+      }
+  };
+
+  if (n_ent > 0) {
+    // entries of tiles t, t+1, t+2 (two tiles per entry), read ahead with scalar loads
+    int ent[3];
+    ent[0] = load_uniform(a.row_ent, e0);
+    ent[1] = ent[0];
+    ent[2] = n_ent > 1 ? load_uniform(a.row_ent, e0 + 1) : ent[0];
+    int ent_next = n_ent > 2 ? load_uniform(a.row_ent, e0 + 2) : ent[2];
+
+    // prologue: tiles 0 and 1 resident; S, dP of tile 0
+    prepare_copy(ent[0], 0, true);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) copy(i, sK0, sV0);
+    prepare_copy(ent[1], 1, ntile > 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) copy(i, sK1, sV1);
+    wait_loads_and_barrier();
+
+    f32x16 sA[2], dA[2], sB[2], dB[2];  // S^T, dP^T of two consecutive tiles (2 key blocks)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sA[k2][i] = dA[k2][i] = 0.f;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        sA[k2] = mfma32x32x16(load16(sK0 + ofs_a(k2, dd)), qf[dd], sA[k2]);
+        dA[k2] = mfma32x32x16(load16(sV0 + ofs_a(k2, dd)), df[dd], dA[k2]);
+      }
     }
-    __syncthreads();
-    if (sidx + 1 < n_sub) fetch(sidx + 1);
+    uint32_t dsp[2][2][4];  // packed dS^T of the previous tile: [k2][hf] bf16x8 as 4 words
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) dsp[k2][hf][w] = 0u;
 
-    // S^T and dP^T for both 32-key halves first: four independent accumulation chains
-    f32x16 s2[SUB / 32], dp2[SUB / 32];
+    // One iteration for tile tt (tt % 4 = TC at compile time).  cur: S, dP of tile tt;
+    // nxt: S, dP of tile tt + 1 (computed here).
+    auto iteration = [&](auto tcc, const int tt, f32x16 (&cs)[2], f32x16 (&cd)[2], f32x16 (&ns)[2],
+                         f32x16 (&nd)[2]) {
+      constexpr int TC = decltype(tcc)::value;
+      wait_loads_and_barrier();  // tile tt + 1 resident; every wave done with tile tt - 1
+      // copies of tile tt + 2 (K into the buffer of tile tt - 2, V into that of tile tt)
+      prepare_copy(ent[2], tt + 2, tt + 2 < ntile);
+      __bf16* kd = kbuf(IC<(TC + 2) & 3>{});
+      __bf16* vd = vbuf(IC<TC & 1>{});
+      if (ent[0] & 1) mask(cs, tile_j0(ent[0], tt));
+      const __bf16* kq = kbuf(IC<(TC + 3) & 3>{});  // K of tile tt - 1 (dQ)
+      const __bf16* kn = kbuf(IC<(TC + 1) & 3>{});  // K of tile tt + 1 (S)
+      const __bf16* vn = vbuf(IC<(TC + 1) & 1>{});  // V of tile tt + 1 (dP)
 #pragma unroll
-    for (int k2 = 0; k2 < SUB / 32; ++k2)
+      for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s2[k2][i] = dp2[k2][i] = 0.f;
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd)
-#pragma unroll
-      for (int k2 = 0; k2 < SUB / 32; ++k2) {
-        const bf16x8 kf = load16(sK + lds_swz(32 * k2 + n, 16 * dd + 8 * h2));
-        const bf16x8 vf = load16(sV + lds_swz(32 * k2 + n, 16 * dd + 8 * h2));
-        s2[k2] = mfma32x32x16(kf, qf[dd], s2[k2]);
-        dp2[k2] = mfma32x32x16(vf, df[dd], dp2[k2]);
-      }
-#pragma unroll
-    for (int k2 = 0; k2 < SUB / 32; ++k2) {
-      const f32x16& s = s2[k2];
-      const f32x16& dp = dp2[k2];
-      float pr[16], ds[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
-      if (partial) {  // one uniform branch; the predicate per element, branch-free
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = jb + 32 * k2 + 8 * (i >> 2) + 4 * h2 + (i & 3);
-          pr[i] = (rvalid & visible(p, j, a.Lk, a.win.sink, a.win.near_w, band)) ? pr[i] : 0.f;
+        for (int i = 0; i < 16; ++i) ns[k2][i] = nd[k2][i] = 0.f;
+      float pr[2][16], dsv[2][16];
+      uint32_t npk[2][2][4];
+      // operands: transposed K of tile tt - 1 for the first 16 MFMAs, K / V rows of tile
+      // tt + 1 for the other 32, each read two MFMAs ahead
+      bf16x8 opA[48];
+      auto load_op = [&](int x) {
+        if (x < 16) {
+          const int k2 = x >> 3, hf = (x >> 2) & 1, db = x & 3;
+          opA[x] = join(lds_read_tr4(kq + ofs_t(k2, hf, 0, db)), lds_read_tr4(kq + ofs_t(k2, hf, 1, db)));
+        } else {  // four chains (k2, S / dP) in rotation
+          const int y = x - 16, k2 = y & 1, dd = y >> 2;
+          opA[x] = load16((((y >> 1) & 1) ? vn : kn) + ofs_a(k2, dd));
         }
-      }
+      };
+      load_op(0);
+      load_op(1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ds[i] = pr[i] * (dp[i] - dlt);
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const bf16x8 dsf = join(to_bf16x4(ds[8 * hf], ds[8 * hf + 1], ds[8 * hf + 2], ds[8 * hf + 3]),
-                                to_bf16x4(ds[8 * hf + 4], ds[8 * hf + 5], ds[8 * hf + 6], ds[8 * hf + 7]));
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int r0 = 32 * k2 + 16 * hf + vrow, col = 32 * db + vcol;
-          const bf16x8 ktf = join(lds_read_tr4(sK + lds_swz(r0, col)), lds_read_tr4(sK + lds_swz(r0 + 8, col)));
-          acc[db] = mfma32x32x16(ktf, dsf, acc[db]);
+      for (int x = 0; x < 48; ++x) {
+        if (x + 2 < 48) load_op(x + 2);
+        if (x < 16) {
+          const int k2 = x >> 3, hf = (x >> 2) & 1, db = x & 3;
+          const u32x4 w = {dsp[k2][hf][0], dsp[k2][hf][1], dsp[k2][hf][2], dsp[k2][hf][3]};
+          acc[db] = mfma32x32x16(opA[x], __builtin_bit_cast(bf16x8, w), acc[db]);
+        } else {
+          const int y = x - 16, k2 = y & 1, dd = y >> 2;
+          if ((y >> 1) & 1) nd[k2] = mfma32x32x16(opA[x], df[dd], nd[k2]);
+          else ns[k2] = mfma32x32x16(opA[x], qf[dd], ns[k2]);
         }
+        if (x >= 4 && x < 12) copy(x - 4, kd, vd);
+        __builtin_amdgcn_sched_barrier(0);
+        // VALU of tile tt: element e = x (0..31) gets P in step x, dS in step x + 4;
+        // pairs are packed to bf16 in steps 38..47 (two pairs per step from 40)
+        if (x < 32) {
+          const int k2 = x >> 4, i = x & 15;
+          pr[k2][i] = __builtin_amdgcn_exp2f(fmaf(pin(cs[k2][i]), a.scale_log2, -lse2));
+          pin_out(pr[k2][i]);
+        }
+        if (x >= 4 && x < 36) {
+          const int e = x - 4, k2 = e >> 4, i = e & 15;
+          dsv[k2][i] = pr[k2][i] * (pin(cd[k2][i]) - dlt);
+          pin_out(dsv[k2][i]);
+        }
+        if (x >= 32) {
+          const int q = x - 32;  // pair q of 16: k2 = q / 8, hf = (q / 4) % 2, word q % 4
+          const int k2 = q >> 3, hf = (q >> 2) & 1, w = q & 3;
+          const float x0 = dsv[k2][8 * hf + 2 * w], x1 = dsv[k2][8 * hf + 2 * w + 1];
+          const bf16x2 v = {(__bf16)x0, (__bf16)x1};
+          npk[k2][hf][w] = __builtin_bit_cast(uint32_t, v);
+          pin_out(npk[k2][hf][w]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) dsp[k2][hf][w] = npk[k2][hf][w];
+      // advance the entry window at entry boundaries (two tiles per entry)
+      if (tt & 1) {
+        ent[0] = ent[2];
+        ent[1] = ent[2];
+        ent[2] = ent_next;
+        const int en = ((tt + 1) >> 1) + 2;  // entry of tile tt + 5
+        if (en < n_ent) ent_next = load_uniform(a.row_ent, e0 + en);
+      } else {
+        ent[0] = ent[1];
+      }
+    };
+    int tt = 0;
+    for (; tt + 4 <= ntile; tt += 4) {
+      iteration(IC<0>{}, tt, sA, dA, sB, dB);
+      iteration(IC<1>{}, tt + 1, sB, dB, sA, dA);
+      iteration(IC<2>{}, tt + 2, sA, dA, sB, dB);
+      iteration(IC<3>{}, tt + 3, sB, dB, sA, dA);
+    }
+    if (tt < ntile) {  // ntile is even: two more tiles
+      iteration(IC<0>{}, tt, sA, dA, sB, dB);
+      iteration(IC<1>{}, tt + 1, sB, dB, sA, dA);
+    }
+    // dQ of the last tile (its K sits in buffer (ntile - 1) % 4)
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    const int lastc = (ntile - 1) & 3;
+    const __bf16* kl = lastc == 0 ? sK0 : lastc == 1 ? sK1 : lastc == 2 ? sK2 : sK3;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int k2 = x >> 3, hf = (x >> 2) & 1, db = x & 3;
+      const bf16x8 ka = join(lds_read_tr4(kl + ofs_t(k2, hf, 0, db)), lds_read_tr4(kl + ofs_t(k2, hf, 1, db)));
+      const u32x4 w = {dsp[k2][hf][0], dsp[k2][hf][1], dsp[k2][hf][2], dsp[k2][hf][3]};
+      acc[db] = mfma32x32x16(ka, __builtin_bit_cast(bf16x8, w), acc[db]);
     }
   }
 
@@ -224,16 +388,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 // filled by direct global->LDS copies issued one q-block ahead.
 constexpr int QTILE = ROWS * D;  // one q-block of Q (or dO) in LDS
 
-// Returns x unchanged, but the value is taken at this point of the program: computations
-// that use the result cannot be hoisted above it (it pins VALU work to its pipeline slot).
-__device__ __forceinline__ float pin(float x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
-__device__ __forceinline__ void pin_out(uint32_t& x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin_out(float& x) { asm volatile("" : "+v"(x)); }
-
 // One pair of the hi/lo split: (x0, x1) -> bf16 pair hi = bf16(x), lo = bf16(x - hi).
 __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
   const bf16x2 h = {(__bf16)x0, (__bf16)x1};
@@ -244,9 +398,6 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
   hi = w;
   lo = __builtin_bit_cast(uint32_t, l);
 }
-
-template <int V>
-using IC = std::integral_constant<int, V>;
 
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // Q and dO of a q-block, [Q, dO][rows] with swizzled 256-byte rows (lds_swz); dO sits at

@@ -84,7 +84,7 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
 // Raw buffer resource over [base, base + bytes): loads through it take a 32-bit per-lane
 // byte offset (plus a scalar one) and return zeros past `bytes`.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes < 0x7fffffff ? (int)bytes : 0x7fffffff;
+  const int n = bytes <= 0 ? 0 : bytes < 0x7fffffff ? (int)bytes : 0x7fffffff;
   return __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr((const char*)base), (short)0, n,
                                            0x00020000);
 }
