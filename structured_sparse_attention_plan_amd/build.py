@@ -32,10 +32,18 @@ FLAGS = [
 ]
 
 
+# Per-file additions.  The forward kernel takes running maxima of scores that are finite
+# or -inf, never NaN: without NaN semantics max(max(a, b), c) becomes one v_max3_f32 (IEEE
+# NaN rules otherwise keep it as two v_max_f32 per element).
+FILE_FLAGS = {
+    "fwd_bf16.hip": ["-fno-honor-nans"],
+}
+
+
 def _compile(src):
     out = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
