@@ -8,33 +8,39 @@
 // 32-column blocks of v_mfma_f32_32x32x16_bf16.
 //
 // The item walks the planner's row list of visible 64-key blocks (masked blocks are
-// never touched).  Per block t, in one pipelined loop iteration:
-//   [A] S(t+1)^T = K(t+1) Q^T on MFMA: K (A operand, one key row per lane) and Q^T (B
-//       operand) from LDS, so each lane owns one query row (column) and 16 of every 32
-//       keys; a boundary (PARTIAL) block gets the window predicate per element at the
-//       start of its own iteration;
-//   [B] online softmax of S(t) in base 2 (scale * log2 e folded into one FMA), the row
-//       max taken across the two lane halves of a column; the running max only moves
-//       when a row's tile max exceeds it by more than 8 (log2 units) — exact, because
-//       O / l does not depend on the reference, and P stays <= 256; P(t) is computed
-//       with the current reference and recomputed only on such a (rare) move;
-//   [C] O^T += V(t)^T P(t)^T: P^T goes from the C-layout accumulator straight into the B
-//       operand (no LDS round trip) and V^T is read from the row-major LDS tile with
-//       ds_read_b64_tr_b16, two 4-key runs per operand matching the accumulator layout.
-// [A] has no dependence on [B], so the scheduler overlaps the two (MFMA and VALU run
-// in parallel within a wave).
+// never touched).  Three products run as a software pipeline, one block t per loop
+// iteration of 64 MFMA slots:
+//   [A] S(t+1)^T = K(t+1) Q^T on the even slots: K (A operand, one key row per lane) and
+//       Q^T (B operand) from LDS, so each lane owns one query row (column) and 16 of every
+//       32 keys.  Its accumulators are VGPRs: the softmax reads them as plain VALU
+//       operands (reading accumulation registers while the matrix core runs costs several
+//       cycles per value);
+//   [B] online softmax of S(t) in base 2 (scale * log2 e folded into one FMA), one
+//       element per slot beside the MFMAs; a boundary (PARTIAL) block gets the window
+//       predicate per element first;
+//   [C] O^T += V(t-1)^T P(t-1)^T on the odd slots: P^T goes from the softmax registers
+//       straight into the B operand (no LDS round trip) and V^T is read from the
+//       row-major LDS tile with ds_read_b64_tr_b16, two 4-key runs per operand matching
+//       the accumulator layout.  O stays in the accumulation registers.
+// Reference: the result O / l does not depend on the value m subtracted before exp2, so
+// no running max is kept.  The first tile sets m to its column max; later tiles keep it
+// unless a column's sum over the tile leaves [2^-32, 2^32] (the low bound only while
+// the column has no mass yet), when the tile's column max replaces it and O, l follow.
+// With P <= 2^32 and at most 2^31 keys, O and l stay finite in fp32.
 //
-// Memory pipeline: K and V are double-buffered in LDS and filled by direct
-// global->LDS loads (global_load_lds_dwordx4, no staging registers); the loads of K(t+2)
-// and V(t+1) are issued right after the single barrier of iteration t and waited for at
-// the next one.  LDS rows are 256 bytes with the 16-byte chunks XOR-swizzled by a function
-// of the row, so both the row-wise operand reads and the transposed V reads are free of
-// bank conflicts.
+// Memory pipeline: K and V are double-buffered in LDS and filled by direct buffer->LDS
+// copies (no staging registers), spread over the MFMA slots: K(t+2) and V(t) are copied
+// during block t and waited for at the next block's single barrier.  LDS rows are 256
+// bytes with the 16-byte chunks XOR-swizzled by a function of the row, so both the
+// row-wise operand reads and the transposed V reads are free of bank conflicts, and the
+// addresses of one lane differ only in the XOR of the chunk bits.
 // Output: O / l in bf16 and LSE = ln 2 * (m + log2 l) in fp32.
 //
 // MFMA lane layouts of v_mfma_f32_32x32x16_bf16 (n = lane % 32, h2 = lane / 32):
 //   A (32 x 16): A[n][8 h2 + e]   B (16 x 32): B[8 h2 + e][n]
 //   C (32 x 32): element i of 16 is C[8 (i / 4) + 4 h2 + i % 4][n]
+
+#include <type_traits>
 
 #include "device_common.h"
 
@@ -50,6 +56,19 @@ constexpr int BK = kFwdBk;           // 64 keys per tile
 constexpr int KB2 = BK / 32;         // 2 key blocks of 32
 constexpr int TILE = BK * D;         // elements per K or V tile
 constexpr float kRescaleThreshold = 8.0f;
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// f(IC<B>), f(IC<B+1>), ..., f(IC<E-1>): straight-line code with a compile-time index,
+// whatever the size of the body
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // LDS tiles: 256-byte rows with XOR-swizzled 16-byte chunks (lds_sw / lds_swz).
 __device__ __forceinline__ int sw(int r) { return lds_sw(r); }
@@ -67,14 +86,50 @@ __device__ __forceinline__ float agpr_scale(float x, float alpha) {
   return r;
 }
 
+// Returns x unchanged, but the value is taken at this point of the program: computations
+// that use the result cannot be hoisted above it (it pins VALU work to its pipeline slot).
+__device__ __forceinline__ float pin(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ void pin_out(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin_out(bf16x8& x) { asm volatile("" : "+v"(x)); }
+
+// S products with their accumulators in VGPRs: the softmax reads S with plain VALU
+// operands (a read of an accumulation register costs several cycles while the matrix
+// core runs).  Every S accumulator is read by the VALU a block after its last product,
+// and each chain has three other products between dependent steps, so these need no
+// wait states beyond what the matrix core itself enforces; their LDS operands carry the
+// compiler's usual waits.
+__device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+
+
 __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 sQ[ROWS * D];
-  __shared__ __attribute__((aligned(1024))) __bf16 sK[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV[2 * TILE];
+  // K and V double buffers, one array per buffer: the tile parity is known at compile
+  // time in each of the two unrolled iterations, so every read names the array it reads
+  // and the compiler can tell it from the copies in flight into the other one.
+  __shared__ __attribute__((aligned(1024))) __bf16 sK0[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK1[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV0[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV1[TILE];
+  auto kbuf = [&](auto c) __attribute__((always_inline)) -> __bf16* {
+    if constexpr ((decltype(c)::value & 1) == 0) return sK0;
+    else return sK1;
+  };
+  auto vbuf = [&](auto c) __attribute__((always_inline)) -> __bf16* {
+    if constexpr ((decltype(c)::value & 1) == 0) return sV0;
+    else return sV1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
   const int n = lane & 31;
   const int h2 = lane >> 5;
   const int item = a.row_order[blockIdx.x];
@@ -89,6 +144,17 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   const __bf16* Q = (const __bf16*)a.q;
   const __bf16* K = (const __bf16*)a.k;
   const __bf16* V = (const __bf16*)a.v;
+
+  // Key rows past Lk are outside the copies' range and keep what LDS held: cleared once
+  // here, they only ever hold zeros or earlier finite rows (their scores are masked).
+#pragma unroll
+  for (int i = 0; i < TILE / (256 * 8); ++i) {
+    store16(sK0 + 8 * (tid + 256 * i), zero_bf16x8());
+    store16(sK1 + 8 * (tid + 256 * i), zero_bf16x8());
+    store16(sV0 + 8 * (tid + 256 * i), zero_bf16x8());
+    store16(sV1 + 8 * (tid + 256 * i), zero_bf16x8());
+  }
+  __syncthreads();
 
   int tok[CB], hq[CB];
   bool rvalid[CB];
@@ -121,15 +187,26 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
       g2lds(Q + (((int64_t)b * a.Lq + t) * a.Hq + h * G + g) * D + 8 * c, dst + 4 * u * D);
     }
   }
-  auto load_tile = [&](const __bf16* src, __bf16* dst, int kb) {
-    // wave w copies rows 16 w .. 16 w + 15 (keys past Lk read key Lk - 1; masked)
+  // K / V tile copies: wave w fills rows 16 w .. 16 w + 15, 4 rows per copy; lane L of
+  // copy u fills row r = 16 w + 4 u + L / 16 at physical chunk L % 16.  voff[u] is the
+  // byte offset of its source chunk from the tile's first key.  A tile is read through a
+  // buffer resource ending at key Lk (keys past Lk read nothing; they are masked), or
+  // with an empty range when the tile does not exist, so the copies need no branches and
+  // can be spread over the MFMA slots of the interleaved block.
+  const int HkvD = a.Hkv * D;
+  uint32_t voff[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = 16 * wave + 4 * u + lrow;
-      const int j = min(kb * BK + r, a.Lk - 1);
-      const int c = lchunk ^ sw(r);
-      g2lds(src + (((int64_t)b * a.Lk + j) * a.Hkv + h) * D + 8 * c, dst + (16 * wave + 4 * u) * D);
-    }
+  for (int u = 0; u < 4; ++u) {
+    const int r = 16 * wave + 4 * u + lrow;
+    voff[u] = 2u * (uint32_t)(r * HkvD + h * D + 8 * (lchunk ^ sw(r)));
+  }
+  auto tile_rsrc = [&](const __bf16* src, int ent, bool real) __attribute__((always_inline)) {
+    const int j0 = (ent >> 1) * BK;
+    const int64_t bytes = real ? (int64_t)(a.Lk - j0) * HkvD * 2 : 0;
+    return make_rsrc(src + ((int64_t)b * a.Lk + j0) * HkvD, bytes);
+  };
+  auto copy_tile = [&](__amdgpu_buffer_rsrc_t r, int u, __bf16* dst) __attribute__((always_inline)) {
+    buf2lds(r, voff[u], dst + (16 * wave + 4 * u) * D);
   };
 
   f32x16 acc[CB][4];
@@ -139,206 +216,334 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[c][db][i] = 0.f;
+  // m: the reference subtracted from the scaled scores (base 2) before exp2, per column;
+  // l: this lane's share of the column's row sum in that reference
   float m[CB], l[CB];
 #pragma unroll
   for (int c = 0; c < CB; ++c) {
-    m[c] = -INFINITY;
+    m[c] = 0.f;
     l[c] = 0.f;
   }
 
   const int e0 = a.row_ptr[item];
   const int nt = a.row_ptr[item + 1] - e0;
-  const __bf16* sQw = sQ + wave * WROWS * D;
-
-  // tr-read addressing for the V^T operand: 16-lane group gg covers d columns
-  // 16 (gg & 1) .. +15 of a 32-column block and key run 4 (gg >> 1) (+8)
+  // LDS addressing.  With the chunk swizzle, the operand addresses of one lane differ
+  // only by an XOR of the chunk bits, so each is one XOR away from a per-lane base:
+  //   K / Q rows n of a tile at dd: kofs ^ (dd << 5) bytes (+ 8192 for key / row block 1);
+  //   V^T operand (k2, hf, db), first and second run of 4 rows:
+  //     vofs ^ (db << 6) and (vofs ^ (db << 6) ^ 32) + 2048, + 4096 (2 k2 + hf) bytes,
+  // where 16-lane group gg covers d columns 16 (gg & 1) .. +15 of a 32-column block and
+  // key run 4 (gg >> 1) (+8).  The bases are re-taken at the top of every iteration
+  // (pin), so the compiler forms the few addresses of the iteration there instead of
+  // keeping one register per address and buffer alive across the whole loop.
   const int gg = lane >> 4, j16 = lane & 15;
   const int vrow = 4 * (gg >> 1) + (j16 >> 2);
   const int vcol = 16 * (gg & 1) + 4 * (j16 & 3);
-
-  // boundary tile t: branch-free window predicate per element
-  auto mask = [&](f32x16 (&s)[KB2][CB], int ent) {
-    if (ent & 1) {
-      const int kb = ent >> 1;
-#pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const int p = tok[c] + off;
-#pragma unroll
-        for (int k2 = 0; k2 < KB2; ++k2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = kb * BK + 32 * k2 + 8 * (i >> 2) + 4 * h2 + (i & 3);
-            const bool vis = rvalid[c] & visible(p, j, a.Lk, a.win.sink, a.win.near_w, band);
-            s[k2][c][i] = vis ? s[k2][c][i] : -INFINITY;
-          }
-      }
-    }
+  const uint32_t kofs0 = 2u * (uint32_t)swz(n, 8 * h2);
+  const uint32_t qofs0 = kofs0 + 2u * (uint32_t)(wave * WROWS * D);
+  const uint32_t vofs0 = 2u * (uint32_t)swz(vrow, vcol);
+  auto at = [](const __bf16* base, uint32_t byte_ofs) __attribute__((always_inline)) {
+    return (const __bf16*)((const char*)base + byte_ofs);
   };
 
-  auto scores = [&](f32x16 (&s)[KB2][CB], int t) {
-    const __bf16* kt = sK + (t & 1) * TILE;
-#pragma unroll
-    for (int k2 = 0; k2 < KB2; ++k2)
-#pragma unroll
-      for (int c = 0; c < CB; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[k2][c][i] = 0.f;
+  auto scores = [&](f32x16 (&s)[KB2][CB]) __attribute__((always_inline)) {  // S of tile 0
+    const __bf16* kt = sK0;
 #pragma unroll
     for (int dd = 0; dd < D / 16; ++dd) {
       bf16x8 qf[CB];
 #pragma unroll
-      for (int c = 0; c < CB; ++c) qf[c] = load16(sQw + swz(c * 32 + n, 16 * dd + 8 * h2));
+      for (int c = 0; c < CB; ++c) qf[c] = load16(at(sQ, (qofs0 ^ (dd << 5)) + 8192 * c));
 #pragma unroll
       for (int k2 = 0; k2 < KB2; ++k2) {
-        const bf16x8 kf = load16(kt + swz(32 * k2 + n, 16 * dd + 8 * h2));
+        const bf16x8 kf = load16(at(kt, (kofs0 ^ (dd << 5)) + 8192 * k2));
 #pragma unroll
-        for (int c = 0; c < CB; ++c) s[k2][c] = mfma32x32x16(kf, qf[c], s[k2][c]);
-      }
-    }
-  };
-
-  // List entries of tiles t .. t+2 are kept in registers and entry t+3 is loaded one
-  // iteration ahead: a load of it issued after the direct copies and waited for at once
-  // would also wait for those copies (one in-order counter covers both).
-  int ent0 = 0, ent1 = 0, ent2 = 0;
-  auto iteration = [&](int t, f32x16 (&cur)[KB2][CB], f32x16 (&next)[KB2][CB]) {
-    wait_loads_and_barrier();  // K(t+1), V(t), entry t+3 resident; every wave is done with t-1
-    const int ent3 = (t + 3 < nt) ? a.row_ent[e0 + t + 3] : 0;  // made uniform when used
-    if (t + 2 < nt) load_tile(K, sK + (t & 1) * TILE, __builtin_amdgcn_readfirstlane(ent2) >> 1);
-    if (t + 1 < nt) load_tile(V, sV + ((t + 1) & 1) * TILE, __builtin_amdgcn_readfirstlane(ent1) >> 1);
-    mask(cur, __builtin_amdgcn_readfirstlane(ent0));
-    ent0 = ent1;
-    ent1 = ent2;
-    ent2 = ent3;
-
-    // Interleaved block: step i issues one MFMA of S(t+1) (dd = i / 4, (k2, c) = i % 4;
-    // past the last tile it reads a resident buffer and the result is unused), then the
-    // softmax work of two elements of S(t): exp2 with the current reference, running max,
-    // and every 4 steps the bf16 packing and row sum of 8 probabilities.  The scheduling
-    // fences keep this order, so the matrix core and the VALU run at the same time.
-    const __bf16* kt = sK + ((t + 1) & 1) * TILE;
-#pragma unroll
-    for (int k2 = 0; k2 < KB2; ++k2)
-#pragma unroll
-      for (int c = 0; c < CB; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) next[k2][c][i] = 0.f;
-    bf16x8 kf[2][KB2], qf[2][CB];
-#pragma unroll
-    for (int x = 0; x < KB2; ++x) kf[0][x] = load16(kt + swz(32 * x + n, 8 * h2));
-#pragma unroll
-    for (int x = 0; x < CB; ++x) qf[0][x] = load16(sQw + swz(32 * x + n, 8 * h2));
-    float ref[CB], mx[CB], sum[CB];
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      ref[c] = (m[c] == -INFINITY) ? 0.f : m[c];
-      mx[c] = -INFINITY;
-      sum[c] = 0.f;
-    }
-    bf16x8 pf[KB2][CB][2];
-    float pb[8];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int dd = i >> 2, k2 = (i >> 1) & 1, c = i & 1;
-      if ((i & 3) == 0 && dd + 1 < D / 16) {
-#pragma unroll
-        for (int x = 0; x < KB2; ++x) kf[(dd + 1) & 1][x] = load16(kt + swz(32 * x + n, 16 * (dd + 1) + 8 * h2));
-#pragma unroll
-        for (int x = 0; x < CB; ++x) qf[(dd + 1) & 1][x] = load16(sQw + swz(32 * x + n, 16 * (dd + 1) + 8 * h2));
-      }
-      next[k2][c] = mfma32x32x16(kf[dd & 1][k2], qf[dd & 1][c], next[k2][c]);
-      __builtin_amdgcn_sched_barrier(0);
-      // elements 2i, 2i+1 of S(t) in (c, k2, hf, e2) order
-      const int ec = i >> 4, ek2 = (i >> 3) & 1, ehf = (i >> 2) & 1, e2 = 2 * (i & 3);
-      const float x0 = cur[ek2][ec][8 * ehf + e2], x1 = cur[ek2][ec][8 * ehf + e2 + 1];
-      mx[ec] = fmaxf(mx[ec], fmaxf(x0, x1));
-      pb[e2] = __builtin_amdgcn_exp2f(fmaf(x0, a.scale_log2, -ref[ec]));
-      pb[e2 + 1] = __builtin_amdgcn_exp2f(fmaf(x1, a.scale_log2, -ref[ec]));
-      sum[ec] += pb[e2] + pb[e2 + 1];  // fp32 row sum (it sets LSE, which the backward reuses)
-      if ((i & 3) == 3)
-        pf[ek2][ec][ehf] = join(to_bf16x4(pb[0], pb[1], pb[2], pb[3]), to_bf16x4(pb[4], pb[5], pb[6], pb[7]));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    float mt[CB];
-    bool need[CB];
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const float x = fmaxf(mx[c], __shfl_xor(mx[c], 32));
-      mt[c] = x * a.scale_log2;
-      need[c] = mt[c] > m[c] + kRescaleThreshold;
-    }
-    if (__builtin_amdgcn_ballot_w64(need[0] | need[1]) != 0) {
-      // rare: rows whose max moved past the threshold take it as their new reference;
-      // their accumulators, sums and P(t) are rescaled / recomputed, the other rows keep
-      // theirs
-#pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const float mn = need[c] ? mt[c] : m[c];
-        const float alpha = (m[c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[c] - mn);
-        m[c] = mn;
-        l[c] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[c][db][i] = agpr_scale(acc[c][db][i], alpha);
-      }
-#pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const float rf = (m[c] == -INFINITY) ? 0.f : m[c];
-        float s2 = 0.f;
-#pragma unroll
-        for (int k2 = 0; k2 < KB2; ++k2)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              p[e] = __builtin_amdgcn_exp2f(fmaf(cur[k2][c][8 * hf + e], a.scale_log2, -rf));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s2 += p[e];
-            const bf16x8 pn = join(to_bf16x4(p[0], p[1], p[2], p[3]), to_bf16x4(p[4], p[5], p[6], p[7]));
-            pf[k2][c][hf] = need[c] ? pn : pf[k2][c][hf];
-          }
-        sum[c] = need[c] ? s2 : sum[c];
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < CB; ++c) l[c] += sum[c];
-    // O^T += V(t)^T P(t)^T
-    // (k2, hf) outermost so that the 8 accumulators rotate: each one is next updated only
-    // after 7 independent MFMAs
-    const __bf16* vt = sV + (t & 1) * TILE;
-#pragma unroll
-    for (int k2 = 0; k2 < KB2; ++k2) {
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int r0 = 32 * k2 + 16 * hf + vrow;
-          const int col = 32 * db + vcol;
-          const bf16x8 vf = join(lds_read_tr4(vt + swz(r0, col)), lds_read_tr4(vt + swz(r0 + 8, col)));
-#pragma unroll
-          for (int c = 0; c < CB; ++c) acc[c][db] = mfma32x32x16(vf, pf[k2][c][hf], acc[c][db]);
+        for (int c = 0; c < CB; ++c) {
+          if (dd == 0) mfma_v0(s[k2][c], kf, qf[c]);
+          else mfma_v(s[k2][c], kf, qf[c]);
         }
       }
     }
   };
 
-  if (nt > 0) {
-    ent0 = a.row_ent[e0];
-    ent1 = nt > 1 ? a.row_ent[e0 + 1] : 0;
-    ent2 = nt > 2 ? a.row_ent[e0 + 2] : 0;
-    load_tile(K, sK, __builtin_amdgcn_readfirstlane(ent0) >> 1);
-    load_tile(V, sV, __builtin_amdgcn_readfirstlane(ent0) >> 1);
-    if (nt > 1) load_tile(K, sK + TILE, __builtin_amdgcn_readfirstlane(ent1) >> 1);
-    f32x16 sa[KB2][CB], sb[KB2][CB];
-    wait_loads_and_barrier();
-    scores(sa, 0);
-    for (int t = 0; t < nt; t += 2) {
-      iteration(t, sa, sb);
-      if (t + 1 < nt) iteration(t + 1, sb, sa);
+  // tr-read of the V^T operand for (k2, hf, db) from a V tile at lane base vofs
+  auto vfrag = [&](const __bf16* vt, uint32_t vofs, int k2, int hf, int db) __attribute__((always_inline)) {
+    const uint32_t a0 = vofs ^ (uint32_t)(db << 6);
+    const uint32_t rows = 4096u * (uint32_t)(2 * k2 + hf);
+    return join(lds_read_tr4(at(vt, a0 + rows)), lds_read_tr4(at(vt, (a0 ^ 32u) + 2048u + rows)));
+  };
+
+  // Boundary tile: window predicate on one row block (32 columns c) of S, in place in
+  // its accumulators; element i of key block k2 is key 32 k2 + 8 (i / 4) + 4 h2 + i % 4
+  // of the tile.
+  auto mask_rows = [&](f32x16 (&v)[KB2][CB], int c, int ent) __attribute__((always_inline)) {
+    if (ent & 1) {
+      const int kb = ent >> 1;
+      const int p = tok[c] + off;
+      // taken here, so that the key indices are formed on this (rare) path only
+      int j0 = kb * BK + 4 * h2;
+      asm volatile("" : "+v"(j0));
+#pragma unroll
+      for (int k2 = 0; k2 < KB2; ++k2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = j0 + 32 * k2 + 8 * (i >> 2) + (i & 3);
+          const bool vis = rvalid[c] & visible(p, j, a.Lk, a.win.sink, a.win.near_w, band);
+          const float x = (v[k2][c][i]);
+          v[k2][c][i] = (vis ? x : -INFINITY);
+        }
     }
+  };
+
+  // Reference check.  The softmax is exact for any reference, so P(t) is computed with
+  // the current one and the reference only moves when a column's sum over the tile
+  // leaves the safe range: above 2^32 (a P near overflow), or below 2^-32 while the
+  // column has no mass yet (its first visible keys all far below the reference).  Then
+  // the tile's column max becomes the reference and the column's P(t) is recomputed; O
+  // and l follow by alpha once O holds the previous tiles.  P <= 2^32 with at most 2^31
+  // keys keeps O and l finite in fp32.
+  constexpr float kSumHi = 4294967296.0f, kSumLo = 1.0f / 4294967296.0f;
+  // the value of the same column in the other half of the wave
+  auto swap_halves = [&](float x) __attribute__((always_inline)) {
+    const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(h2 == 0 ? sw2[1] : sw2[0]);
+  };
+  // recompute row block c of P(t) from its scores with reference mr; returns its sum
+  auto softmax_rows = [&](const f32x16 (&sc)[KB2][CB], bf16x8 (&pfc)[KB2][CB][2], int c, float mr)
+      __attribute__((always_inline)) {
+    float sum = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < KB2; ++k2)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float pb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pb[e] = __builtin_amdgcn_exp2f(fmaf((sc[k2][c][8 * hf + e]), a.scale_log2, -mr));
+          sum += pb[e];
+        }
+        pfc[k2][c][hf] = join(to_bf16x4(pb[0], pb[1], pb[2], pb[3]), to_bf16x4(pb[4], pb[5], pb[6], pb[7]));
+      }
+    return sum;
+  };
+
+  // 8 probabilities packed to bf16 for the PV product, and their fp32 row sum (it sets
+  // LSE, which the backward reuses)
+  auto pack8 = [&](const float (&pb)[8], bf16x8& dst, float& sum) __attribute__((always_inline)) {
+    dst = join(to_bf16x4(pb[0], pb[1], pb[2], pb[3]), to_bf16x4(pb[4], pb[5], pb[6], pb[7]));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) sum += pb[q];
+  };
+
+  // List entries of tiles t .. t+2 are kept in scalar registers; entry t+3 is fetched
+  // during iteration t with a vector load (through a resource over this item's entries,
+  // so a fetch past the end reads 0) and taken at the top of iteration t+1.  A scalar
+  // load would share its wait counter with the LDS operand reads, whose first wait would
+  // then also wait for it.
+  int ent0 = 0, ent1 = 0, ent2 = 0;
+  const __amdgpu_buffer_rsrc_t r_ent = make_rsrc(a.row_ent + e0, (int64_t)nt * 4);
+  int ent_next = 0;  // entry t+3 in flight (VGPR)
+
+  // Iteration t (parity PAR = t % 2) is one block of 64 MFMA slots:
+  //   even slots: S(t+1) = K(t+1) Q^T, four products per 16-wide slice of d;
+  //   odd slots:  O^T += V(t-1)^T P(t-1)^T;
+  //   VALU, one softmax element of S(t) per slot, read from its accumulator one slot
+  //   ahead (row block 0 in slots 0-31, row block 1 in slots 32-63).
+  // After the block O holds every tile up to t-1: the reference check runs on the column
+  // sums of P(t) (rarely moving a reference and rescaling O), and l takes the sums.
+  // Registers: S(t) and S(t+1) take two sets of accumulators (128) beside O (128), all
+  // of the accumulation registers; P(t-1) and P(t) alternate the same way.
+  // LDS: K(t+1) and V(t-1) are read; K(t+2) and V(t) are copied in meanwhile, into the
+  // buffers of K(t) and V(t-2), which every wave finished with in iteration t-1.
+  f32x16 sx[2][KB2][CB];
+  bf16x8 pf[2][KB2][CB][2];
+  auto iteration = [&](auto parity, int t) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(parity)::value;
+    f32x16(&sc)[KB2][CB] = sx[PAR];      // S(t)
+    f32x16(&sn)[KB2][CB] = sx[PAR ^ 1];  // S(t+1)
+    bf16x8(&pfc)[KB2][CB][2] = pf[PAR];
+    const bf16x8(&pfp)[KB2][CB][2] = pf[PAR ^ 1];
+    wait_loads_and_barrier();  // K(t+1), V(t-1) resident; every wave is done with t-1
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(K, ent2, t + 2 < nt);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(V, ent0, true);
+    __bf16* const kdst = kbuf(IC<PAR>{});          // K(t+2)
+    __bf16* const vdst = vbuf(IC<PAR>{});          // V(t)
+    const __bf16* const kt = kbuf(IC<PAR ^ 1>{});  // K(t+1)
+    const __bf16* const vt = vbuf(IC<PAR ^ 1>{});  // V(t-1)
+    const int ent3 = __builtin_amdgcn_readfirstlane(ent_next);  // loaded in iteration t-1
+    ent_next = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * (t + 4), 0);
+    const int ent_t = ent0;  // tile t
+    ent0 = ent1;
+    ent1 = ent2;
+    ent2 = ent3;
+
+    // S(t+1) operands by step dd (four MFMAs, (k2, c)): the K rows of both key blocks and
+    // the Q^T columns of both row blocks at dd; step dd + 1 is read during step dd
+    uint32_t kofs = kofs0, qofs = qofs0, vofs = vofs0;
+    asm volatile("" : "+v"(kofs), "+v"(qofs), "+v"(vofs));
+    bf16x8 kq[2][4];
+    auto load_step = [&](int dd, bf16x8 (&dst)[4]) __attribute__((always_inline)) {
+      const uint32_t ka = kofs ^ (uint32_t)(dd << 5), qa = qofs ^ (uint32_t)(dd << 5);
+      dst[0] = load16(at(kt, ka));
+      dst[1] = load16(at(kt, ka + 8192u));
+      dst[2] = load16(at(sQ, qa));
+      dst[3] = load16(at(sQ, qa + 8192u));
+    };
+    load_step(0, kq[0]);
+    bf16x8 vf[3];
+    vf[0] = vfrag(vt, vofs, 0, 0, 0);
+    vf[1] = vfrag(vt, vofs, 0, 0, 1);
+    mask_rows(sc, 0, ent_t);
+    mask_rows(sc, 1, ent_t);
+
+    float sum[CB] = {0.f, 0.f};
+    float pb[8];
+    float xin = (sc[0][0][0]);
+    static_for<0, 64>([&](auto slot) __attribute__((always_inline)) {
+      constexpr int s = decltype(slot)::value;
+      if constexpr ((s & 1) == 0) {
+        // MFMA k = s / 2 covers dd = k / 4, (k2, c) = k % 4
+        constexpr int k = s >> 1, dd = k >> 2, k2 = (k >> 1) & 1, c = k & 1;
+        if constexpr ((k & 3) == 0 && dd + 1 < D / 16) load_step(dd + 1, kq[(dd + 1) & 1]);
+        // the first product of an accumulator (dd = 0) starts from zero
+        if constexpr (dd == 0) mfma_v0(sn[k2][c], kq[dd & 1][k2], kq[dd & 1][2 + c]);
+        else mfma_v(sn[k2][c], kq[dd & 1][k2], kq[dd & 1][2 + c]);
+      } else {
+        // MFMA k = s / 2 covers operand group g = k / 2 ((k2, hf) = g / 4, db = g % 4)
+        // and row block c = k % 2; the V^T operand of group g + 2 is read at the first
+        // MFMA of group g
+        constexpr int k = s >> 1, g = k >> 1, c = k & 1;
+        constexpr int k2 = g >> 3, hf = (g >> 2) & 1, db = g & 3;
+        if constexpr (c == 0 && g + 2 < 16) {
+          constexpr int g2 = g + 2;
+          vf[g2 % 3] = vfrag(vt, vofs, g2 >> 3, (g2 >> 2) & 1, g2 & 3);
+        }
+        acc[c][db] = mfma32x32x16(vf[g % 3], pfp[k2][c][hf], acc[c][db]);
+      }
+      if constexpr ((s & 7) == 5) {
+        constexpr int u = s >> 3;  // 0..7: K(t+2) copies, then V(t) copies
+        if constexpr (u < 4) copy_tile(rk, u, kdst);
+        else copy_tile(rv, u - 4, vdst);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        // softmax element s: row block s / 32, element e = s % 32 (key block e / 16,
+        // accumulator element e % 16); input taken one slot ahead, result fenced one slot
+        // late, packing (and its row sum) one slot after the eighth element of a run
+        constexpr int c = s >> 5;
+        const float x = xin;
+        if constexpr (s + 1 < 64) xin = (sc[((s + 1) >> 4) & 1][(s + 1) >> 5][(s + 1) & 15]);
+        if constexpr (s >= 1) {
+          constexpr int p = s - 1, pc = p >> 5, pe = p & 31;
+          pin_out(pb[p & 7]);
+          if constexpr ((p & 7) == 7) {
+            bf16x8& dst = pfc[pe >> 4][pc][(pe >> 3) & 1];
+            pack8(pb, dst, sum[pc]);
+            pin_out(dst);
+            pin_out(sum[pc]);
+          }
+        }
+        pb[s & 7] = __builtin_amdgcn_exp2f(fmaf(x, a.scale_log2, -m[c]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    pin_out(pb[7]);
+    pack8(pb, pfc[1][1][1], sum[1]);
+
+    // reference check on the column sums (both lane halves)
+    float alpha[CB] = {1.f, 1.f};
+    bool redo[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const float cs = sum[c] + swap_halves(sum[c]);
+      const float cl = l[c] + swap_halves(l[c]);
+      redo[c] = (cs > kSumHi) | ((cl == 0.f) & (cs < kSumLo));
+    }
+    if (__builtin_amdgcn_ballot_w64(redo[0] | redo[1]) != 0) {
+      // rare: the tile's column max becomes the reference of the columns that need one
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int k2 = 0; k2 < KB2; ++k2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, (sc[k2][c][i]));
+        const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        const float mt = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * a.scale_log2;
+        const bool mv = redo[c] & (mt > -INFINITY);
+        alpha[c] = mv ? __builtin_amdgcn_exp2f(m[c] - mt) : 1.f;
+        m[c] = mv ? mt : m[c];
+        if (__builtin_amdgcn_ballot_w64(mv) != 0) {
+          const float s2 = softmax_rows(sc, pfc, c, m[c]);
+          sum[c] = mv ? s2 : sum[c];
+        }
+      }
+      // O holds tiles up to t-1 in the previous references: take it to the new ones
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[c][db][i] = agpr_scale(acc[c][db][i], alpha[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) l[c] = l[c] * alpha[c] + sum[c];  // fp32 row sums set LSE
+  };
+
+  // O^T += V(t)^T P(t)^T for the last tile, alone
+  auto last_pv = [&](auto parity) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(parity)::value;
+    const __bf16* const vt = vbuf(IC<PAR>{});
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const bf16x8 vf = vfrag(vt, vofs0, g >> 3, (g >> 2) & 1, g & 3);
+#pragma unroll
+      for (int c = 0; c < CB; ++c) acc[c][g & 3] = mfma32x32x16(vf, pf[PAR][g >> 3][c][(g >> 2) & 1], acc[c][g & 3]);
+    }
+  };
+
+  if (nt > 0) {
+    ent0 = load_uniform(a.row_ent, e0);
+    ent1 = nt > 1 ? load_uniform(a.row_ent, e0 + 1) : 0;
+    ent2 = nt > 2 ? load_uniform(a.row_ent, e0 + 2) : 0;
+    ent_next = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * 3, 0);
+    {
+      const __amdgpu_buffer_rsrc_t rk0 = tile_rsrc(K, ent0, true);
+      const __amdgpu_buffer_rsrc_t rk1 = tile_rsrc(K, ent1, nt > 1);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        copy_tile(rk0, u, sK0);
+        copy_tile(rk1, u, sK1);
+      }
+    }
+    // P(-1) = 0: the first iteration's PV stage adds nothing
+#pragma unroll
+    for (int k2 = 0; k2 < KB2; ++k2)
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) pf[1][k2][c][hf] = zero_bf16x8();
+    wait_loads_and_barrier();
+    // S(0), masked, sets the first reference: its column max (exact P = 1 for the
+    // column's top key, so a column that sees one key reproduces its V row), or 0 for a
+    // column with no visible key in tile 0
+    scores(sx[0]);
+    mask_rows(sx[0], 0, ent0);
+    mask_rows(sx[0], 1, ent0);
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) mx = fmaxf(mx, sx[0][e >> 4][c][e & 15]);
+      const float mt = fmaxf(mx, swap_halves(mx)) * a.scale_log2;
+      m[c] = mt > -INFINITY ? mt : 0.f;
+    }
+    for (int t = 0; t < nt; t += 2) {
+      iteration(IC<0>{}, t);
+      if (t + 1 < nt) iteration(IC<1>{}, t + 1);
+    }
+    wait_loads_and_barrier();  // V(nt-1) resident
+    if ((nt - 1) & 1) last_pv(IC<1>{});
+    else last_pv(IC<0>{});
   }
 
   // ---- finalize: l summed over the two lane halves of a column
