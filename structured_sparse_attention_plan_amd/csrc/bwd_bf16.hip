@@ -196,12 +196,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   // first key of tile tt, and its entry; tiles past the list get an empty copy range
   auto tile_j0 = [&](int ent, int tt) { return (ent >> 1) * BK + (tt & 1) * QBK; };
   __amdgpu_buffer_rsrc_t rk, rv;
+  // the batch's K / V base and byte count are formed once; per tile only the offset
+  const int64_t kv_bytes = (int64_t)a.Lk * HkvD * 2;
+  const char* const kbase = (const char*)(K + (int64_t)b * a.Lk * HkvD);
+  const char* const vbase = (const char*)(V + (int64_t)b * a.Lk * HkvD);
   auto prepare_copy = [&](int ent, int tt, bool real) {
-    const int j0 = tile_j0(ent, tt);
-    const int64_t base = ((int64_t)b * a.Lk + j0) * HkvD;
-    const int64_t bytes = real ? (int64_t)(a.Lk - j0) * HkvD * 2 : 0;
-    rk = make_rsrc(K + base, bytes);
-    rv = make_rsrc(V + base, bytes);
+    const int64_t off = (int64_t)tile_j0(ent, tt) * (HkvD * 2);
+    rk = tile_rsrc(kbase, kv_bytes, off, real);
+    rv = tile_rsrc(vbase, kv_bytes, off, real);
   };
   auto copy = [&](int i, __bf16* kd, __bf16* vd) {  // copy i of 8 (u = i / 2, K then V)
     const int u = i >> 1;
@@ -219,12 +221,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   };
 
   if (n_ent > 0) {
-    // entries of tiles t, t+1, t+2 (two tiles per entry), read ahead with scalar loads
+    // entries of tiles t, t+1, t+2 (two tiles per entry).  The entry after them is
+    // fetched by a vector load (a scalar load would share its wait counter with the LDS
+    // operand reads) through a resource over this item's entries, so a fetch past the end
+    // reads 0 (only ever used for tiles that are not copied), and taken two tiles later.
+    const __amdgpu_buffer_rsrc_t r_ent = make_rsrc(a.row_ent + e0, (int64_t)n_ent * 4);
     int ent[3];
     ent[0] = load_uniform(a.row_ent, e0);
     ent[1] = ent[0];
     ent[2] = n_ent > 1 ? load_uniform(a.row_ent, e0 + 1) : ent[0];
-    int ent_next = n_ent > 2 ? load_uniform(a.row_ent, e0 + 2) : ent[2];
+    int ent_next = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * 2, 0);
 
     // prologue: tiles 0 and 1 resident; S, dP of tile 0
     prepare_copy(ent[0], 0, true);
@@ -335,9 +341,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
       if (tt & 1) {
         ent[0] = ent[2];
         ent[1] = ent[2];
-        ent[2] = ent_next;
+        ent[2] = __builtin_amdgcn_readfirstlane(ent_next);
         const int en = ((tt + 1) >> 1) + 2;  // entry of tile tt + 5
-        if (en < n_ent) ent_next = load_uniform(a.row_ent, e0 + en);
+        ent_next = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * en, 0);
       } else {
         ent[0] = ent[1];
       }
@@ -521,12 +527,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // Delta of its rows into registers; copy(i) issues copy i of 16 (u = i / 2, Q then dO)
   // into buffer bufc, so the copies can be spread over MFMA slots.
   __amdgpu_buffer_rsrc_t rq_n, rd_n;
+  const int64_t qd_bytes = (int64_t)a.Lq * HqD * 2;
+  const char* const qbase = (const char*)(Q + (int64_t)b * a.Lq * HqD);
+  const char* const dobase = (const char*)(dO + (int64_t)b * a.Lq * HqD);
   auto prepare_entry = [&](int qb, bool real) {
     const int t0 = qb * Bq;
-    const int64_t base = ((int64_t)b * a.Lq + t0) * HqD;
-    const int64_t bytes = real ? (int64_t)(a.Lq - t0) * HqD * 2 : 0;
-    rq_n = make_rsrc(Q + base, bytes);
-    rd_n = make_rsrc(dO + base, bytes);
+    const int64_t off = (int64_t)t0 * (HqD * 2);
+    rq_n = tile_rsrc(qbase, qd_bytes, off, real);
+    rd_n = tile_rsrc(dobase, qd_bytes, off, real);
     if (tid < ROWS) {
       pvalid = my_rt < Bq && t0 + my_rt < a.Lq;
       // rows past Lq read row Lq - 1 (in bounds; discarded by pvalid)
@@ -571,8 +579,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   if (n_ent > 0) {
     int ent_c = load_uniform(a.col_ent, e0);  // entry of the current q-block
-    // entry of the next q-block, read one q-block before it is needed
-    int ent_ahead = n_ent > 1 ? load_uniform(a.col_ent, e0 + 1) : 0;
+    // entry of the next q-block, fetched one q-block before it is needed by a vector load
+    // (a scalar load would share its wait counter with the LDS operand reads) through a
+    // resource over this item's entries (a fetch past the end reads 0 and is not used)
+    const __amdgpu_buffer_rsrc_t r_ent = make_rsrc(a.col_ent + e0, (int64_t)n_ent * 4);
+    int ent_ahead = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * 1, 0);
     int ent_n = ent_c;
     prepare_entry(ent_c >> 1, true);
 #pragma unroll
@@ -626,9 +637,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         // every wave is done with q-block e - 1: its buffer takes q-block e + 1, copied
         // during the phase-2 MFMAs of this step and the next
         __syncthreads();
-        if (more) ent_n = ent_ahead;
+        const int ea = __builtin_amdgcn_readfirstlane(ent_ahead);
+        if (more) ent_n = ea;
         prepare_entry(ent_n >> 1, more);
-        if (e + 2 < n_ent) ent_ahead = load_uniform(a.col_ent, e0 + e + 2);
+        ent_ahead = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * (e + 2), 0);
       }
       const int ent_g1 = RB == 3 ? ent_n : ent_c;  // entry of the next block
       if constexpr (RB == 3) {

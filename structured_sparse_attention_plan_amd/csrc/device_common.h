@@ -89,6 +89,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 
+// Resource over [base + off, base + total) (empty when !real): per copy tile only the
+// offset product and a 64-bit add and subtract run on the scalar unit, the base and
+// total being formed once per work item.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int64_t total, int64_t off,
+                                                           bool real) {
+  const int64_t left = total - off;
+  const int n = (!real || left <= 0) ? 0 : left < 0x7fffffff ? (int)left : 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), (short)0, n, 0x00020000);
+}
+
 // One 1 KB direct buffer->LDS copy per wave: lane L moves the 16 bytes at byte offset
 // voff of the resource to lds + 16 L (lds is wave-uniform).
 __device__ __forceinline__ void buf2lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, __bf16* lds) {

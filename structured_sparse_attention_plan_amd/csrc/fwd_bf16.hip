@@ -200,16 +200,14 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     const int r = 16 * wave + 4 * u + lrow;
     voff[u] = 2u * (uint32_t)(r * HkvD + h * D + 8 * (lchunk ^ sw(r)));
   }
-  // Per tile only a 32-bit product and a 64-bit add remain on the scalar unit (the
-  // batch's base and byte count are formed once per item; K/V of one batch are < 2 GB).
-  const uint32_t tile_bytes = (uint32_t)(BK * HkvD * 2);
-  const uint32_t kv_bytes = (uint32_t)min((int64_t)a.Lk * HkvD * 2, (int64_t)0x7fffffff);
+  // The batch's base and byte count are formed once per item; per tile only the offset
+  // remains on the scalar unit.
+  const int tile_bytes = BK * HkvD * 2;
+  const int64_t kv_bytes = (int64_t)a.Lk * HkvD * 2;
   const char* const kbase = (const char*)(K + (int64_t)b * a.Lk * HkvD);
   const char* const vbase = (const char*)(V + (int64_t)b * a.Lk * HkvD);
-  auto tile_rsrc = [&](const char* base, int ent, bool real) __attribute__((always_inline)) {
-    const uint32_t off = (uint32_t)(ent >> 1) * tile_bytes;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), (short)0, real ? (int)(kv_bytes - off) : 0,
-                                             0x00020000);
+  auto tile_copy_rsrc = [&](const char* base, int ent, bool real) __attribute__((always_inline)) {
+    return tile_rsrc(base, kv_bytes, (int64_t)(ent >> 1) * tile_bytes, real);
   };
   auto copy_tile = [&](__amdgpu_buffer_rsrc_t r, int u, __bf16* dst) __attribute__((always_inline)) {
     buf2lds(r, voff[u], dst + (16 * wave + 4 * u) * D);
@@ -369,8 +367,8 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     bf16x8(&pfc)[KB2][CB][2] = pf[PAR];
     const bf16x8(&pfp)[KB2][CB][2] = pf[PAR ^ 1];
     wait_loads_and_barrier();  // K(t+1), V(t-1) resident; every wave is done with t-1
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, ent2, t + 2 < nt);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase, ent0, true);
+    const __amdgpu_buffer_rsrc_t rk = tile_copy_rsrc(kbase, ent2, t + 2 < nt);
+    const __amdgpu_buffer_rsrc_t rv = tile_copy_rsrc(vbase, ent0, true);
     __bf16* const kdst = kbuf(IC<PAR>{});          // K(t+2)
     __bf16* const vdst = vbuf(IC<PAR>{});          // V(t)
     const __bf16* const kt = kbuf(IC<PAR ^ 1>{});  // K(t+1)
@@ -513,8 +511,8 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     ent2 = nt > 2 ? load_uniform(a.row_ent, e0 + 2) : 0;
     ent_next = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * 3, 0);
     {
-      const __amdgpu_buffer_rsrc_t rk0 = tile_rsrc(kbase, ent0, true);
-      const __amdgpu_buffer_rsrc_t rk1 = tile_rsrc(kbase, ent1, nt > 1);
+      const __amdgpu_buffer_rsrc_t rk0 = tile_copy_rsrc(kbase, ent0, true);
+      const __amdgpu_buffer_rsrc_t rk1 = tile_copy_rsrc(kbase, ent1, nt > 1);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         copy_tile(rk0, u, sK0);
