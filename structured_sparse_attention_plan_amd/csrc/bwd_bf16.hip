@@ -394,6 +394,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 // filled by direct global->LDS copies issued one q-block ahead.
 constexpr int QTILE = ROWS * D;  // one q-block of Q (or dO) in LDS
 
+// (x0, x1) -> packed bf16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
+  const bf16x2 h = {(__bf16)x0, (__bf16)x1};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // One pair of the hi/lo split: (x0, x1) -> bf16 pair hi = bf16(x), lo = bf16(x - hi).
 __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
   const bf16x2 h = {(__bf16)x0, (__bf16)x1};
@@ -569,10 +575,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  // Carried from one step to the next: P of the block as packed bf16 hi and lo (2 halves
-  // x 4 words), and dS in fp32 (split in the next step's phase 1).
+  // Carried from one step to the next: P of the block as packed bf16 (2 halves x 4
+  // words), and dS in fp32 (split into hi and lo bf16 in the next step's phase 1).
+  // P in [0, 1] is rounded to bf16 once; dS keeps the hi/lo pair (dK sums the products of
+  // many rows per key, where one rounding of dS is not accurate enough).
   struct Carry {
-    uint32_t pa[2][4], pl[2][4];
+    uint32_t pa[2][4];
     float ds[16];
   };
   auto as_bf16x8 = [](const uint32_t (&w)[4]) { return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]}); };
@@ -615,13 +623,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) split_pair(pr[2 * k], pr[2 * k + 1], wA.pa[k >> 2][k & 3], wA.pl[k >> 2][k & 3]);
+      for (int k = 0; k < 8; ++k) wA.pa[k >> 2][k & 3] = pack_bf16x2(pr[2 * k], pr[2 * k + 1]);
     }
 
     // One pipeline step for row block RB of the q-block in buffer BUF (both compile-time).
     // Phase 1: S, dP of the next block (16 MFMAs) with the hi/lo split of dS(g) between
-    // them.  Phase 2: dV, dK of block g (32 MFMAs) with P, dS of the next block and the
-    // split of its P between them.  After the item's last block the "next" block is the
+    // them.  Phase 2: dV, dK of block g (24 MFMAs: dV from P, dK from dS hi and lo) with
+    // P, dS of the next block and the packing of its P between them.  After the item's last block the "next" block is the
     // resident other buffer's first block: computed and discarded, so the step has no
     // branches inside its interleaved parts.
     auto step = [&](auto rbc, auto bufc, const int e, const Carry& cur, Carry& nxt) {
@@ -713,37 +721,40 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) l4[i4] = *(const f32x4*)(lt + 8 * i4);
       const bf16x8 pa[2] = {as_bf16x8(cur.pa[0]), as_bf16x8(cur.pa[1])};
-      const bf16x8 pl[2] = {as_bf16x8(cur.pl[0]), as_bf16x8(cur.pl[1])};
       const bf16x8 sa[2] = {as_bf16x8(wsa[0]), as_bf16x8(wsa[1])};
       const bf16x8 sl[2] = {as_bf16x8(wsl[0]), as_bf16x8(wsl[1])};
       float snv[2], dpv[2];
       snv[0] = pin(sn[0]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int x = 0; x < 32; ++x) {
-        // MFMA x: half hf, hi products (k < 8) then lo products, V and K alternating
-        const int hf = x >> 4, k = x & 15, db = (k & 7) >> 1;
+      for (int x = 0; x < 24; ++x) {
+        // MFMA x: half hf = x / 12; k = x % 12: dV (k even < 8) and dK hi (k odd < 8) for
+        // db = k / 2, then dK lo for db = k - 8
+        const int hf = x / 12, k = x % 12;
         if (k < 8) {
+          const int db = k >> 1;
           if (k & 1) accK[db] = mfma32x32x16(sa[hf], qt[hf][db], accK[db]);
           else accV[db] = mfma32x32x16(pa[hf], dt[hf][db], accV[db]);
         } else {
-          if (k & 1) accK[db] = mfma32x32x16(sl[hf], qt[hf][db], accK[db]);
-          else accV[db] = mfma32x32x16(pl[hf], dt[hf][db], accV[db]);
+          const int db = k - 8;
+          accK[db] = mfma32x32x16(sl[hf], qt[hf][db], accK[db]);
         }
-        // transposed operands of half 1, each read right after its half-0 register is
-        // last used (MFMA 8 + 2 db for dO, 9 + 2 db for Q), 7 MFMAs before its own use
-        if (x >= 9 && x <= 16) {
-          const int db1 = (x - 9) >> 1;
-          const __bf16* th = tg + 2048 + (((x - 9) & 1) ? 0 : QTILE);
-          const bf16x8 v = join(lds_read_tr4(th + ofs_t(0, db1)), lds_read_tr4(th + ofs_t(1, db1)));
-          if ((x - 9) & 1) qt[1][db1] = v;
-          else dt[1][db1] = v;
+        // transposed operands of half 1, each read right after its half-0 register is last
+        // used: dO^T (db) after MFMA 2 db, read at 2 db + 1; Q^T (db) after MFMA 8 + db,
+        // read at 9 + db (used from MFMA 12 + 2 db and 13 + 2 db on)
+        if (x == 1 || x == 3 || x == 5 || x == 7) {
+          const int db1 = (x - 1) >> 1;
+          dt[1][db1] = join(lds_read_tr4(tg + 2048 + QTILE + ofs_t(0, db1)), lds_read_tr4(tg + 2048 + QTILE + ofs_t(1, db1)));
+        }
+        if (x >= 9 && x <= 12) {
+          const int db1 = x - 9;
+          qt[1][db1] = join(lds_read_tr4(tg + 2048 + ofs_t(0, db1)), lds_read_tr4(tg + 2048 + ofs_t(1, db1)));
         }
         // copies of the next q-block: 8 in each of the first two steps, one every 2 MFMAs
         if constexpr (RB < 2)
-          if (x >= 17 && (x & 1)) copy(8 * RB + ((x - 17) >> 1), IC<BUF ^ 1>{});
+          if (x >= 9 && (x & 1)) copy(8 * RB + ((x - 9) >> 1), IC<BUF ^ 1>{});
         __builtin_amdgcn_sched_barrier(0);
-        // P (exp) in steps 0..15, dS 4 steps behind, the split of P pair q in step 2q + 17.
+        // P (exp) in steps 0..15, dS 4 steps behind, the packing of P pair q in step 16 + q.
         // Inputs are taken (pin) one step before use and results fenced (pin_out) one step
         // after they are made: each piece stays in its slot without stalling on itself.
         if (x < 16) pr[x] = __builtin_amdgcn_exp2f(fmaf(snv[x & 1], a.scale_log2, -l4[x >> 2][x & 3]));
@@ -756,19 +767,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
         if (x >= 3 && x < 19) dpv[(x - 3) & 1] = pin(dpn[x - 3]);
         if (x >= 5 && x <= 20) pin_out(nxt.ds[x - 5]);
-        if (x >= 16 && (x & 1)) {
-          const int q = (x - 17) >> 1;
-          split_pair(pr[2 * q], pr[2 * q + 1], nxt.pa[q >> 2][q & 3], nxt.pl[q >> 2][q & 3]);
+        if (x >= 16) {
+          const int q = x - 16;
+          nxt.pa[q >> 2][q & 3] = pack_bf16x2(pr[2 * q], pr[2 * q + 1]);
         }
-        if (x >= 18 && !(x & 1)) {
-          const int q = (x - 18) >> 1;
+        if (x >= 17) {
+          const int q = x - 17;
           pin_out(nxt.pa[q >> 2][q & 3]);
-          pin_out(nxt.pl[q >> 2][q & 3]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       pin_out(nxt.pa[1][3]);
-      pin_out(nxt.pl[1][3]);
       if constexpr (RB == 3) ent_c = ent_n;
     };
     auto entry = [&](auto bufc, const int e) {
