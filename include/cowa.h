@@ -153,8 +153,9 @@ typedef struct cowa_problem {
  * op must be built with them.  Errors: INVALID_ARG, UNSUPPORTED. */
 int cowa_tile_sizes(int op, const cowa_problem* p, int32_t* Bq, int32_t* Bk);
 
-/* Bytes of device workspace `op` needs for problem p (0 if none).  The backward needs
- * an fp32 dQ accumulator and the per-row Delta; the decode needs its split partials. */
+/* Bytes of device workspace `op` needs for problem p (0 if none).  The backward keeps
+ * Delta and a power-of-two scale per (query head, row) in fp32 and an fp16 copy of Q
+ * (B * Lq * Hq * D * 2 bytes); the decode keeps its split partials. */
 int cowa_workspace_size(int op, const cowa_problem* p, size_t* bytes);
 
 /* Forward (the operator of the abstract; training forward and prefill).  For every
@@ -174,9 +175,14 @@ int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan,
  *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO   (dK, dV summed over the
  *   query heads of each KV head).
  * `stages` selects the kernels to run (COWA_BWD_ALL for the whole backward): DELTA
- * writes Delta into the workspace; DQ and DKDV read it from there, so a caller that runs
- * them separately (for example on two streams) must run DELTA first on the same
- * workspace.  dQ is written by DQ, dK and dV by DKDV; no output is accumulated into.
+ * writes Delta, the row scales of Q and the fp16 copy of Q into the workspace; DQ and
+ * DKDV read them from there, so a caller that runs them separately (for example on two
+ * streams) must run DELTA first on the same workspace.  dK is formed from dS and Q in
+ * fp16: each row of Q is divided by a power of two that puts its max |q| in [1, 2),
+ * which copies every entry of at least 2^-14 times the row's max exactly, and dS is
+ * scaled by the same power; the result stays finite while |dS| times the row's max |q|
+ * stays below 2^15.  dQ is written by DQ, dK and dV by DKDV; no output is accumulated
+ * into.
  * Supported: dtype BF16, D = 128.  All tensors bf16 except lse (fp32).  The plan must
  * hold both row and column lists at cowa_tile_sizes(COWA_OP_BWD).  workspace must be
  * at least cowa_workspace_size(COWA_OP_BWD) bytes, 256-byte aligned.

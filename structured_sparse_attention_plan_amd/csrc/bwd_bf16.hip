@@ -7,7 +7,8 @@
 //   P = exp(scale q.k - LSE), Delta_i = dO_i . O_i, dP = dO V^T, dS = P (dP - Delta)
 //   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO
 // Three kernels, no atomics (deterministic):
-//   delta  : Delta per (row, query head);
+//   delta  : Delta per (row, query head), and an fp16 copy of Q scaled per row by a
+//            power of two;
 //   dq     : one work item per (KV head, q-block of 128 / G tokens), walking the row list
 //            of visible 128-key blocks: S^T, dP^T, dS^T on MFMA, dQ^T += K^T dS^T with
 //            K^T read by ds_read_b64_tr_b16 from the row-major LDS tile;
@@ -15,8 +16,9 @@
 //            visible q-blocks; each of the 4 waves keeps 32 keys of K and V in registers
 //            and accumulates dK, dV for them over all G query heads of the KV head:
 //            S = Q K^T and dP = dO V^T on MFMA, then dV += P^T dO and dK += dS^T Q with
-//            P, dS taken from the accumulator registers as A operands (each as a bf16
-//            hi + lo pair) and dO, Q read transposed from LDS.
+//            P (bf16) and dS (fp16) packed from the accumulator registers as A operands
+//            and dO, Q read transposed from LDS; Q, K and dS enter the S and dK products
+//            in fp16 (exact power-of-two scalings undone through per-row constants).
 // Rows of a q-block are token-major (row r = token * G + head-in-group); rows beyond
 // G * Bq or Lq carry LSE = +inf and Delta = 0 so that they contribute nothing.
 
@@ -43,30 +45,48 @@ __device__ __forceinline__ void pin_out(uint32_t& x) { asm volatile("" : "+v"(x)
 __device__ __forceinline__ void pin_out(float& x) { asm volatile("" : "+v"(x)); }
 
 // ------------------------------------------------------------------------ Delta
+// Per row (token, query head): Delta = dO . O, and the fp16 copy of q that the dK
+// product reads, q / 2^e with max |q| / 2^e in [1, 2) (2^e stored beside Delta).  Sixteen
+// lanes per row, 8 elements each.
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b, t, hq) flat
   const int li = threadIdx.x & 15;
   const int64_t nrows = (int64_t)a.B * a.Lq * a.Hq;
-  float acc = 0.f;
+  float acc = 0.f, qm = 0.f;
+  u32x4 qw = {0u, 0u, 0u, 0u};
   if (row < nrows) {
     const u32x4 ow = *(const u32x4*)((const __bf16*)a.o + row * D + 8 * li);
     const u32x4 dw = *(const u32x4*)((const __bf16*)a.dout + row * D + 8 * li);
+    qw = *(const u32x4*)((const __bf16*)a.q + row * D + 8 * li);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       acc = fmaf(__uint_as_float(ow[k] << 16), __uint_as_float(dw[k] << 16), acc);
       acc = fmaf(__uint_as_float(ow[k] & 0xffff0000u), __uint_as_float(dw[k] & 0xffff0000u), acc);
+      qm = fmaxf(qm, fmaxf(fabsf(__uint_as_float(qw[k] << 16)), fabsf(__uint_as_float(qw[k] & 0xffff0000u))));
     }
   }
-  acc += __shfl_xor(acc, 1, 16);
-  acc += __shfl_xor(acc, 2, 16);
-  acc += __shfl_xor(acc, 4, 16);
-  acc += __shfl_xor(acc, 8, 16);
-  if (row < nrows && li == 0) {
-    const int hq = (int)(row % a.Hq);
-    const int64_t bt = row / a.Hq;
-    const int t = (int)(bt % a.Lq);
-    const int b = (int)(bt / a.Lq);
-    a.delta[((int64_t)b * a.Hq + hq) * a.Lq + t] = acc;
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    acc += __shfl_xor(acc, m, 16);
+    qm = fmaxf(qm, __shfl_xor(qm, m, 16));
+  }
+  if (row < nrows) {
+    const int qe = pow2_exponent(qm);
+    u32x4 hw;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      hw[k] = pack_f16x2(__builtin_amdgcn_ldexpf(__uint_as_float(qw[k] << 16), -qe),
+                         __builtin_amdgcn_ldexpf(__uint_as_float(qw[k] & 0xffff0000u), -qe));
+    *(u32x4*)((uint16_t*)a.q16 + row * D + 8 * li) = hw;
+    if (li == 0) {
+      const int hq = (int)(row % a.Hq);
+      const int64_t bt = row / a.Hq;
+      const int t = (int)(bt % a.Lq);
+      const int b = (int)(bt / a.Lq);
+      const int64_t o = ((int64_t)b * a.Hq + hq) * a.Lq + t;
+      a.delta[o] = acc;
+      a.qscale[o] = __builtin_amdgcn_ldexpf(1.f, qe);
+    }
   }
 }
 
@@ -386,12 +406,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------ dK, dV
-// Software pipeline over the 32-row blocks g of the item's column list (4 per q-block):
-// step g issues S, dP of block g + 1 (16 MFMAs, phase 1), then dV, dK of block g
-// (32 MFMAs, phase 2) with the VALU work of block g + 1 (P, dS and their hi/lo split)
-// placed between those MFMAs by scheduling fences, so the matrix core and the VALU run
-// at the same time.  The Q and dO tiles of a q-block are double-buffered in LDS and
-// filled by direct global->LDS copies issued one q-block ahead.
+// Software pipeline over the 32-row blocks g of the item's column list (4 per q-block).
+// Step g: phase 1 issues S and dP of block g + 1 (16 MFMAs) with dS of block g and the
+// packing of P and dS of block g between them; phase 2 issues dV and dK of block g (16
+// MFMAs) with P of block g + 1 between them.  Scheduling fences keep each piece of VALU
+// work in its slot, so the matrix core and the VALU run at the same time.  The Q and dO
+// tiles of a q-block are double-buffered in LDS and filled by direct global->LDS copies
+// issued one q-block ahead.
+//
+// dK is formed in fp16: dS and Q are each rounded once to fp16 (10-bit mantissa), which
+// keeps dK well inside the bf16 tolerance (a single bf16 rounding of dS is not enough:
+// dK sums the products of many rows whose dS nearly cancel).  Q comes from the fp16
+// copy the Delta kernel writes, each row divided by 2^e_r (its max |q| then in [1, 2)),
+// so the copy is exact; S = Q K^T then also runs in fp16, with K divided by 2^e_K per
+// work item.  The scales come back through per-row constants:
+//   P = exp2(S16 c_r - LSE_r log2 e)   with c_r = scale log2(e) 2^(e_r + e_K),
+//   dS16 = 2^e_r dS = P (2^e_r dP - 2^e_r Delta_r),   so dS16^T Q16 = dS^T Q.
 constexpr int QTILE = ROWS * D;  // one q-block of Q (or dO) in LDS
 
 // (x0, x1) -> packed bf16 pair, round to nearest even.
@@ -400,27 +430,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// One pair of the hi/lo split: (x0, x1) -> bf16 pair hi = bf16(x), lo = bf16(x - hi).
-__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const bf16x2 h = {(__bf16)x0, (__bf16)x1};
-  const uint32_t w = __builtin_bit_cast(uint32_t, h);
-  const float h0 = __uint_as_float(__builtin_amdgcn_perm(w, w, 0x01000c0cu));  // w << 16
-  const float h1 = __uint_as_float(w & 0xffff0000u);
-  const bf16x2 l = {(__bf16)(x0 - h0), (__bf16)(x1 - h1)};
-  hi = w;
-  lo = __builtin_bit_cast(uint32_t, l);
+// bf16 x -> fp16 bits of x / 2^e (exact while |x| / 2^e is in the fp16 normal range).
+__device__ __forceinline__ bf16x8 bf16_to_f16_scaled(const bf16x8& x, int e) {
+  const u32x4 w = __builtin_bit_cast(u32x4, x);
+  u32x4 h;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    h[q] = pack_f16x2(__builtin_amdgcn_ldexpf(__uint_as_float(w[q] << 16), -e),
+                      __builtin_amdgcn_ldexpf(__uint_as_float(w[q] & 0xffff0000u), -e));
+  return __builtin_bit_cast(bf16x8, h);
 }
 
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  // Q and dO of a q-block, [Q, dO][rows] with swizzled 256-byte rows (lds_swz); dO sits at
-  // a fixed distance from Q, so one address serves both.  Two separate arrays (not one
-  // indexed by the buffer): every read names the array it reads, so the compiler can tell
-  // it apart from the copies in flight into the other one and does not wait for them.
+  // Q (fp16 copy) and dO of a q-block, [Q, dO][rows] with swizzled 256-byte rows
+  // (lds_swz); dO sits at a fixed distance from Q, so one address serves both.  Two
+  // separate arrays (not one indexed by the buffer): every read names the array it reads,
+  // so the compiler can tell it apart from the copies in flight into the other one and
+  // does not wait for them.
   __shared__ __attribute__((aligned(1024))) __bf16 sQD0[2 * QTILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sQD1[2 * QTILE];
-  __shared__ __attribute__((aligned(16))) float sLT0[2 * ROWS];  // [LSE * log2 e, Delta][rows]
-  __shared__ __attribute__((aligned(16))) float sLT1[2 * ROWS];
+  // per-row constants of a q-block: [LSE log2 e, c_r, 2^e_r, 2^e_r Delta][rows]
+  __shared__ __attribute__((aligned(16))) float sLT0[4 * ROWS];
+  __shared__ __attribute__((aligned(16))) float sLT1[4 * ROWS];
   __shared__ int sRt[ROWS];  // row -> token in the q-block
+  __shared__ float sKmax[4];  // max |k| of each wave's keys
   auto tiles = [&](auto bufc) -> __bf16* {
     if constexpr (decltype(bufc)::value == 0) return sQD0;
     else return sQD1;
@@ -443,7 +476,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int off = a.Lk - a.Lq;
   const HeadBand band = head_band(a.win, h);
 
-  const __bf16* Q = (const __bf16*)a.q;
+  const uint16_t* Q16 = (const uint16_t*)a.q16;
   const __bf16* K = (const __bf16*)a.k;
   const __bf16* V = (const __bf16*)a.v;
   const __bf16* dO = (const __bf16*)a.dout;
@@ -471,7 +504,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       vf[dd] = kvalid ? load16(V + ko + 16 * dd) : zero_bf16x8();
       // held in AGPRs (MFMA reads its A/B operands from either file): leaves the VGPRs
       // to the pipeline's temporaries
-      asm volatile("" : "+a"(kf[dd]));
       asm volatile("" : "+a"(vf[dd]));
     }
   }
@@ -513,28 +545,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
     voff_u[u] = 2u * (uint32_t)(rt * HqD + (h * G + g) * D + 8 * ((lane & 15) ^ lds_sw(r)));
   }
-  // LSE / Delta staging: thread tid < ROWS owns row tid of the next q-block.  The raw
+  // Row constants staging: thread tid < ROWS owns row tid of the next q-block.  The raw
   // loaded values are only touched when stored to LDS (after the wait that precedes the
   // q-block's first use), so the loads do not stall the wave when they are issued.
   const int my_rt = tid / G, my_g = tid - my_rt * G;
-  float plse = 0.f, pdel = 0.f;
+  float plse = 0.f, pdel = 0.f, pqs = 1.f, ck = a.scale_log2;
   bool pvalid = false;
-  // LSE and Delta rows of this KV head's G query heads, [G, Lq] each
+  // LSE, Delta and Q row scales of this KV head's G query heads, [G, Lq] each
   const int64_t lt_base = ((int64_t)b * a.Hq + h * G) * a.Lq;
   const __amdgpu_buffer_rsrc_t r_lse = make_rsrc(a.lse + lt_base, (int64_t)G * a.Lq * 4);
   const __amdgpu_buffer_rsrc_t r_del = make_rsrc(a.delta + lt_base, (int64_t)G * a.Lq * 4);
+  const __amdgpu_buffer_rsrc_t r_qs = make_rsrc(a.qscale + lt_base, (int64_t)G * a.Lq * 4);
 
   const int e0 = load_uniform(a.col_ptr, item);
   const int n_ent = load_uniform(a.col_ptr, item + 1) - e0;
 
   // Copies of q-block qb's Q and dO rows: prepare_entry builds the two buffer resources
   // (scalar; the range ends at token Lq, so rows past Lq read zeros; an empty range when
-  // there is no next q-block, so the copies then touch no memory) and loads the LSE /
-  // Delta of its rows into registers; copy(i) issues copy i of 16 (u = i / 2, Q then dO)
-  // into buffer bufc, so the copies can be spread over MFMA slots.
+  // there is no next q-block, so the copies then touch no memory) and loads the row
+  // constants into registers; copy(i) issues copy i of 16 (u = i / 2, Q then dO) into
+  // buffer bufc, so the copies can be spread over MFMA slots.
   __amdgpu_buffer_rsrc_t rq_n, rd_n;
   const int64_t qd_bytes = (int64_t)a.Lq * HqD * 2;
-  const char* const qbase = (const char*)(Q + (int64_t)b * a.Lq * HqD);
+  const char* const qbase = (const char*)(Q16 + (int64_t)b * a.Lq * HqD);
   const char* const dobase = (const char*)(dO + (int64_t)b * a.Lq * HqD);
   auto prepare_entry = [&](int qb, bool real) {
     const int t0 = qb * Bq;
@@ -547,18 +580,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const uint32_t vo = 4u * (uint32_t)(my_g * a.Lq + min(t0 + my_rt, a.Lq - 1));
       plse = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_lse, vo, 0, 0));
       pdel = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_del, vo, 0, 0));
+      pqs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_qs, vo, 0, 0));
     }
   };
   auto copy = [&](int i, auto bufc) {
     __bf16* dst = tiles(bufc) + wave * 32 * D + 4 * (i >> 1) * D + ((i & 1) ? QTILE : 0);
     buf2lds((i & 1) ? rd_n : rq_n, voff_u[i >> 1], dst);
   };
-  // rows with no token or no visible key: LSE +inf (P = 0) and Delta 0
+  // Rows with no token or no visible key: LSE +inf (P = 0), c_r > 0 (so that a masked
+  // S = -inf still gives P = 0), and 0 for the dS scale and Delta.  ck = scale log2(e)
+  // 2^e_K.
   auto store_lse = [&](auto bufc) {
     if (tid < ROWS) {
       float* lt = lts(bufc);
       lt[tid] = (pvalid && plse != -INFINITY) ? plse * kLog2e : INFINITY;
-      lt[ROWS + tid] = pvalid ? pdel : 0.f;
+      lt[ROWS + tid] = pvalid ? ck * pqs : ck;
+      lt[2 * ROWS + tid] = pvalid ? pqs : 0.f;
+      lt[3 * ROWS + tid] = pvalid ? pdel * pqs : 0.f;
     }
   };
   // boundary q-block: the window predicate per element (S = -inf where hidden)
@@ -575,64 +613,104 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  // Carried from one step to the next: P of the block as packed bf16 (2 halves x 4
-  // words), and dS in fp32 (split into hi and lo bf16 in the next step's phase 1).
-  // P in [0, 1] is rounded to bf16 once; dS keeps the hi/lo pair (dK sums the products of
-  // many rows per key, where one rounding of dS is not accurate enough).
+  // Carried from one step to the next: P of the block in fp32, dP as the MFMA left it,
+  // and the first group of the block's dS constants (2^e_r, 2^e_r Delta), read early so
+  // the next step's first slot does not wait for LDS.
   struct Carry {
-    uint32_t pa[2][4];
-    float ds[16];
+    float pr[16];
+    f32x16 dp;
+    f32x4 f0, t0;
   };
   auto as_bf16x8 = [](const uint32_t (&w)[4]) { return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]}); };
 
   if (n_ent > 0) {
-    int ent_c = load_uniform(a.col_ent, e0);  // entry of the current q-block
+    // The list is walked cyclically from its first q-block at or after the one holding
+    // token (kb | 31) Bk.  The work items an XCD runs together are about 32 neighbouring
+    // k-blocks of one head, whose lists are near-translates of each other and all hold
+    // that q-block: started there, they read the same Q / dO tiles at the same time (one
+    // L2 fill serves all of them) instead of ranges shifted by Bk tokens per k-block.
+    int rot = 0;
+    {
+      const int qa = max(0, ((kb | 31) * BK - off) / Bq);
+      int lo = 0, hi = n_ent;  // first index whose q-block is >= qa (the list ascends)
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((load_uniform(a.col_ent, e0 + mid) >> 1) < qa) lo = mid + 1;
+        else hi = mid;
+      }
+      rot = lo < n_ent ? lo : 0;
+    }
+    auto ent_index = [&](int e) {  // list index of walk position e (e < 2 n_ent)
+      const int i = e + rot;
+      return i >= n_ent ? i - n_ent : i;
+    };
+    int ent_c = load_uniform(a.col_ent, e0 + rot);  // entry of the current q-block
     // entry of the next q-block, fetched one q-block before it is needed by a vector load
     // (a scalar load would share its wait counter with the LDS operand reads) through a
     // resource over this item's entries (a fetch past the end reads 0 and is not used)
     const __amdgpu_buffer_rsrc_t r_ent = make_rsrc(a.col_ent + e0, (int64_t)n_ent * 4);
-    int ent_ahead = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * 1, 0);
+    int ent_ahead = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * ent_index(1), 0);
     int ent_n = ent_c;
     prepare_entry(ent_c >> 1, true);
 #pragma unroll
     for (int i = 0; i < 16; ++i) copy(i, IC<0>{});
+    // K of the work item in fp16, divided by 2^e_K (max |k| over its 128 keys then in
+    // [1, 2)): each wave's max goes through LDS
+    {
+      float km = 0.f;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const u32x4 w = __builtin_bit_cast(u32x4, kf[dd]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          km = fmaxf(km, fmaxf(fabsf(__uint_as_float(w[q] << 16)), fabsf(__uint_as_float(w[q] & 0xffff0000u))));
+      }
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) km = fmaxf(km, __shfl_xor(km, m));
+      if (lane == 0) sKmax[wave] = km;
+    }
     wait_loads_and_barrier();
+    {
+      const int ek = pow2_exponent(fmaxf(fmaxf(sKmax[0], sKmax[1]), fmaxf(sKmax[2], sKmax[3])));
+      ck = a.scale_log2 * __builtin_amdgcn_ldexpf(1.f, ek);
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        kf[dd] = bf16_to_f16_scaled(kf[dd], ek);
+        asm volatile("" : "+a"(kf[dd]));
+      }
+    }
     store_lse(IC<0>{});
     __syncthreads();
 
     Carry wA, wB;
-    {  // prologue: S, dP, P (split) and dS of block 0
-      f32x16 s, dp;
+    {  // prologue: S, dP and P of block 0
+      f32x16 s;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+      for (int i = 0; i < 16; ++i) s[i] = wA.dp[i] = 0.f;
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
-        s = mfma32x32x16(load16(sQD0 + ofs_a(dd)), kf[dd], s);
-        dp = mfma32x32x16(load16(sQD0 + QTILE + ofs_a(dd)), vf[dd], dp);
+        s = mfma32x32x16_f16(load16(sQD0 + ofs_a(dd)), kf[dd], s);
+        wA.dp = mfma32x32x16(load16(sQD0 + QTILE + ofs_a(dd)), vf[dd], wA.dp);
       }
       if (ent_c & 1) mask(s, 0, ent_c >> 1);
-      float pr[16];
+      const float* lt = sLT0 + 4 * h2;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 l4 = *(const f32x4*)(sLT0 + 8 * i4 + 4 * h2);
-        const f32x4 t4 = *(const f32x4*)(sLT0 + ROWS + 8 * i4 + 4 * h2);
+        const f32x4 l4 = *(const f32x4*)(lt + 8 * i4);
+        const f32x4 c4 = *(const f32x4*)(lt + ROWS + 8 * i4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[4 * i4 + i] = __builtin_amdgcn_exp2f(fmaf(s[4 * i4 + i], a.scale_log2, -l4[i]));
-          wA.ds[4 * i4 + i] = pr[4 * i4 + i] * (dp[4 * i4 + i] - t4[i]);
-        }
+        for (int i = 0; i < 4; ++i)
+          wA.pr[4 * i4 + i] = __builtin_amdgcn_exp2f(fmaf(s[4 * i4 + i], c4[i], -l4[i]));
       }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) wA.pa[k >> 2][k & 3] = pack_bf16x2(pr[2 * k], pr[2 * k + 1]);
+      wA.f0 = *(const f32x4*)(lt + 2 * ROWS);
+      wA.t0 = *(const f32x4*)(lt + 3 * ROWS);
     }
 
     // One pipeline step for row block RB of the q-block in buffer BUF (both compile-time).
-    // Phase 1: S, dP of the next block (16 MFMAs) with the hi/lo split of dS(g) between
-    // them.  Phase 2: dV, dK of block g (24 MFMAs: dV from P, dK from dS hi and lo) with
-    // P, dS of the next block and the packing of its P between them.  After the item's last block the "next" block is the
-    // resident other buffer's first block: computed and discarded, so the step has no
-    // branches inside its interleaved parts.
-    auto step = [&](auto rbc, auto bufc, const int e, const Carry& cur, Carry& nxt) {
+    // After the item's last block the "next" block is the resident other buffer's first
+    // block: computed and discarded, so the step has no branches inside its interleaved
+    // parts.
+    auto step = [&](auto rbc, auto bufc, const int e, Carry& cur, Carry& nxt) {
       constexpr int RB = decltype(rbc)::value;
       constexpr int BUF = decltype(bufc)::value;
       constexpr int RB1 = (RB + 1) & 3;
@@ -648,7 +726,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         const int ea = __builtin_amdgcn_readfirstlane(ent_ahead);
         if (more) ent_n = ea;
         prepare_entry(ent_n >> 1, more);
-        ent_ahead = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * (e + 2), 0);
+        ent_ahead = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * ent_index(e + 2), 0);
       }
       const int ent_g1 = RB == 3 ? ent_n : ent_c;  // entry of the next block
       if constexpr (RB == 3) {
@@ -659,9 +737,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
 
-      // ---- phase 1
-      const __bf16* tg = tiles(bufc) + 4096 * RB;     // Q rows of block g (dO: + QTILE)
+      // ---- phase 1: S, dP of the next block; dS of block g, packing of P and dS
+      const __bf16* tg = tiles(bufc) + 4096 * RB;         // Q rows of block g (dO: + QTILE)
       const __bf16* t1 = tiles(IC<BUF1>{}) + 4096 * RB1;  // Q rows of the next block
+      const float* lg = lts(bufc) + 32 * RB + 4 * h2;     // row constants of block g
+      const float* lt = lts(IC<BUF1>{}) + 32 * RB1 + 4 * h2;  // and of the next block
       // operands of the next block's S, dP: four dd steps in flight, dd + 4 read when dd's
       // pair of MFMAs has been issued
       bf16x8 qa[8], da[8];
@@ -676,108 +756,113 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         dt[0][db] = join(lds_read_tr4(tg + QTILE + ofs_t(0, db)), lds_read_tr4(tg + QTILE + ofs_t(1, db)));
         qt[0][db] = join(lds_read_tr4(tg + ofs_t(0, db)), lds_read_tr4(tg + ofs_t(1, db)));
       }
-      f32x16 sn, dpn;
+      f32x16 sn;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sn[i] = dpn[i] = 0.f;
-      uint32_t wsa[2][4], wsl[2][4];
-      float dsv[16];
-      dsv[0] = pin(cur.ds[0]);
-      dsv[1] = pin(cur.ds[1]);
+      for (int i = 0; i < 16; ++i) sn[i] = nxt.dp[i] = 0.f;
+      f32x4 f4[4], t4[4], l4[4], c4[4];
+      f4[0] = cur.f0;
+      t4[0] = cur.t0;
+      float ds[16], prv[2], dpv[2];
+      uint32_t wpa[2][4], wds[2][4];
+      prv[0] = pin(cur.pr[0]);
+      dpv[0] = pin(cur.dp[0]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int dd = x >> 1;
-        if (x & 1) dpn = mfma32x32x16(da[dd], vf[dd], dpn);
-        else sn = mfma32x32x16(qa[dd], kf[dd], sn);
+        if (x & 1) nxt.dp = mfma32x32x16(da[dd], vf[dd], nxt.dp);
+        else sn = mfma32x32x16_f16(qa[dd], kf[dd], sn);
         if ((x & 1) && dd + 4 < 8) {
           qa[dd + 4] = load16(t1 + ofs_a(dd + 4));
           da[dd + 4] = load16(t1 + QTILE + ofs_a(dd + 4));
         }
+        // dS constants of groups 1..3, four slots before their first use; P constants of
+        // the next block's group 0, for phase 2
+        if ((x & 3) == 0 && x < 12) {
+          const int i4 = (x >> 2) + 1;
+          f4[i4] = *(const f32x4*)(lg + 2 * ROWS + 8 * i4);
+          t4[i4] = *(const f32x4*)(lg + 3 * ROWS + 8 * i4);
+        }
+        if (x == 12) {
+          l4[0] = *(const f32x4*)lt;
+          c4[0] = *(const f32x4*)(lt + ROWS);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        // pair q split in step 2q; its inputs are taken one step earlier and its outputs
-        // fenced one step later, so nothing waits on a result in its own step
+        // dS element x; inputs are taken (pin) one slot before and the result fenced
+        // (pin_out) one slot after, so nothing waits on a result in its own slot
+        ds[x] = prv[x & 1] * fmaf(dpv[x & 1], f4[x >> 2][x & 3], -t4[x >> 2][x & 3]);
+        if (x + 1 < 16) {
+          prv[(x + 1) & 1] = pin(cur.pr[x + 1]);
+          dpv[(x + 1) & 1] = pin(cur.dp[x + 1]);
+        }
+        if (x >= 1) pin_out(ds[x - 1]);
+        // P pair x / 2 at even slots (fenced at the next slot); dS pair (x - 3) / 2 at odd
+        // slots from 3 on (its second element was fenced at the slot before)
         if ((x & 1) == 0) {
           const int q = x >> 1;
-          split_pair(dsv[2 * q], dsv[2 * q + 1], wsa[q >> 2][q & 3], wsl[q >> 2][q & 3]);
+          wpa[q >> 2][q & 3] = pack_bf16x2(cur.pr[2 * q], cur.pr[2 * q + 1]);
+        } else {
+          const int q = (x - 1) >> 1;
+          pin_out(wpa[q >> 2][q & 3]);
         }
-        if ((x & 1) && x < 15) {
-          const int q = (x + 1) >> 1;
-          dsv[2 * q] = pin(cur.ds[2 * q]);
-          dsv[2 * q + 1] = pin(cur.ds[2 * q + 1]);
+        if ((x & 1) && x >= 3) {
+          const int q = (x - 3) >> 1;
+          wds[q >> 2][q & 3] = pack_f16x2(ds[2 * q], ds[2 * q + 1]);
         }
-        if (x & 1) {
-          const int q = x >> 1;
-          pin_out(wsa[q >> 2][q & 3]);
-          pin_out(wsl[q >> 2][q & 3]);
+        if ((x & 1) == 0 && x >= 4) {
+          const int q = (x - 4) >> 1;
+          pin_out(wds[q >> 2][q & 3]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      pin_out(ds[15]);
+      pin_out(wds[1][2]);
+      wds[1][3] = pack_f16x2(ds[14], ds[15]);
       if (ent_g1 & 1) mask(sn, RB1, ent_g1 >> 1);
 
-      // ---- phase 2: dV, dK of block g, interleaved with P, dS of the next block
-      const float* lt = lts(IC<BUF1>{}) + 32 * RB1 + 4 * h2;  // LSE; Delta at + ROWS
-      f32x4 l4[4], t4[4];
-      float pr[16];
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) l4[i4] = *(const f32x4*)(lt + 8 * i4);
-      const bf16x8 pa[2] = {as_bf16x8(cur.pa[0]), as_bf16x8(cur.pa[1])};
-      const bf16x8 sa[2] = {as_bf16x8(wsa[0]), as_bf16x8(wsa[1])};
-      const bf16x8 sl[2] = {as_bf16x8(wsl[0]), as_bf16x8(wsl[1])};
-      float snv[2], dpv[2];
+      // ---- phase 2: dV, dK of block g, interleaved with P of the next block
+      const bf16x8 pa[2] = {as_bf16x8(wpa[0]), as_bf16x8(wpa[1])};
+      const bf16x8 sa[2] = {as_bf16x8(wds[0]), as_bf16x8(wds[1])};
+      float snv[2];
       snv[0] = pin(sn[0]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int x = 0; x < 24; ++x) {
-        // MFMA x: half hf = x / 12; k = x % 12: dV (k even < 8) and dK hi (k odd < 8) for
-        // db = k / 2, then dK lo for db = k - 8
-        const int hf = x / 12, k = x % 12;
-        if (k < 8) {
-          const int db = k >> 1;
-          if (k & 1) accK[db] = mfma32x32x16(sa[hf], qt[hf][db], accK[db]);
-          else accV[db] = mfma32x32x16(pa[hf], dt[hf][db], accV[db]);
-        } else {
-          const int db = k - 8;
-          accK[db] = mfma32x32x16(sl[hf], qt[hf][db], accK[db]);
-        }
+      for (int x = 0; x < 16; ++x) {
+        // MFMA x: half hf = x / 8; dV (x even) and dK (x odd) for db = (x % 8) / 2
+        const int hf = x >> 3, db = (x & 7) >> 1;
+        if (x & 1) accK[db] = mfma32x32x16_f16(sa[hf], qt[hf][db], accK[db]);
+        else accV[db] = mfma32x32x16(pa[hf], dt[hf][db], accV[db]);
         // transposed operands of half 1, each read right after its half-0 register is last
-        // used: dO^T (db) after MFMA 2 db, read at 2 db + 1; Q^T (db) after MFMA 8 + db,
-        // read at 9 + db (used from MFMA 12 + 2 db and 13 + 2 db on)
-        if (x == 1 || x == 3 || x == 5 || x == 7) {
-          const int db1 = (x - 1) >> 1;
+        // used: dO^T (db) after MFMA 2 db, read at 2 db + 1; Q^T (db) after MFMA 2 db + 1,
+        // read at 2 db + 2
+        if (x < 8 && (x & 1)) {
+          const int db1 = x >> 1;
           dt[1][db1] = join(lds_read_tr4(tg + 2048 + QTILE + ofs_t(0, db1)), lds_read_tr4(tg + 2048 + QTILE + ofs_t(1, db1)));
         }
-        if (x >= 9 && x <= 12) {
-          const int db1 = x - 9;
+        if (x >= 2 && x <= 8 && (x & 1) == 0) {
+          const int db1 = (x - 2) >> 1;
           qt[1][db1] = join(lds_read_tr4(tg + 2048 + ofs_t(0, db1)), lds_read_tr4(tg + 2048 + ofs_t(1, db1)));
         }
         // copies of the next q-block: 8 in each of the first two steps, one every 2 MFMAs
         if constexpr (RB < 2)
-          if (x >= 9 && (x & 1)) copy(8 * RB + ((x - 9) >> 1), IC<BUF ^ 1>{});
+          if (x & 1) copy(8 * RB + (x >> 1), IC<BUF ^ 1>{});
+        // P constants of groups 1..3, four slots ahead; the next step's first dS constants
+        if ((x & 3) == 0 && x < 12) {
+          const int i4 = (x >> 2) + 1;
+          l4[i4] = *(const f32x4*)(lt + 8 * i4);
+          c4[i4] = *(const f32x4*)(lt + ROWS + 8 * i4);
+        }
+        if (x == 12) {
+          nxt.f0 = *(const f32x4*)(lt + 2 * ROWS);
+          nxt.t0 = *(const f32x4*)(lt + 3 * ROWS);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        // P (exp) in steps 0..15, dS 4 steps behind, the packing of P pair q in step 16 + q.
-        // Inputs are taken (pin) one step before use and results fenced (pin_out) one step
-        // after they are made: each piece stays in its slot without stalling on itself.
-        if (x < 16) pr[x] = __builtin_amdgcn_exp2f(fmaf(snv[x & 1], a.scale_log2, -l4[x >> 2][x & 3]));
+        nxt.pr[x] = __builtin_amdgcn_exp2f(fmaf(snv[x & 1], c4[x >> 2][x & 3], -l4[x >> 2][x & 3]));
         if (x + 1 < 16) snv[(x + 1) & 1] = pin(sn[x + 1]);
-        if (x >= 1 && x <= 16) pin_out(pr[x - 1]);
-        if ((x & 3) == 0 && x < 16) t4[x >> 2] = *(const f32x4*)(lt + ROWS + 2 * x);
-        if (x >= 4 && x < 20) {
-          const int i = x - 4;
-          nxt.ds[i] = pr[i] * (dpv[i & 1] - t4[i >> 2][i & 3]);
-        }
-        if (x >= 3 && x < 19) dpv[(x - 3) & 1] = pin(dpn[x - 3]);
-        if (x >= 5 && x <= 20) pin_out(nxt.ds[x - 5]);
-        if (x >= 16) {
-          const int q = x - 16;
-          nxt.pa[q >> 2][q & 3] = pack_bf16x2(pr[2 * q], pr[2 * q + 1]);
-        }
-        if (x >= 17) {
-          const int q = x - 17;
-          pin_out(nxt.pa[q >> 2][q & 3]);
-        }
+        if (x >= 1) pin_out(nxt.pr[x - 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      pin_out(nxt.pa[1][3]);
+      pin_out(nxt.pr[15]);
       if constexpr (RB == 3) ent_c = ent_n;
     };
     auto entry = [&](auto bufc, const int e) {

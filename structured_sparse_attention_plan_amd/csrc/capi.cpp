@@ -142,9 +142,11 @@ extern "C" int cowa_workspace_size(int op, const cowa_problem* p, size_t* bytes)
     case COWA_OP_FWD:
       *bytes = 0;
       break;
-    case COWA_OP_BWD:
-      *bytes = (size_t)p->B * p->Hq * p->Lq * sizeof(float);
+    case COWA_OP_BWD: {  // Delta, the row scales of Q and the fp16 copy of Q
+      const size_t rows = (size_t)p->B * p->Hq * p->Lq;
+      *bytes = 2 * ((rows * sizeof(float) + 255) / 256 * 256) + rows * p->D * 2;
       break;
+    }
     default: {
       const size_t rows = (size_t)p->B * p->Hq * decode_splits(p);
       const size_t part = (rows * p->D * sizeof(float) + 255) / 256 * 256;
@@ -222,8 +224,10 @@ extern "C" int cowa_bwd(const cowa_problem* p, const cowa_plan_dev* plan, const 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  const size_t row_bytes = ((size_t)p->B * p->Hq * p->Lq * sizeof(float) + 255) / 256 * 256;
   a.delta = (float*)workspace;
-  a.dq_acc = nullptr;
+  a.qscale = (float*)((char*)workspace + row_bytes);
+  a.q16 = (char*)workspace + 2 * row_bytes;
   a.row_ptr = plan->row_ptr;
   a.row_ent = plan->row_ent;
   a.row_order = plan->row_order;

@@ -42,6 +42,28 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The fp16 product of the same shape and lane layout; a and b are 16-bit containers
+// that hold fp16 bit patterns (LDS reads and packed registers share one type).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                c, 0, 0, 0);
+}
+
+// (x0, x1) -> packed fp16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float x0, float x1) {
+  const f16x2 h = {(_Float16)x0, (_Float16)x1};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// floor(log2 |x|) of a normal fp32 x (x >= 0 here, the max of absolute values); 0 for
+// zero and subnormals.  Dividing by 2^e then puts x in [1, 2).
+__device__ __forceinline__ int pow2_exponent(float x) {
+  const int eb = (int)((__float_as_uint(x) >> 23) & 255u);
+  return eb == 0 ? 0 : eb - 127;
+}
+
 // Transposed LDS load (see the header comment).  `p` points into __shared__ memory.
 __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
   const lds_i16x4* lp = (const lds_i16x4*)(__attribute__((address_space(3))) const void*)(p);

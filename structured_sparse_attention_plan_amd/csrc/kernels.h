@@ -42,8 +42,9 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;   // workspace [B, Hq, Lq]
-  float* dq_acc;  // workspace [B, Lq, Hq, D] fp32 (may be unused by a variant)
+  float* delta;   // workspace [B, Hq, Lq]: Delta = dO . O per row
+  float* qscale;  // workspace [B, Hq, Lq]: 2^e with max |q| / 2^e in [1, 2) per row
+  void* q16;      // workspace [B, Lq, Hq, D] fp16: q / qscale per row
   const int32_t* row_ptr;
   const int32_t* row_ent;
   const int32_t* row_order;

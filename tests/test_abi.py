@@ -46,7 +46,8 @@ def test_tile_sizes_and_workspace():
     assert api.tile_sizes("fwd", p) == (256 // 5, 64)
     assert api.tile_sizes("bwd", p) == (128 // 5, 128)
     assert api.workspace_size("fwd", p) == 0
-    assert api.workspace_size("bwd", p) == 40 * 256 * 4
+    # Delta and the row scales of Q (fp32 each), then the fp16 copy of Q
+    assert api.workspace_size("bwd", p) == 2 * 40 * 256 * 4 + 256 * 40 * 128 * 2
     pd = _prob(Lq=1, Lk=4096)
     assert api.tile_sizes("decode", pd) == (1, 64)
     assert api.workspace_size("decode", pd) > 0
@@ -101,7 +102,7 @@ def test_entry_points_validate_before_launch():
     assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, x, x, x, x, x, 7, x, 16,
                           None) == C.COWA_ERR_WORKSPACE_TOO_SMALL
     assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, x, x, x, x, x, 7,
-                          ctypes.c_void_p(260), 1 << 20, None) == C.COWA_ERR_INVALID_ARG
+                          ctypes.c_void_p(260), 1 << 23, None) == C.COWA_ERR_INVALID_ARG
     for bad_stages in (0, 8):
         assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, x, x, x, x, x,
                               bad_stages, ctypes.c_void_p(256), 1 << 20,
