@@ -430,6 +430,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// S and dP products with the accumulator in VGPRs (the VALU reads each element as soon as
+// it is final, without an AGPR read) and the B operand (K or V of the lane's key) in
+// AGPRs; the "0" forms start from a zero accumulator.  The output is early-clobber: it
+// must not share registers with the operands.
+__device__ __forceinline__ void mfma_f16_va(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_f16_va0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_bf16_va(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_bf16_va0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+
 // bf16 x -> fp16 bits of x / 2^e (exact while |x| / 2^e is in the fp16 normal range).
 __device__ __forceinline__ bf16x8 bf16_to_f16_scaled(const bf16x8& x, int e) {
   const u32x4 w = __builtin_bit_cast(u32x4, x);
@@ -719,6 +736,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       // taken afresh each step, so the per-read XORs stay in the step instead of being
       // hoisted into 16 long-lived registers
       asm volatile("" : "+v"(ofs_a0), "+v"(ofs_t0[0]), "+v"(ofs_t0[1]));
+      // the dK, dV accumulators stay in AGPRs across steps (else the allocator parks them
+      // in VGPRs over part of the loop and copies them back and forth)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) asm volatile("" : "+a"(accK[db]), "+a"(accV[db]));
       if constexpr (RB == 0) {
         // every wave is done with q-block e - 1: its buffer takes q-block e + 1, copied
         // during the phase-2 MFMAs of this step and the next
@@ -757,8 +778,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         qt[0][db] = join(lds_read_tr4(tg + ofs_t(0, db)), lds_read_tr4(tg + ofs_t(1, db)));
       }
       f32x16 sn;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sn[i] = nxt.dp[i] = 0.f;
       f32x4 f4[4], t4[4], l4[4], c4[4];
       f4[0] = cur.f0;
       t4[0] = cur.t0;
@@ -770,8 +789,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int dd = x >> 1;
-        if (x & 1) nxt.dp = mfma32x32x16(da[dd], vf[dd], nxt.dp);
-        else sn = mfma32x32x16_f16(qa[dd], kf[dd], sn);
+        if (x == 0) mfma_f16_va0(sn, qa[0], kf[0]);
+        else if (x == 1) mfma_bf16_va0(nxt.dp, da[0], vf[0]);
+        else if (x & 1) mfma_bf16_va(nxt.dp, da[dd], vf[dd]);
+        else mfma_f16_va(sn, qa[dd], kf[dd]);
         if ((x & 1) && dd + 4 < 8) {
           qa[dd + 4] = load16(t1 + ofs_a(dd + 4));
           da[dd + 4] = load16(t1 + QTILE + ofs_a(dd + 4));
@@ -796,11 +817,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           dpv[(x + 1) & 1] = pin(cur.dp[x + 1]);
         }
         if (x >= 1) pin_out(ds[x - 1]);
-        // P pair x / 2 at even slots (fenced at the next slot); dS pair (x - 3) / 2 at odd
-        // slots from 3 on (its second element was fenced at the slot before)
+        // P pair x / 2 at even slots, from the two pinned values (fenced at the next slot);
+        // dS pair (x - 3) / 2 at odd slots from 3 on (its second element was fenced at the
+        // slot before)
         if ((x & 1) == 0) {
           const int q = x >> 1;
-          wpa[q >> 2][q & 3] = pack_bf16x2(cur.pr[2 * q], cur.pr[2 * q + 1]);
+          wpa[q >> 2][q & 3] = pack_bf16x2(prv[0], prv[1]);
         } else {
           const int q = (x - 1) >> 1;
           pin_out(wpa[q >> 2][q & 3]);
