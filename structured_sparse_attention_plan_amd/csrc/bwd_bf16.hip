@@ -482,7 +482,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: copy targets form on the SALU
   const int n = lane & 31;
   const int h2 = lane >> 5;
   const int item = load_uniform(a.col_order, blockIdx.x);
@@ -733,9 +733,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       constexpr int RB1 = (RB + 1) & 3;
       constexpr int BUF1 = RB == 3 ? BUF ^ 1 : BUF;
       const bool more = e + 1 < n_ent;  // a next q-block exists
-      // taken afresh each step, so the per-read XORs stay in the step instead of being
-      // hoisted into 16 long-lived registers
-      asm volatile("" : "+v"(ofs_a0), "+v"(ofs_t0[0]), "+v"(ofs_t0[1]));
       // the dK, dV accumulators stay in AGPRs across steps (else the allocator parks them
       // in VGPRs over part of the loop and copies them back and forth)
 #pragma unroll
@@ -809,6 +806,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           c4[0] = *(const f32x4*)(lt + ROWS);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // P pair q at slot 2 q + 1, from the two pinned values (fenced at the next slot),
+        // ahead of the slot's dS
+        if (x & 1) {
+          const int q = x >> 1;
+          wpa[q >> 2][q & 3] = pack_bf16x2(prv[0], prv[1]);
+        } else if (x >= 2) {
+          const int q = (x - 2) >> 1;
+          pin_out(wpa[q >> 2][q & 3]);
+        }
         // dS element x; inputs are taken (pin) one slot before and the result fenced
         // (pin_out) one slot after, so nothing waits on a result in its own slot
         ds[x] = prv[x & 1] * fmaf(dpv[x & 1], f4[x >> 2][x & 3], -t4[x >> 2][x & 3]);
@@ -817,28 +823,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           dpv[(x + 1) & 1] = pin(cur.dp[x + 1]);
         }
         if (x >= 1) pin_out(ds[x - 1]);
-        // P pair x / 2 at even slots, from the two pinned values (fenced at the next slot);
-        // dS pair (x - 3) / 2 at odd slots from 3 on (its second element was fenced at the
-        // slot before)
-        if ((x & 1) == 0) {
-          const int q = x >> 1;
-          wpa[q >> 2][q & 3] = pack_bf16x2(prv[0], prv[1]);
-        } else {
-          const int q = (x - 1) >> 1;
-          pin_out(wpa[q >> 2][q & 3]);
+        // dS pair q at slot 2 q + 2, right after its second element is fenced (fenced in
+        // turn at the next slot)
+        if ((x & 1) == 0 && x >= 2) {
+          const int q = (x - 2) >> 1;
+          wds[q >> 2][q & 3] = pack_f16x2(ds[2 * q], ds[2 * q + 1]);
         }
         if ((x & 1) && x >= 3) {
           const int q = (x - 3) >> 1;
-          wds[q >> 2][q & 3] = pack_f16x2(ds[2 * q], ds[2 * q + 1]);
-        }
-        if ((x & 1) == 0 && x >= 4) {
-          const int q = (x - 4) >> 1;
           pin_out(wds[q >> 2][q & 3]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       pin_out(ds[15]);
-      pin_out(wds[1][2]);
+      pin_out(wpa[1][3]);
       wds[1][3] = pack_f16x2(ds[14], ds[15]);
       if (ent_g1 & 1) mask(sn, RB1, ent_g1 >> 1);
 
