@@ -93,6 +93,23 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
 template <int V>
 using IC = std::integral_constant<int, V>;
 
+// S and dP products with the accumulator in VGPRs (the VALU reads each element as soon as
+// it is final, without an AGPR read) and the B operand (K or V of the lane's key) in
+// AGPRs; the "0" forms start from a zero accumulator.  The output is early-clobber: it
+// must not share registers with the operands.
+__device__ __forceinline__ void mfma_f16_va(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_f16_va0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_bf16_va(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_bf16_va0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+
 // ------------------------------------------------------------------------ dQ
 // One work item = (KV head, q-block of 128 rows), 4 waves x 32 rows; each lane owns one
 // query row (column of the transposed products) and keeps its Q and dO fragments in
@@ -128,7 +145,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: copy targets form on the SALU
   const int n = lane & 31;
   const int h2 = lane >> 5;
   const int item = load_uniform(a.row_order, blockIdx.x);
@@ -180,6 +197,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) qf[dd] = df[dd] = zero_bf16x8();
   }
+  // held in AGPRs as the B operands of the S, dP products: the VGPRs hold those products'
+  // accumulators
+#pragma unroll
+  for (int dd = 0; dd < 8; ++dd) asm volatile("" : "+a"(qf[dd]), "+a"(df[dd]));
   if (lse2 == -INFINITY) lse2 = INFINITY;  // a row with no visible key has P = 0
 
   f32x16 acc[4];
@@ -264,12 +285,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     f32x16 sA[2], dA[2], sB[2], dB[2];  // S^T, dP^T of two consecutive tiles (2 key blocks)
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
+      mfma_bf16_va0(sA[k2], load16(sK0 + ofs_a(k2, 0)), qf[0]);
+      mfma_bf16_va0(dA[k2], load16(sV0 + ofs_a(k2, 0)), df[0]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sA[k2][i] = dA[k2][i] = 0.f;
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        sA[k2] = mfma32x32x16(load16(sK0 + ofs_a(k2, dd)), qf[dd], sA[k2]);
-        dA[k2] = mfma32x32x16(load16(sV0 + ofs_a(k2, dd)), df[dd], dA[k2]);
+      for (int dd = 1; dd < 8; ++dd) {
+        mfma_bf16_va(sA[k2], load16(sK0 + ofs_a(k2, dd)), qf[dd]);
+        mfma_bf16_va(dA[k2], load16(sV0 + ofs_a(k2, dd)), df[dd]);
       }
     }
     uint32_t dsp[2][2][4];  // packed dS^T of the previous tile: [k2][hf] bf16x8 as 4 words
@@ -294,10 +315,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
       const __bf16* kq = kbuf(IC<(TC + 3) & 3>{});  // K of tile tt - 1 (dQ)
       const __bf16* kn = kbuf(IC<(TC + 1) & 3>{});  // K of tile tt + 1 (S)
       const __bf16* vn = vbuf(IC<(TC + 1) & 1>{});  // V of tile tt + 1 (dP)
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ns[k2][i] = nd[k2][i] = 0.f;
       float pr[2][16], dsv[2][16];
       uint32_t npk[2][2][4];
       // operands: transposed K of tile tt - 1 for the first 16 MFMAs, K / V rows of tile
@@ -323,9 +340,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
           const u32x4 w = {dsp[k2][hf][0], dsp[k2][hf][1], dsp[k2][hf][2], dsp[k2][hf][3]};
           acc[db] = mfma32x32x16(opA[x], __builtin_bit_cast(bf16x8, w), acc[db]);
         } else {
+          // accumulators in VGPRs, each chain starting from zero (dd = 0)
           const int y = x - 16, k2 = y & 1, dd = y >> 2;
-          if ((y >> 1) & 1) nd[k2] = mfma32x32x16(opA[x], df[dd], nd[k2]);
-          else ns[k2] = mfma32x32x16(opA[x], qf[dd], ns[k2]);
+          if ((y >> 1) & 1) {
+            if (dd == 0) mfma_bf16_va0(nd[k2], opA[x], df[0]);
+            else mfma_bf16_va(nd[k2], opA[x], df[dd]);
+          } else {
+            if (dd == 0) mfma_bf16_va0(ns[k2], opA[x], qf[0]);
+            else mfma_bf16_va(ns[k2], opA[x], qf[dd]);
+          }
         }
         if (x >= 4 && x < 12) copy(x - 4, kd, vd);
         __builtin_amdgcn_sched_barrier(0);
@@ -428,23 +451,6 @@ constexpr int QTILE = ROWS * D;  // one q-block of Q (or dO) in LDS
 __device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
   const bf16x2 h = {(__bf16)x0, (__bf16)x1};
   return __builtin_bit_cast(uint32_t, h);
-}
-
-// S and dP products with the accumulator in VGPRs (the VALU reads each element as soon as
-// it is final, without an AGPR read) and the B operand (K or V of the lane's key) in
-// AGPRs; the "0" forms start from a zero accumulator.  The output is early-clobber: it
-// must not share registers with the operands.
-__device__ __forceinline__ void mfma_f16_va(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma_f16_va0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma_bf16_va(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma_bf16_va0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
 }
 
 // bf16 x -> fp16 bits of x / 2^e (exact while |x| / 2^e is in the fp16 normal range).
