@@ -706,6 +706,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();
 
     Carry wA, wB;
+    // Q and dO operands (dd = 0, 1) of the S, dP products a step issues first, read during
+    // the previous step's phase 2 so that its first MFMAs do not wait for LDS (possible
+    // whenever those rows are resident then: not for the step that follows row block 2,
+    // whose rows come from the q-block still being copied)
+    bf16x8 pfq[2], pfd[2];
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd) {
+      pfq[dd] = load16(sQD0 + 4096 + ofs_a(dd));
+      pfd[dd] = load16(sQD0 + 4096 + QTILE + ofs_a(dd));
+    }
     {  // prologue: S, dP and P of block 0
       f32x16 s;
 #pragma unroll
@@ -771,8 +781,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       bf16x8 qa[8], da[8];
 #pragma unroll
       for (int dd = 0; dd < 4; ++dd) {
-        qa[dd] = load16(t1 + ofs_a(dd));
-        da[dd] = load16(t1 + QTILE + ofs_a(dd));
+        if (RB != 3 && dd < 2) {
+          qa[dd] = pfq[dd];
+          da[dd] = pfd[dd];
+        } else {
+          qa[dd] = load16(t1 + ofs_a(dd));
+          da[dd] = load16(t1 + QTILE + ofs_a(dd));
+        }
       }
       bf16x8 dt[2][4], qt[2][4];
 #pragma unroll
@@ -881,6 +896,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         if (x == 12) {
           nxt.f0 = *(const f32x4*)(lt + 2 * ROWS);
           nxt.t0 = *(const f32x4*)(lt + 3 * ROWS);
+        }
+        // the next step's first operands (rows of block g + 2)
+        if constexpr (RB != 2) {
+          constexpr int RBn = (RB + 1) & 3, BUFn = RB == 3 ? BUF ^ 1 : BUF;
+          constexpr int RB1n = (RBn + 1) & 3, BUF1n = RBn == 3 ? BUFn ^ 1 : BUFn;
+          const __bf16* t1n = tiles(IC<BUF1n>{}) + 4096 * RB1n;
+          if (x == 13 || x == 14) {
+            const int dd = x - 13;
+            pfq[dd] = load16(t1n + ofs_a(dd));
+            pfd[dd] = load16(t1n + QTILE + ofs_a(dd));
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         nxt.pr[x] = __builtin_amdgcn_exp2f(fmaf(snv[x & 1], c4[x >> 2][x & 3], -l4[x >> 2][x & 3]));
