@@ -318,7 +318,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
       float pr[2][16], dsv[2][16];
       uint32_t npk[2][2][4];
       // operands: transposed K of tile tt - 1 for the first 16 MFMAs, K / V rows of tile
-      // tt + 1 for the other 32, each read two MFMAs ahead
+      // tt + 1 for the other 32, each read kLead MFMAs ahead
+      constexpr int kLead = 4;
       bf16x8 opA[48];
       auto load_op = [&](int x) {
         if (x < 16) {
@@ -329,12 +330,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
           opA[x] = load16((((y >> 1) & 1) ? vn : kn) + ofs_a(k2, dd));
         }
       };
-      load_op(0);
-      load_op(1);
+#pragma unroll
+      for (int x = 0; x < kLead; ++x) load_op(x);
+      float csv[2], cdv[2];  // S, dP elements taken one step before use
+      csv[0] = pin(cs[0][0]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int x = 0; x < 48; ++x) {
-        if (x + 2 < 48) load_op(x + 2);
+        if (x + kLead < 48) load_op(x + kLead);
         if (x < 16) {
           const int k2 = x >> 3, hf = (x >> 2) & 1, db = x & 3;
           const u32x4 w = {dsp[k2][hf][0], dsp[k2][hf][1], dsp[k2][hf][2], dsp[k2][hf][3]};
@@ -352,25 +355,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
         }
         if (x >= 4 && x < 12) copy(x - 4, kd, vd);
         __builtin_amdgcn_sched_barrier(0);
-        // VALU of tile tt: element e = x (0..31) gets P in step x, dS in step x + 4;
-        // pairs are packed to bf16 in steps 38..47 (two pairs per step from 40)
-        if (x < 32) {
-          const int k2 = x >> 4, i = x & 15;
-          pr[k2][i] = __builtin_amdgcn_exp2f(fmaf(pin(cs[k2][i]), a.scale_log2, -lse2));
-          pin_out(pr[k2][i]);
-        }
+        // VALU of tile tt: element e = x (0..31) gets P in step x, dS in step x + 4; pairs
+        // are packed to bf16 in steps 32..47.  Inputs are taken (pin) one step before use
+        // and results fenced (pin_out) one step after they are made: a read right at a pin
+        // or a fence right after an exp costs a wait state each.
+        if (x < 32) pr[x >> 4][x & 15] = __builtin_amdgcn_exp2f(fmaf(csv[x & 1], a.scale_log2, -lse2));
+        if (x + 1 < 32) csv[(x + 1) & 1] = pin(cs[(x + 1) >> 4][(x + 1) & 15]);
+        if (x >= 1 && x <= 32) pin_out(pr[(x - 1) >> 4][(x - 1) & 15]);
         if (x >= 4 && x < 36) {
           const int e = x - 4, k2 = e >> 4, i = e & 15;
-          dsv[k2][i] = pr[k2][i] * (pin(cd[k2][i]) - dlt);
-          pin_out(dsv[k2][i]);
+          dsv[k2][i] = pr[k2][i] * (cdv[e & 1] - dlt);
         }
-        if (x >= 32) {
-          const int q = x - 32;  // pair q of 16: k2 = q / 8, hf = (q / 4) % 2, word q % 4
-          const int k2 = q >> 3, hf = (q >> 2) & 1, w = q & 3;
-          const float x0 = dsv[k2][8 * hf + 2 * w], x1 = dsv[k2][8 * hf + 2 * w + 1];
+        if (x >= 3 && x < 35) {
+          const int e = x - 3;
+          cdv[e & 1] = pin(cd[e >> 4][e & 15]);
+        }
+        if (x >= 5 && x <= 36) pin_out(dsv[(x - 5) >> 4][(x - 5) & 15]);
+        // dS pair q (elements 2 q, 2 q + 1) packed to bf16 at step 2 q + 6, right after its
+        // second element is fenced, and fenced in turn a step later; pair q sits in word
+        // q % 4 of half (q / 4) % 2 of block q / 8
+        if (x >= 6 && x <= 36 && (x & 1) == 0) {
+          const int q = (x - 6) >> 1, k2 = q >> 3, hf = (q >> 2) & 1, w = q & 3;
+          const float x0 = dsv[k2][2 * (q & 7)], x1 = dsv[k2][2 * (q & 7) + 1];
           const bf16x2 v = {(__bf16)x0, (__bf16)x1};
           npk[k2][hf][w] = __builtin_bit_cast(uint32_t, v);
-          pin_out(npk[k2][hf][w]);
+        }
+        if (x >= 7 && x <= 37 && (x & 1)) {
+          const int q = (x - 7) >> 1;
+          pin_out(npk[q >> 3][(q >> 2) & 1][q & 3]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
