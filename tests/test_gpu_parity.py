@@ -128,6 +128,52 @@ def test_bwd_bf16_mid_2048_full():
     assert_bf16_close("dV", dv, rv, value_scaled=True)
 
 
+@pytest.mark.parametrize("B,Lq,Lk,Hq,Hkv,sink,near,mode", [
+    (1, 300, 1100, 40, 8, 20, 90, "complementary"),   # prefill chunk: rows at the end of Lk
+    (2, 130, 700, 40, 8, 7, 64, "duplicated"),
+])
+def test_bwd_bf16_prefill_chunk(B, Lq, Lk, Hq, Hkv, sink, near, mode):
+    """Backward of a chunk of Lq query rows at positions Lk - Lq .. Lk - 1 (bottom-right
+    distance d = i + Lk - Lq - j)."""
+    _case(f"bwd bf16 B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} sink={sink} near={near} {mode}")
+    ow, win = _windows(Lk, Hkv, sink, near, mode=mode)
+    q, k, v, do = inputs.attention_inputs(B, Lq, Lk, Hq, Hkv, 128, seed=8, with_dout=True)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = api.fwd(qd, kd, vd, win)
+    dq, dk, dv = api.bwd(qd, kd, vd, o, lse, dod, win)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attn_bwd(q, k, v, do, ow, 128 ** -0.5)
+    assert_bf16_close("dQ", dq, rq, value_scaled=True)
+    assert_bf16_close("dK", dk, rk, value_scaled=True)
+    assert_bf16_close("dV", dv, rv, value_scaled=True)
+
+
+def test_chunked_prefill_matches_full_forward():
+    """Chunked prefill: the forward of rows [c0, c1) against keys [0, c1) (Lq < Lk, the
+    same window) equals rows c0..c1-1 of the forward over the whole sequence, bit for bit.
+    Each row's result depends only on its own visible keys taken in ascending tile order,
+    and with sink >= 1 every row's first tile (keys 0..63) is visible to it, so the
+    softmax reference is the same however rows are grouped into q-blocks.  The decode of
+    each chunk's last token then agrees with the full forward's row within bf16."""
+    L = 2000
+    _case(f"chunked prefill L={L} chunks 0-700-1300-2000 + decode at each chunk end")
+    _, win = _windows(L, 8, 32, 256)
+    q, k, v = (t.to(DEV) for t in inputs.attention_inputs(1, L, L, 40, 8, 128, seed=9))
+    o, lse = api.fwd(q, k, v, win)
+    for c0, c1 in ((0, 700), (700, 1300), (1300, 2000)):
+        oc, lsec = api.fwd(q[:, c0:c1].contiguous(), k[:, :c1].contiguous(), v[:, :c1].contiguous(), win)
+        od, lsed = api.decode(q[:, c1 - 1:c1].contiguous(), k[:, :c1].contiguous(), v[:, :c1].contiguous(), win)
+        torch.cuda.synchronize()
+        n_o = int((oc != o[:, c0:c1]).sum().item())
+        n_l = int((lsec != lse[:, :, c0:c1]).sum().item())
+        d = (od.float() - o[:, c1 - 1:c1].float()).abs().max().item()
+        dl = (lsed - lse[:, :, c1 - 1]).abs().max().item()
+        print(f"  chunk [{c0}, {c1}): O differs at {n_o}, LSE at {n_l}; decode max|dO|={d:.3e} "
+              f"max|dLSE|={dl:.3e}", flush=True)
+        assert n_o == 0 and n_l == 0
+        assert d <= 1e-2 and dl <= 1e-3
+
+
 # ----------------------------------------------------------------------------- decode
 
 @pytest.mark.parametrize("B,Lk,Hq,Hkv,sink,near,mode", [
