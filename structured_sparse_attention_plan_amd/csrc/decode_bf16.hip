@@ -11,8 +11,8 @@
 // the head's visible blocks.  Inside the group, 16 slots of 16 lanes each take one key
 // at a time; a lane holds 8 of the 128 dims (16-byte loads, so a slot reads one 256-byte
 // K or V row), and the G query heads of the KV head share every K/V read.  Scores are
-// reduced across the 16 lanes of a slot; the online softmax runs per slot, four keys at
-// a time.  The 16 slots are merged through LDS into one partial (max, sum, o[128]) per
+// reduced across the 16 lanes of a slot with DPP moves; the online softmax runs per slot,
+// four keys at a time.  The 16 slots are merged through LDS into one partial (max, sum, o[128]) per
 // query head and split; a second kernel merges the splits (log-sum-exp) into O and LSE.
 
 #include "device_common.h"
@@ -30,6 +30,23 @@ __device__ __forceinline__ void unpack8(const u32x4& w, float* x) {
     x[2 * k] = __uint_as_float(w[k] << 16);
     x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
   }
+}
+
+// Sum over the 16 lanes of a row (lanes 16 r .. 16 r + 15), left in every lane of the
+// row, with DPP moves (no LDS): pairs by quad permutes (lane ^ 1, lane ^ 2), then the
+// half-row mirror pairs the two quads of each 8 lanes and the row mirror the two halves.
+// Each step adds the same two values in both lanes of a pair, so all 16 lanes end with
+// the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_pair(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float sum16(float x) {
+  x = dpp_pair<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x = dpp_pair<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x = dpp_pair<0x141>(x);  // row_half_mirror
+  x = dpp_pair<0x140>(x);  // row_mirror
+  return x;
 }
 
 template <int G>
@@ -96,10 +113,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         float acc = 0.f;
 #pragma unroll
         for (int x = 0; x < 8; ++x) acc = fmaf(q[gi][x], kx[x], acc);
-        acc += __shfl_xor(acc, 1, 16);
-        acc += __shfl_xor(acc, 2, 16);
-        acc += __shfl_xor(acc, 4, 16);
-        acc += __shfl_xor(acc, 8, 16);
+        acc = sum16(acc);
         s[rr][gi] = ok[rr] ? acc * a.scale_log2 : -INFINITY;
       }
     }
