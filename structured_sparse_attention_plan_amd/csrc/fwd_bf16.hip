@@ -200,14 +200,20 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     const int r = 16 * wave + 4 * u + lrow;
     voff[u] = 2u * (uint32_t)(r * HkvD + h * D + 8 * (lchunk ^ sw(r)));
   }
-  // The batch's base and byte count are formed once per item; per tile only the offset
-  // remains on the scalar unit.
+  // The batch's base is formed once per item; per tile only the offset and the tile's
+  // row count remain on the scalar unit.
   const int tile_bytes = BK * HkvD * 2;
-  const int64_t kv_bytes = (int64_t)a.Lk * HkvD * 2;
   const char* const kbase = (const char*)(K + (int64_t)b * a.Lk * HkvD);
   const char* const vbase = (const char*)(V + (int64_t)b * a.Lk * HkvD);
+  // resource over the BK rows of tile ent (fewer at the end of the sequence, none when
+  // !real): the copies only read inside their tile, so the range needs no 64-bit
+  // arithmetic beyond the tile's base
+  const int row_bytes = HkvD * 2;
   auto tile_copy_rsrc = [&](const char* base, int ent, bool real) __attribute__((always_inline)) {
-    return tile_rsrc(base, kv_bytes, (int64_t)(ent >> 1) * tile_bytes, real);
+    const int kb = ent >> 1;
+    const int rows = min(a.Lk - kb * BK, BK);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kb * tile_bytes), (short)0,
+                                             real ? rows * row_bytes : 0, 0x00020000);
   };
   auto copy_tile = [&](__amdgpu_buffer_rsrc_t r, int u, __bf16* dst) __attribute__((always_inline)) {
     buf2lds(r, voff[u], dst + (16 * wave + 4 * u) * D);
