@@ -217,8 +217,8 @@ def _events_ms(fn, steps, warmup):
 def extras(seed, main_fb_ms, main_fwd_ms, main_bwd_ms, main_dec_ms, main_E, main_dec_bytes):
     """Secondary workloads timed with the same kernels: the 32K forward, the 32K coverage
     ablation (complementary / duplicated / dense bands, forward + backward), dense causal
-    attention at 128K (forward + backward and decode) for the CoWA-vs-dense ratios, and the
-    fp32 1K forward."""
+    attention at 128K (forward + backward and decode) for the CoWA-vs-dense ratios, a
+    variable-length decode over the 128K caches, and the fp32 1K forward."""
     import torch
     from structured_sparse_attention_plan_amd import api, inputs
     from structured_sparse_attention_plan_amd import _cowa as C
@@ -279,6 +279,22 @@ def extras(seed, main_fb_ms, main_fwd_ms, main_bwd_ms, main_dec_ms, main_E, main
         lambda: api.decode(qd, kc, vc, win_d, D ** -0.5, plan=plan_dd, out=od, lse=lsed, workspace=wsd),
         10, 3)
     dense_dec_bytes = plan_dd.info.edges * DEC_B * 2 * D * 2
+    # variable-length decode: the same 16 caches of 131072 positions, sequence b of length
+    # 65536 + 4096 b (query at its last position), CoWA window of the capacity, no plan
+    win_c = api.make_window(L, HKV, SINK, NEAR)
+    lens = [65536 + 4096 * b for b in range(DEC_B)]
+    seq = torch.tensor(lens, dtype=torch.int32, device=dev)
+    var_us = 1e3 * _events_ms(
+        lambda: api.decode_varlen(qd, kc, vc, seq, win_c, D ** -0.5, out=od, lse=lsed, workspace=wsd),
+        10, 3)
+    var_bytes = sum(api.plan_info(1, n, HKV, 1, 64, win_c).edges for n in lens) * 2 * D * 2
+    out["decode_varlen_16x64k_128k"] = {
+        "lengths": f"65536 + 4096 b, b = 0..{DEC_B - 1}", "capacity": L,
+        "us_per_step": var_us, "visible_kv_bytes": var_bytes,
+        "gbps": var_bytes / (var_us * 1e-6) / 1e9,
+        "hbm_frac": var_bytes / (var_us * 1e-6) / (HBM_PEAK_GBPS * 1e9)}
+    del qd, kc, vc
+    torch.cuda.empty_cache()
     out["dense_128k"] = dense
     out["cowa_vs_dense_128k"] = {
         "fwd_speedup": dense["fwd_ms"] / main_fwd_ms,

@@ -205,6 +205,23 @@ int cowa_decode(const cowa_problem* p, const cowa_plan_dev* plan,
                 const void* q, const void* k_cache, const void* v_cache,
                 void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode over caches of different lengths: a batch of sequences at different positions,
+ * each under the same bottom-right distance as the forward (slinene.github.io
+ * ai-papers-daily page, method key point 2).
+ * k_cache/v_cache hold p->Lk positions per sequence (the capacity); sequence b uses the
+ * first seqlens_k[b] of them, including its new token's K/V, and its query sits at
+ * position seqlens_k[b] - 1, so d = seqlens_k[b] - 1 - j.  The window is p->win for every
+ * sequence.  No plan: each work group derives its sequence's visible 64-key blocks (prefix
+ * sink, near window, the head's band) from the length and checks every key.
+ * seqlens_k: device int32 [B], read by the kernel; values are clamped to [0, Lk], and a
+ * sequence of length 0 gets O = 0, LSE = -inf.  q/o/lse as in cowa_decode; workspace:
+ * cowa_workspace_size(COWA_OP_DECODE).  With every length equal to Lk the result is
+ * cowa_decode's.  Errors: INVALID_ARG (also for NULL seqlens_k), UNSUPPORTED,
+ * WORKSPACE_TOO_SMALL, HIP. */
+int cowa_decode_varlen(const cowa_problem* p, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* seqlens_k, void* o, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

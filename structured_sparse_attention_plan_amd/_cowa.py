@@ -23,7 +23,7 @@ COWA_OP_FWD, COWA_OP_BWD, COWA_OP_DECODE = 0, 1, 2
 COWA_BWD_DELTA, COWA_BWD_DQ, COWA_BWD_DKDV, COWA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTS = ("cowa_status_string", "cowa_window_make", "cowa_plan_blocks", "cowa_tile_sizes",
-           "cowa_workspace_size", "cowa_fwd", "cowa_bwd", "cowa_decode")
+           "cowa_workspace_size", "cowa_fwd", "cowa_bwd", "cowa_decode", "cowa_decode_varlen")
 
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
@@ -79,6 +79,9 @@ def _load():
     lib.cowa_decode.argtypes = [ctypes.POINTER(cowa_problem), ctypes.POINTER(cowa_plan_dev),
                                 _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
     lib.cowa_decode.restype = ctypes.c_int
+    lib.cowa_decode_varlen.argtypes = [ctypes.POINTER(cowa_problem), _p, _p, _p, _p, _p, _p, _p,
+                                       ctypes.c_size_t, _p]
+    lib.cowa_decode_varlen.restype = ctypes.c_int
     return lib
 
 

@@ -180,3 +180,28 @@ def decode(q, k_cache, v_cache, win, scale=None, plan=None, out=None, lse=None, 
                                              out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
                                              workspace.numel(), _stream(q.device)))
     return out, lse
+
+
+def decode_varlen(q, k_cache, v_cache, seqlens, win, scale=None, out=None, lse=None, workspace=None):
+    """Decode of B sequences of their own lengths: q [B,1,Hq,D]; caches [B,Lk,Hkv,D] hold
+    Lk positions, sequence b uses the first seqlens[b] (int32 [B] on the device) and its
+    query sits at position seqlens[b]-1 -> (o, lse [B,Hq])."""
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k_cache.shape[1], k_cache.shape[2]
+    scale = D ** -0.5 if scale is None else scale
+    prob = problem(B, Lq, Lk, Hq, Hkv, D, q.dtype, scale, win)
+    _check_tensor("q", q, (B, 1, Hq, D), q.dtype)
+    _check_tensor("k_cache", k_cache, (B, Lk, Hkv, D), q.dtype)
+    _check_tensor("v_cache", v_cache, (B, Lk, Hkv, D), q.dtype)
+    _check_tensor("seqlens", seqlens, (B,), torch.int32)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    nbytes = workspace_size("decode", prob)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    C.check("cowa_decode_varlen",
+            C.lib.cowa_decode_varlen(ctypes.byref(prob), q.data_ptr(), k_cache.data_ptr(),
+                                     v_cache.data_ptr(), seqlens.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                     _stream(q.device)))
+    return out, lse

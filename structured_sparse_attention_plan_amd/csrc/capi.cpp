@@ -287,3 +287,38 @@ extern "C" int cowa_decode(const cowa_problem* p, const cowa_plan_dev* plan, con
   a.win = dev_window(p->win);
   return hip_status(launch_decode_bf16_d128(a, (hipStream_t)stream));
 }
+
+extern "C" int cowa_decode_varlen(const cowa_problem* p, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* seqlens_k, void* o, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_problem(p);
+  if (st != COWA_OK) return st;
+  st = check_op_support(COWA_OP_DECODE, p);
+  if (st != COWA_OK) return st;
+  if (!q || !k_cache || !v_cache || !o || !seqlens_k) return COWA_ERR_INVALID_ARG;
+  size_t need = 0;
+  cowa_workspace_size(COWA_OP_DECODE, p, &need);
+  if (!workspace || workspace_bytes < need) return COWA_ERR_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)workspace & 255) != 0) return COWA_ERR_INVALID_ARG;
+
+  DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = o;
+  a.lse = lse;
+  a.nsplit = decode_splits(p);
+  const size_t rows = (size_t)p->B * p->Hq * a.nsplit;
+  a.part = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + (rows * p->D * sizeof(float) + 255) / 256 * 256);
+  a.seqlens = seqlens_k;
+  a.B = p->B;
+  a.Lk = p->Lk;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.G = p->Hq / p->Hkv;
+  a.Bk = kDecBk;
+  a.scale_log2 = p->scale * 1.44269504088896340736f;
+  a.win = dev_window(p->win);
+  return hip_status(launch_decode_bf16_d128(a, (hipStream_t)stream));
+}

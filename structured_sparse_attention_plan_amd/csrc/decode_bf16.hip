@@ -49,7 +49,75 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-template <int G>
+// Visible 64-key blocks of one query at position p of a sequence of Lb keys (Lb >= 1):
+// the prefix sink [0, sink), the near window (p - near, p] and the head's band
+// (p - hi, p - lo], each taken to blocks, sorted and merged into at most three disjoint
+// ascending runs [ba, bb) (the list the planner gives a one-row q-block).
+struct BlockRuns {
+  int ba[3], bb[3];
+  int n;      // runs
+  int total;  // blocks over all runs
+};
+__device__ __forceinline__ BlockRuns visible_block_runs(int p, int Lb, int sink, int near_w, HeadBand band) {
+  int ra[3], rb[3], n = 0;
+  if (sink > 0) {
+    ra[n] = 0;
+    rb[n] = min(sink, Lb);
+    ++n;
+  }
+  if (near_w > 0) {
+    ra[n] = max(0, p - near_w + 1);
+    rb[n] = p + 1;
+    ++n;
+  }
+  if (band.hi > band.lo && p >= band.lo) {
+    ra[n] = max(0, p - band.hi + 1);  // hi clamped to int32 max: dense bands start at 0
+    rb[n] = p - band.lo + 1;
+    ++n;
+  }
+  int ba[3], bb[3];
+  for (int k = 0; k < n; ++k) {
+    ba[k] = ra[k] / kDecBk;
+    bb[k] = (rb[k] - 1) / kDecBk + 1;
+  }
+  // sort three runs by start, then merge overlapping or adjacent ones
+  for (int x = 0; x < n; ++x)
+    for (int y = x + 1; y < n; ++y)
+      if (ba[y] < ba[x]) {
+        const int t0 = ba[x], t1 = bb[x];
+        ba[x] = ba[y];
+        bb[x] = bb[y];
+        ba[y] = t0;
+        bb[y] = t1;
+      }
+  BlockRuns r;
+  r.n = 0;
+  r.total = 0;
+  for (int k = 0; k < n; ++k) {
+    if (r.n > 0 && ba[k] <= r.bb[r.n - 1]) {
+      r.bb[r.n - 1] = max(r.bb[r.n - 1], bb[k]);
+    } else {
+      r.ba[r.n] = ba[k];
+      r.bb[r.n] = bb[k];
+      ++r.n;
+    }
+  }
+  for (int k = 0; k < r.n; ++k) r.total += r.bb[k] - r.ba[k];
+  return r;
+}
+
+// Block of run position e (0 <= e < total), runs in ascending order.
+__device__ __forceinline__ int run_block(const BlockRuns& r, int e) {
+  int kb = r.ba[0] + e;
+  if (r.n > 1 && e >= r.bb[0] - r.ba[0]) {
+    e -= r.bb[0] - r.ba[0];
+    kb = r.ba[1] + e;
+    if (r.n > 2 && e >= r.bb[1] - r.ba[1]) kb = r.ba[2] + (e - (r.bb[1] - r.ba[1]));
+  }
+  return kb;
+}
+
+template <int G, bool VAR>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   __shared__ float sm[SLOTS][G];
   __shared__ float sl[SLOTS][G];
@@ -62,8 +130,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int split = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int p = a.Lk - 1;
   const HeadBand band = head_band(a.win, h);
+  // the sequence's length: the cache capacity, or its own length in varlen mode (clamped
+  // to [0, Lk]; a sequence of length 0 sees nothing)
+  const int Lb = VAR ? min(max(a.seqlens[b], 0), a.Lk) : a.Lk;
+  const int p = Lb - 1;
 
   // query rows of the G heads, 8 dims per lane, as fp32
   float q[G][8];
@@ -80,7 +151,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int x = 0; x < 8; ++x) o[gi][x] = 0.f;
   }
 
-  const int e0 = a.row_ptr[h], e1 = a.row_ptr[h + 1];
+  // this split's share of the head's visible blocks: entries [s0, s1) of the plan's row
+  // list, or of the runs derived from the sequence's length
+  BlockRuns runs;
+  int e0, e1;
+  if constexpr (VAR) {
+    runs = Lb > 0 ? visible_block_runs(p, Lb, a.win.sink, a.win.near_w, band) : BlockRuns{{0, 0, 0}, {0, 0, 0}, 0, 0};
+    e0 = 0;
+    e1 = runs.total;
+  } else {
+    e0 = a.row_ptr[h];
+    e1 = a.row_ptr[h + 1];
+  }
   const int chunk = (e1 - e0 + a.nsplit - 1) / a.nsplit;
   const int s0 = e0 + split * chunk;
   const int s1 = min(e1, s0 + chunk);
@@ -89,7 +171,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int64_t rstride = (int64_t)a.Hkv * D;
 
   for (int e = s0; e < s1; ++e) {
-    const int ent = a.row_ent[e];
+    // varlen: every block takes the per-key check (no FULL/PARTIAL flags without a plan)
+    const int ent = VAR ? (run_block(runs, e) << 1) | 1 : a.row_ent[e];
     const int kb = ent >> 1;
     const bool partial = ent & 1;
     u32x4 kw[4], vw[4];
@@ -97,11 +180,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int j = kb * BK + rr * SLOTS + slot;
-      ok[rr] = j < a.Lk;
+      ok[rr] = j < Lb;
       const int jj = ok[rr] ? j : 0;
       kw[rr] = *(const u32x4*)(Kb + jj * rstride);
       vw[rr] = *(const u32x4*)(Vb + jj * rstride);
-      if (partial) ok[rr] = ok[rr] && visible(p, j, a.Lk, a.win.sink, a.win.near_w, band);
+      if (partial) ok[rr] = ok[rr] && visible(p, j, Lb, a.win.sink, a.win.near_w, band);
     }
     float s[4][G];
 #pragma unroll
@@ -212,7 +295,10 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
 
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(a.nsplit, a.Hkv, a.B), dim3(256), 0, s, a);
+  if (a.seqlens)
+    hipLaunchKernelGGL((decode_split_kernel<G, true>), dim3(a.nsplit, a.Hkv, a.B), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<G, false>), dim3(a.nsplit, a.Hkv, a.B), dim3(256), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(D), 0, s, a);

@@ -68,6 +68,7 @@ struct DecodeArgs {
   float* part_ml;    // workspace: [B, Hq, nsplit, 2] (max in log2 units, sum)
   const int32_t* row_ptr;
   const int32_t* row_ent;
+  const int32_t* seqlens;  // varlen decode: [B] cache lengths (no plan); else null
   int32_t B, Lk, Hq, Hkv, G;
   int32_t Bk, nsplit;
   float scale_log2;
@@ -77,7 +78,7 @@ struct DecodeArgs {
 hipError_t launch_fwd_f32_d64(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16_d128(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16_d128(const BwdArgs& a, int stages, hipStream_t s);
-hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t s);  // varlen when a.seqlens
 bool decode_supports_group(int G);
 
 // Tile shapes of each kernel family (tokens per q-block, keys per k-block).

@@ -112,3 +112,11 @@ def test_entry_points_validate_before_launch():
     pld = _fake_plan(pd, "decode")
     assert C.lib.cowa_decode(ctypes.byref(pd), ctypes.byref(pld), x, x, x, x, None, x, 8,
                              None) == C.COWA_ERR_WORKSPACE_TOO_SMALL
+    # varlen decode: NULL lengths, workspace too small, more than one query row
+    assert C.lib.cowa_decode_varlen(ctypes.byref(pd), x, x, x, None, x, None, x, 1 << 30,
+                                    None) == C.COWA_ERR_INVALID_ARG
+    assert C.lib.cowa_decode_varlen(ctypes.byref(pd), x, x, x, x, x, None, x, 8,
+                                    None) == C.COWA_ERR_WORKSPACE_TOO_SMALL
+    p2 = _prob(Lq=2, Lk=4096, win=api.make_window(4096, 8, 4, 16))
+    assert C.lib.cowa_decode_varlen(ctypes.byref(p2), x, x, x, x, x, None, x, 1 << 30,
+                                    None) == C.COWA_ERR_UNSUPPORTED

@@ -193,6 +193,43 @@ def test_decode_small(B, Lk, Hq, Hkv, sink, near, mode):
     assert_bf16_close("LSE", lse, Lo[:, :, 0])
 
 
+def test_decode_varlen():
+    """Decode of sequences of different lengths in one batch (capacity 3000): each
+    sequence b against the oracle's decode over its first seqlens[b] keys, with the
+    window of the capacity; length 0 gives O = 0 and LSE = -inf."""
+    Lk, B = 3000, 6
+    lens = [3000, 1, 77, 1500, 2999, 0]
+    _case(f"decode varlen capacity {Lk} lengths {lens}")
+    ow, win = _windows(Lk, 8, 128, 256)
+    q, k, v = inputs.attention_inputs(B, 1, Lk, 40, 8, 128, seed=10)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o, lse = api.decode_varlen(q.to(DEV), k.to(DEV), v.to(DEV), seq, win)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.all(o[b] == 0) and torch.all(lse[b] == -float("inf")), "empty sequence"
+            continue
+        Oo, Lo = oracle.decode(q[b:b + 1], k[b:b + 1, :n], v[b:b + 1, :n], ow, 128 ** -0.5)
+        assert_bf16_close(f"O[{b}] (len {n})", o[b:b + 1], Oo)
+        assert_bf16_close(f"LSE[{b}]", lse[b:b + 1], Lo[:, :, 0])
+
+
+def test_decode_varlen_full_lengths_equal_decode():
+    """With every length equal to the capacity the varlen decode visits the same blocks in
+    the same order as the planned decode: bit-equal outputs."""
+    B, Lk = 4, 5000
+    _case(f"decode varlen B={B} all lengths {Lk} vs planned decode")
+    _, win = _windows(Lk, 8, 128, 256)
+    q, k, v = (t.to(DEV) for t in inputs.attention_inputs(B, 1, Lk, 40, 8, 128, seed=11))
+    o, lse = api.decode(q, k, v, win)
+    ov, lsev = api.decode_varlen(q, k, v, torch.full((B,), Lk, dtype=torch.int32, device=DEV), win)
+    torch.cuda.synchronize()
+    n_o = int((o != ov).sum().item())
+    n_l = int((lse != lsev).sum().item())
+    print(f"  O differs at {n_o}, LSE at {n_l}", flush=True)
+    assert n_o == 0 and n_l == 0
+
+
 def test_decode_equals_forward_last_row():
     _case("decode vs forward last row L=3000")
     L = 3000
