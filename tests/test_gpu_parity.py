@@ -148,6 +148,28 @@ def test_bwd_bf16_prefill_chunk(B, Lq, Lk, Hq, Hkv, sink, near, mode):
     assert_bf16_close("dV", dv, rv, value_scaled=True)
 
 
+@pytest.mark.parametrize("qexp", [9, -9])
+def test_bwd_bf16_scaled_q(qexp):
+    """Q multiplied by 2^qexp and K by 2^-qexp (exact in bf16; the scores do not change):
+    the fp16 dK product's per-row and per-item power-of-two scales move away from 1, dK
+    scales by 2^qexp and dQ by 2^-qexp."""
+    L = 600
+    _case(f"bwd bf16 L={L} Q * 2^{qexp}, K * 2^{-qexp}")
+    ow, win = _windows(L, 8, 16, 64)
+    q, k, v, do = inputs.attention_inputs(1, L, L, 40, 8, 128, seed=12, with_dout=True)
+    q = (q.float() * 2.0 ** qexp).to(torch.bfloat16)
+    k = (k.float() * 2.0 ** -qexp).to(torch.bfloat16)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = api.fwd(qd, kd, vd, win)
+    dq, dk, dv = api.bwd(qd, kd, vd, o, lse, dod, win)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attn_bwd(q, k, v, do, ow, 128 ** -0.5)
+    # compare in the units of the unscaled problem, where the bars are set
+    assert_bf16_close("dQ * 2^qexp", dq.float() * 2.0 ** qexp, rq * 2.0 ** qexp, value_scaled=True)
+    assert_bf16_close("dK * 2^-qexp", dk.float() * 2.0 ** -qexp, rk * 2.0 ** -qexp, value_scaled=True)
+    assert_bf16_close("dV", dv, rv, value_scaled=True)
+
+
 def test_chunked_prefill_matches_full_forward():
     """Chunked prefill: the forward of rows [c0, c1) against keys [0, c1) (Lq < Lk, the
     same window) equals rows c0..c1-1 of the forward over the whole sequence, bit for bit.
