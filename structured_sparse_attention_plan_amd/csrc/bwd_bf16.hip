@@ -94,9 +94,10 @@ template <int V>
 using IC = std::integral_constant<int, V>;
 
 // S and dP products with the accumulator in VGPRs (the VALU reads each element as soon as
-// it is final, without an AGPR read) and the B operand (K or V of the lane's key) in
-// AGPRs; the "0" forms start from a zero accumulator.  The output is early-clobber: it
-// must not share registers with the operands.
+// it is final, without an AGPR read) and the B operand in AGPRs (the lane's register-
+// resident fragment: K or V in the dK/dV kernel, Q or dO in the dQ kernel).  The "0"
+// forms start from a zero accumulator; their output is early-clobber, so it never shares
+// registers with the operands.
 __device__ __forceinline__ void mfma_f16_va(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
 }
@@ -113,7 +114,8 @@ __device__ __forceinline__ void mfma_bf16_va0(f32x16& acc, const bf16x8& a, cons
 // ------------------------------------------------------------------------ dQ
 // One work item = (KV head, q-block of 128 rows), 4 waves x 32 rows; each lane owns one
 // query row (column of the transposed products) and keeps its Q and dO fragments in
-// registers.  The item walks its row list as 64-key tiles t (two per listed 128-key
+// AGPRs (the B operands of S^T and dP^T, whose accumulators are VGPRs).  The item walks
+// its row list as 64-key tiles t (two per listed 128-key
 // block).  Iteration t is one block of 48 MFMAs, the dQ^T += K^T dS^T products of tile
 // t-1 (16) then S^T = K Q^T and dP^T = V dO^T of tile t+1 (32), with the VALU work of
 // tile t (P, dS and their bf16 packing) spread between them by scheduling fences.  K
