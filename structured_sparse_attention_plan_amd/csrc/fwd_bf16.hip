@@ -336,12 +336,10 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     return sum;
   };
 
-  // 8 probabilities packed to bf16 for the PV product, and their fp32 row sum (it sets
-  // LSE, which the backward reuses)
-  auto pack8 = [&](const float (&pb)[8], bf16x8& dst, float& sum) __attribute__((always_inline)) {
-    dst = join(to_bf16x4(pb[0], pb[1], pb[2], pb[3]), to_bf16x4(pb[4], pb[5], pb[6], pb[7]));
-#pragma unroll
-    for (int q = 0; q < 8; ++q) sum += pb[q];
+  // probabilities x0, x1 rounded to bf16 as one register (two keys of a PV operand)
+  auto bf16_pair = [&](float x0, float x1) __attribute__((always_inline)) {
+    const bf16x2 h = {(__bf16)x0, (__bf16)x1};
+    return __builtin_bit_cast(uint32_t, h);
   };
 
   // List entries of tiles t .. t+2 are kept in scalar registers; entry t+3 is fetched
@@ -407,6 +405,19 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
 
     float sum[CB] = {0.f, 0.f};
     float pb[8];
+    uint32_t pw[4];
+    // element p of the tile's P into the row sum and, as the second of a pair, into its
+    // bf16 PV operand (complete after every eighth element)
+    auto fold = [&](auto pi) __attribute__((always_inline)) {
+      constexpr int p = decltype(pi)::value, pc = p >> 5, pe = p & 31;
+      sum[pc] += pb[p & 7];
+      if constexpr ((p & 1) == 1) pw[(p & 7) >> 1] = bf16_pair(pb[(p - 1) & 7], pb[p & 7]);
+      if constexpr ((p & 7) == 7) {
+        bf16x8& dst = pfc[pe >> 4][pc][(pe >> 3) & 1];
+        dst = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+        pin_out(dst);
+      }
+    };
     float xin = (sc[0][0][0]);
     static_for<0, 64>([&](auto slot) __attribute__((always_inline)) {
       constexpr int s = decltype(slot)::value;
@@ -437,27 +448,23 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       {
         // softmax element s: row block s / 32, element e = s % 32 (key block e / 16,
-        // accumulator element e % 16); input taken one slot ahead, result fenced one slot
-        // late, packing (and its row sum) one slot after the eighth element of a run
+        // accumulator element e % 16), its input taken one slot ahead.  Element s - 2
+        // joins the fp32 row sum (it sets LSE, which the backward reuses) and, when it
+        // completes a pair, the pair is rounded to bf16 into its PV operand: one add and
+        // half a conversion per slot, in the order of additions of a plain running sum.
+        // Two slots (not one) after its exponential: a product written as an asm
+        // statement does not count as a wait state, and a VALU read of a transcendental
+        // result needs one.
         constexpr int c = s >> 5;
         const float x = xin;
         if constexpr (s + 1 < 64) xin = (sc[((s + 1) >> 4) & 1][(s + 1) >> 5][(s + 1) & 15]);
-        if constexpr (s >= 1) {
-          constexpr int p = s - 1, pc = p >> 5, pe = p & 31;
-          pin_out(pb[p & 7]);
-          if constexpr ((p & 7) == 7) {
-            bf16x8& dst = pfc[pe >> 4][pc][(pe >> 3) & 1];
-            pack8(pb, dst, sum[pc]);
-            pin_out(dst);
-            pin_out(sum[pc]);
-          }
-        }
+        if constexpr (s >= 2) fold(IC<s - 2>{});
         pb[s & 7] = __builtin_amdgcn_exp2f(fmaf(x, a.scale_log2, -m[c]));
       }
       __builtin_amdgcn_sched_barrier(0);
     });
-    pin_out(pb[7]);
-    pack8(pb, pfc[1][1][1], sum[1]);
+    fold(IC<62>{});
+    fold(IC<63>{});
 
     // reference check on the column sums (both lane halves)
     float alpha[CB] = {1.f, 1.f};
