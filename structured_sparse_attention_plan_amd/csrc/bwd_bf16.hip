@@ -372,20 +372,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
           const int e = x - 3;
           cdv[e & 1] = pin(cd[e >> 4][e & 15]);
         }
-        if (x >= 5 && x <= 36) pin_out(dsv[(x - 5) >> 4][(x - 5) & 15]);
-        // dS pair q (elements 2 q, 2 q + 1) packed to bf16 at step 2 q + 6, right after its
-        // second element is fenced, and fenced in turn a step later; pair q sits in word
-        // q % 4 of half (q / 4) % 2 of block q / 8
-        if (x >= 6 && x <= 36 && (x & 1) == 0) {
-          const int q = (x - 6) >> 1, k2 = q >> 3, hf = (q >> 2) & 1, w = q & 3;
+        __builtin_amdgcn_sched_barrier(0);
+        // dS pair q (elements 2 q, 2 q + 1) packed to bf16 at step 2 q + 7, after this
+        // step's own VALU work (its second element was fenced at the end of the previous
+        // step: a read right after the fence would cost a wait state), and fenced in turn
+        // a step later; pair q sits in word q % 4 of half (q / 4) % 2 of block q / 8
+        if (x >= 7 && x <= 37 && (x & 1)) {
+          const int q = (x - 7) >> 1, k2 = q >> 3, hf = (q >> 2) & 1, w = q & 3;
           const float x0 = dsv[k2][2 * (q & 7)], x1 = dsv[k2][2 * (q & 7) + 1];
           const bf16x2 v = {(__bf16)x0, (__bf16)x1};
           npk[k2][hf][w] = __builtin_bit_cast(uint32_t, v);
         }
-        if (x >= 7 && x <= 37 && (x & 1)) {
-          const int q = (x - 7) >> 1;
+        if (x >= 8 && x <= 38 && (x & 1) == 0) {
+          const int q = (x - 8) >> 1;
           pin_out(npk[q >> 3][(q >> 2) & 1][q & 3]);
         }
+        if (x >= 5 && x <= 36) pin_out(dsv[(x - 5) >> 4][(x - 5) & 15]);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -813,10 +815,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       f32x4 f4[4], t4[4], l4[4], c4[4];
       f4[0] = cur.f0;
       t4[0] = cur.t0;
-      float ds[16], prv[2], dpv[2];
+      float ds[16], prv[3], dpv[3];
       uint32_t wpa[2][4], wds[2][4];
-      prv[0] = pin(cur.pr[0]);
-      dpv[0] = pin(cur.dp[0]);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        prv[e] = pin(cur.pr[e]);
+        dpv[e] = pin(cur.dp[e]);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
@@ -845,33 +850,37 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         // ahead of the slot's dS
         if (x & 1) {
           const int q = x >> 1;
-          wpa[q >> 2][q & 3] = pack_bf16x2(prv[0], prv[1]);
+          wpa[q >> 2][q & 3] = pack_bf16x2(prv[(x - 1) % 3], prv[x % 3]);
         } else if (x >= 2) {
           const int q = (x - 2) >> 1;
           pin_out(wpa[q >> 2][q & 3]);
         }
-        // dS element x; inputs are taken (pin) one slot before and the result fenced
-        // (pin_out) one slot after, so nothing waits on a result in its own slot
-        ds[x] = prv[x & 1] * fmaf(dpv[x & 1], f4[x >> 2][x & 3], -t4[x >> 2][x & 3]);
-        if (x + 1 < 16) {
-          prv[(x + 1) & 1] = pin(cur.pr[x + 1]);
-          dpv[(x + 1) & 1] = pin(cur.dp[x + 1]);
+        // dS element x; inputs are taken (pin) two slots before and the result fenced
+        // (pin_out) one slot after, so nothing waits on a result in its own slot.  A VALU
+        // read of a pinned value right after the asm statement costs a wait state, and a
+        // product written as asm does not count as one: hence two slots, not one.
+        ds[x] = prv[x % 3] * fmaf(dpv[x % 3], f4[x >> 2][x & 3], -t4[x >> 2][x & 3]);
+        if (x + 2 < 16) {
+          prv[(x + 2) % 3] = pin(cur.pr[x + 2]);
+          dpv[(x + 2) % 3] = pin(cur.dp[x + 2]);
         }
-        if (x >= 1) pin_out(ds[x - 1]);
-        // dS pair q at slot 2 q + 2, right after its second element is fenced (fenced in
-        // turn at the next slot)
-        if ((x & 1) == 0 && x >= 2) {
-          const int q = (x - 2) >> 1;
-          wds[q >> 2][q & 3] = pack_f16x2(ds[2 * q], ds[2 * q + 1]);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        // dS pair q at slot 2 q + 3, after this slot's dS element (its second element was
+        // fenced at the end of the previous slot), fenced in turn at the next slot
         if ((x & 1) && x >= 3) {
           const int q = (x - 3) >> 1;
+          wds[q >> 2][q & 3] = pack_f16x2(ds[2 * q], ds[2 * q + 1]);
+        }
+        if ((x & 1) == 0 && x >= 4) {
+          const int q = (x - 4) >> 1;
           pin_out(wds[q >> 2][q & 3]);
         }
+        if (x >= 1) pin_out(ds[x - 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
       pin_out(ds[15]);
       pin_out(wpa[1][3]);
+      pin_out(wds[1][2]);
       wds[1][3] = pack_f16x2(ds[14], ds[15]);
       if (ent_g1 & 1) mask(sn, RB1, ent_g1 >> 1);
 
