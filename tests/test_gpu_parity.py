@@ -68,6 +68,31 @@ def test_fwd_bf16_small_full(B, Lq, Lk, Hq, Hkv, sink, near, mode):
     assert_bf16_close("LSE", lse, Lo)
 
 
+@pytest.mark.parametrize("case", ["rises", "first_mass_low"])
+def test_fwd_bf16_reference_moves(case):
+    """Inputs that take the forward's rare path, where a column's softmax reference moves:
+    "rises", later keys score far above the first tile's maximum (tile sums above 2^32);
+    "first_mass_low", no prefix sink, so some columns see no key in their item's first
+    tile, and every score lies far below 0 (their first visible tile sums to less than
+    2^-32).  The result does not depend on the reference, so the oracle's plain softmax
+    is the bar."""
+    L, Hq, Hkv = 700, 8, 2
+    sink, near = (16, 100) if case == "rises" else (0, 64)
+    _case(f"fwd bf16 L={L} Hq={Hq} Hkv={Hkv} sink={sink} near={near}, reference {case}")
+    ow, win = _windows(L, Hkv, sink, near)
+    q, k, v = inputs.attention_inputs(1, L, L, Hq, Hkv, 128, seed=21)
+    q = q.abs()
+    if case == "rises":
+        k[:, 200:330] = 4.0   # q.k scale about +36 against about +3 in the first tile
+    else:
+        k[:] = -4.0           # every score about -36
+    o, lse = api.fwd(q.to(DEV), k.to(DEV), v.to(DEV), win)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.attn_fwd(q, k, v, ow, 128 ** -0.5)
+    assert_bf16_close("O", o, Oo)
+    assert_bf16_close("LSE", lse, Lo)
+
+
 def test_fwd_bf16_mid_4096_full():
     _case("fwd bf16 L=4096 Hq=40 Hkv=8 sink=128 near=512")
     L = 4096
