@@ -123,6 +123,7 @@ def test_fwd_bitwise_repeatable():
     (2, 333, 40, 8, 0, 32, "duplicated"),
     (1, 300, 40, 8, 5, 20, "dense"),
     (1, 400, 8, 2, 16, 64, "complementary"),
+    (1, 333, 8, 8, 5, 40, "complementary"),      # G = 1
 ])
 def test_bwd_bf16_small_full(B, L, Hq, Hkv, sink, near, mode):
     _case(f"bwd bf16 B={B} L={L} Hq={Hq} Hkv={Hkv} sink={sink} near={near} {mode}")
@@ -228,6 +229,9 @@ def test_chunked_prefill_matches_full_forward():
     (2, 4099, 40, 8, 0, 100, "duplicated"),
     (1, 3000, 16, 4, 10, 64, "complementary"),   # G = 4
     (2, 777, 40, 8, 7, 33, "dense"),
+    (2, 2000, 8, 8, 16, 64, "complementary"),    # G = 1
+    (1, 1500, 16, 8, 16, 64, "duplicated"),      # G = 2
+    (2, 2500, 16, 2, 32, 128, "complementary"),  # G = 8
 ])
 def test_decode_small(B, Lk, Hq, Hkv, sink, near, mode):
     _case(f"decode B={B} Lk={Lk} Hq={Hq} Hkv={Hkv} sink={sink} near={near} {mode}")
