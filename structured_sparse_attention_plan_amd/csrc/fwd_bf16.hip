@@ -55,7 +55,6 @@ constexpr int CB = WROWS / 32;       // 2 column blocks of 32 per wave
 constexpr int BK = kFwdBk;           // 64 keys per tile
 constexpr int KB2 = BK / 32;         // 2 key blocks of 32
 constexpr int TILE = BK * D;         // elements per K or V tile
-constexpr float kRescaleThreshold = 8.0f;
 
 template <int V>
 using IC = std::integral_constant<int, V>;
@@ -86,13 +85,8 @@ __device__ __forceinline__ float agpr_scale(float x, float alpha) {
   return r;
 }
 
-// Returns x unchanged, but the value is taken at this point of the program: computations
-// that use the result cannot be hoisted above it (it pins VALU work to its pipeline slot).
-__device__ __forceinline__ float pin(float x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-__device__ __forceinline__ void pin_out(float& x) { asm volatile("" : "+v"(x)); }
+// Fences a result at this point of the program: it must be complete here, so its
+// computation stays in the slot that produced it.
 __device__ __forceinline__ void pin_out(bf16x8& x) { asm volatile("" : "+v"(x)); }
 
 // S products with their accumulators in VGPRs: the softmax reads S with plain VALU
