@@ -320,8 +320,9 @@ def main():
         copy_probe()
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; the operator shards by "
-                                   "KV head with no exchange, see the design notes",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; across GPUs the operator "
+                                   "would shard by KV head, each GPU running these kernels on its "
+                                   "own heads with no exchange between GPUs",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     import numpy as np
