@@ -28,7 +28,7 @@ method saves work by skipping masked keys, not by approximating), so the oracle 
 plain definition: build the mask element by element, then softmax(scale q k^T) v over
 the visible keys in float64.
 
-Readings where the pages are silent (each is also listed in the design notes):
+Readings where the pages are silent:
   distance       d = i + (Lk - Lq) - j  (bottom-right alignment); causal iff d >= 0
   sink           absolute key index j < sink, shared by all heads, still causal
   near           0 <= d < near (half-open, includes the diagonal)
