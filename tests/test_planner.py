@@ -93,7 +93,7 @@ def test_info_only_call_matches_full_call():
 
 @pytest.mark.parametrize("L,sink,near,Bq,Bk,tiles,partial", [
     # tile counts at the 32K and 128K workloads with 128x128 tiles (also derivable by hand
-    # from the band edges; listed in the design notes)
+    # from the band edges)
     (32768, 128, 2048, 128, 128, 64914, 5387),
     (131072, 128, 4096, 128, 128, 768050, 22059),
 ])
