@@ -95,14 +95,17 @@ class Window:
                 f"lr={self.lr}, mode={self.mode})")
 
 
-def mask_rows(rows, Lq, Lk, h, win):
-    """Boolean mask [len(rows), Lk]: key j visible to query row i under KV head h.
+def mask_rows(rows, Lq, Lk, h, win, keys=None):
+    """Boolean mask [len(rows), len(keys)]: key j visible to query row i under KV head h
+    (keys default to all Lk keys).
 
-    Evaluated element by element on the full (i, j) grid from the definition — no
-    interval arithmetic — so it stays independent of any block planner."""
-    i = np.asarray(rows, dtype=np.int64)[:, None]
-    j = np.arange(Lk, dtype=np.int64)[None, :]
-    d = i + (Lk - Lq) - j
+    Evaluated element by element on the (i, j) grid from the definition — no interval
+    arithmetic — so it stays independent of any block planner."""
+    # int32 holds every index and distance of sequences up to 2^30 tokens
+    it = np.int32 if Lq + Lk < 2 ** 30 else np.int64
+    i = np.asarray(rows, dtype=it)[:, None]
+    j = (np.arange(Lk, dtype=it) if keys is None else np.asarray(keys, dtype=it))[None, :]
+    d = (i + it(Lk - Lq)) - j
     causal = d >= 0
     in_sink = j < win.sink
     in_near = d < win.near
@@ -137,16 +140,21 @@ def _take_rows(x, rows):
 
 
 def _masked_softmax_row_stats(s, m):
-    """Row max, denominator and probabilities of a masked score matrix s [R, Lk]."""
-    s = np.where(m, s, -np.inf)
+    """Probabilities and logsumexp of the rows of a masked score matrix s [R, K] (s is
+    overwritten with the probabilities): hidden entries are set to -inf, the row max is
+    subtracted, exp (exactly 0 at -inf), divided by the row sum.  A row with no visible
+    entry gets P = 0 and LSE = -inf."""
+    np.copyto(s, -np.inf, where=~m)
     mx = s.max(axis=1, keepdims=True)
     empty = ~np.isfinite(mx)
-    mx = np.where(empty, 0.0, mx)
-    e = np.where(m, np.exp(s - mx), 0.0)
-    den = e.sum(axis=1, keepdims=True)
-    p = np.where(den > 0, e / np.where(den > 0, den, 1.0), 0.0)
-    lse = np.where(den > 0, mx + np.log(np.where(den > 0, den, 1.0)), -np.inf)
-    return p, lse[:, 0]
+    mx[empty] = 0.0
+    s -= mx
+    np.exp(s, out=s)
+    den = s.sum(axis=1, keepdims=True)
+    safe = np.where(den > 0, den, 1.0)
+    s /= safe
+    lse = np.where(den > 0, mx + np.log(safe), -np.inf)
+    return s, lse[:, 0]
 
 
 def attn_fwd(q, k, v, win, scale, rows=None):
@@ -231,41 +239,65 @@ def attn_bwd_dq_rows(q, k, v, do, win, scale, rows):
     return dq
 
 
-def attn_bwd_dkdv_cols(q, k, v, do, win, scale, cols, row_chunk=512):
+def attn_bwd_dkdv_cols(q, k, v, do, win, scale, cols, row_chunk=256, workers=1):
     """dK and dV on the key columns `cols` only.
 
-    A column j receives from every query row that sees it, so the rows are found from
-    the explicit mask, and each such row's full softmax (over all its visible keys) is
-    computed before its contribution to the requested columns is summed.
-    -> dK [B, C, Hkv, D], dV [B, C, Hkv, D]"""
+    A column j receives from every query row that sees it, so those rows are found from
+    the explicit mask evaluated at the requested columns, and each such row's full
+    softmax (over all of its visible keys) is computed before its contribution to the
+    requested columns is summed.  Per chunk of rows the products run over the keys that
+    some row of the chunk sees (the mask on the full key range says which); every other
+    key has probability exactly 0 for every row of the chunk and adds nothing.
+    Chunks are independent; with workers > 1 they run in threads and their results are
+    summed in chunk order.  -> dK [B, C, Hkv, D], dV [B, C, Hkv, D]"""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, Lq, Hq, D = q.shape
     _, Lk, Hkv, _ = k.shape
     G = Hq // Hkv
     cols = np.asarray(cols, dtype=np.int64)
-    dk = np.zeros((B, len(cols), Hkv, D))
-    dv = np.zeros((B, len(cols), Hkv, D))
+
+    def chunk_part(h, rows):
+        dk = np.zeros((B, len(cols), D))
+        dv = np.zeros((B, len(cols), D))
+        m = mask_rows(rows, Lq, Lk, h, win)
+        keys = np.nonzero(m.any(axis=0))[0]
+        m = m[:, keys]
+        at = np.searchsorted(keys, cols)  # requested columns inside `keys`
+        seen = (at < len(keys)) & (keys[np.minimum(at, len(keys) - 1)] == cols)
+        for b in range(B):
+            kk, vv = k[b, keys, h, :], v[b, keys, h, :]
+            for qh in range(h * G, (h + 1) * G):
+                s = scale * (q[b, rows, qh, :] @ kk.T)
+                p, _ = _masked_softmax_row_stats(s, m)
+                o = p @ vv
+                delta = (do[b, rows, qh, :] * o).sum(axis=1, keepdims=True)
+                pc = np.where(seen[None, :], p[:, np.minimum(at, len(keys) - 1)], 0.0)
+                dpc = do[b, rows, qh, :] @ v[b, cols, h, :].T
+                dsc = pc * (dpc - delta)
+                dk[b] += scale * (dsc.T @ q[b, rows, qh, :])
+                dv[b] += pc.T @ do[b, rows, qh, :]
+        return h, dk, dv
+
+    tasks = []
     for h in range(Hkv):
         # rows that see at least one requested column
-        need = np.zeros(Lq, dtype=bool)
-        for start in range(0, Lq, row_chunk):
-            r = np.arange(start, min(Lq, start + row_chunk))
-            need[r] = mask_rows(r, Lq, Lk, h, win)[:, cols].any(axis=1)
+        need = mask_rows(np.arange(Lq), Lq, Lk, h, win, keys=cols).any(axis=1)
         rows_all = np.nonzero(need)[0]
         for start in range(0, len(rows_all), row_chunk):
-            rows = rows_all[start:start + row_chunk]
-            m = mask_rows(rows, Lq, Lk, h, win)
-            for b in range(B):
-                for qh in range(h * G, (h + 1) * G):
-                    s = scale * (q[b, rows, qh, :] @ k[b, :, h, :].T)
-                    p, _ = _masked_softmax_row_stats(s, m)
-                    o = p @ v[b, :, h, :]
-                    delta = (do[b, rows, qh, :] * o).sum(axis=1, keepdims=True)
-                    pc = p[:, cols]
-                    dpc = do[b, rows, qh, :] @ v[b, cols, h, :].T
-                    dsc = pc * (dpc - delta)
-                    dk[b, :, h, :] += scale * (dsc.T @ q[b, rows, qh, :])
-                    dv[b, :, h, :] += pc.T @ do[b, rows, qh, :]
+            tasks.append((h, rows_all[start:start + row_chunk]))
+    if workers > 1:
+        # one BLAS thread per worker: the workers already fill the cores
+        from concurrent.futures import ThreadPoolExecutor
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+            parts = list(ex.map(lambda t: chunk_part(*t), tasks))
+    else:
+        parts = [chunk_part(*t) for t in tasks]
+    dk = np.zeros((B, len(cols), Hkv, D))
+    dv = np.zeros((B, len(cols), Hkv, D))
+    for h, pk, pv in parts:
+        dk[:, :, h, :] += pk
+        dv[:, :, h, :] += pv
     return dk, dv
 
 

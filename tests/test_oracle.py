@@ -336,9 +336,11 @@ def test_bwd_row_and_column_subsets_match_full():
     cols = [0, 2, 3, 40, 69]
     np.testing.assert_allclose(oracle.attn_bwd_dq_rows(q, k, v, do, win, 0.5, rows),
                                dq[:, rows], atol=1e-12)
-    dkc, dvc = oracle.attn_bwd_dkdv_cols(q, k, v, do, win, 0.5, cols, row_chunk=16)
-    np.testing.assert_allclose(dkc, dk[:, cols], atol=1e-12)
-    np.testing.assert_allclose(dvc, dv[:, cols], atol=1e-12)
+    for chunk, workers in ((16, 1), (7, 4), (256, 1)):
+        dkc, dvc = oracle.attn_bwd_dkdv_cols(q, k, v, do, win, 0.5, cols, row_chunk=chunk,
+                                             workers=workers)
+        np.testing.assert_allclose(dkc, dk[:, cols], atol=1e-12)
+        np.testing.assert_allclose(dvc, dv[:, cols], atol=1e-12)
 
 
 # ----------------------------------------------------------------------------- decode
