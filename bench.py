@@ -234,22 +234,24 @@ def extras(seed, main_fb_ms, main_fwd_ms, main_bwd_ms, main_dec_ms, main_E, main
         q, k, v, do = inputs.attention_inputs(1, L, L, hq, hkv, d, seed=seed, device=dev,
                                               dtype=dtype, with_dout=True)
         o = torch.empty_like(q)
+        o_lo = torch.empty_like(q) if dtype == torch.bfloat16 else None
         lse = torch.empty((1, hq, L), dtype=torch.float32, device=dev)
         E = plan_f.info.edges * (hq // hkv)
         r = {"edges": E, "window": {"sink": win.sink, "near": win.near_w, "band_width": win.lr,
                                     "bands": mode}}
-        r["fwd_ms"] = _events_ms(lambda: api.fwd(q, k, v, win, scale, plan=plan_f, out=o, lse=lse),
-                                 steps, warmup)
+        r["fwd_ms"] = _events_ms(lambda: api.fwd(q, k, v, win, scale, plan=plan_f, out=o, lse=lse,
+                                                 o_lo=o_lo if bwd else None), steps, warmup)
         r["fwd_tflops"] = 4 * d * E / (r["fwd_ms"] * 1e-3) / 1e12
         if bwd:
             plan_b = api.build_plan("bwd", pf, dev)
             grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
             ws = torch.empty(api.workspace_size("bwd", pf), dtype=torch.uint8, device=dev)
             r["bwd_ms"] = _events_ms(lambda: api.bwd(q, k, v, o, lse, do, win, scale, plan=plan_b,
-                                                     grads=grads, workspace=ws), steps, warmup)
+                                                     grads=grads, workspace=ws, o_lo=o_lo),
+                                     steps, warmup)
             r["bwd_tflops"] = 10 * d * E / (r["bwd_ms"] * 1e-3) / 1e12
             r["fwd_bwd_ms"] = r["fwd_ms"] + r["bwd_ms"]
-        del q, k, v, do, o, lse
+        del q, k, v, do, o, o_lo, lse
         torch.cuda.empty_cache()
         return r
 
@@ -356,6 +358,7 @@ def main():
                                           with_dout=True)
     qd, kc, vc = inputs.attention_inputs(DEC_B, 1, L, HQ, HKV, D, seed=args.seed + 10, device=dev)
     o = torch.empty_like(q)
+    o_lo = torch.empty_like(q)     # O's bf16 rounding residual, kept for the backward
     lse = torch.empty((1, HQ, L), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_b = torch.empty(api.workspace_size("bwd", pf), dtype=torch.uint8, device=dev)
@@ -376,11 +379,11 @@ def main():
                 e.record(stream)
                 marks.append(e)
         mark()
-        api.fwd(q, k, v, win, scale, plan=plan_f, out=o, lse=lse)
+        api.fwd(q, k, v, win, scale, plan=plan_f, out=o, lse=lse, o_lo=o_lo)
         mark()
         for st in (C.COWA_BWD_DELTA, C.COWA_BWD_DQ, C.COWA_BWD_DKDV):
             api.bwd(q, k, v, o, lse, do, win, scale, plan=plan_b, grads=(dq, dk, dv), workspace=ws_b,
-                    stages=st)
+                    stages=st, o_lo=o_lo)
             mark()
         api.decode(qd, kc, vc, win, scale, plan=plan_d, out=od, lse=lsed, workspace=ws_d)
         mark()

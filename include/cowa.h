@@ -154,35 +154,52 @@ typedef struct cowa_problem {
 int cowa_tile_sizes(int op, const cowa_problem* p, int32_t* Bq, int32_t* Bk);
 
 /* Bytes of device workspace `op` needs for problem p (0 if none).  The backward keeps
- * Delta and a power-of-two scale per (query head, row) in fp32 and an fp16 copy of Q
- * (B * Lq * Hq * D * 2 bytes); the decode keeps its split partials. */
+ * three fp32 values per (query head, row) (Delta, the power-of-two scales of Q and dO),
+ * 256 bytes of launch-wide maxima, fp16 copies of Q and dO (2 * B * Lq * Hq * D * 2
+ * bytes) and of K (B * Lk * Hkv * D * 2 bytes); the decode keeps its split partials. */
 int cowa_workspace_size(int op, const cowa_problem* p, size_t* bytes);
 
-/* Forward (the operator of the abstract; training forward and prefill).  For every
+/* Forward (the operator of the abstract, used for training and for prefill: "CoWindow
+ * Attention" abstract; beyondmarketintelligence.com post, second paragraph).  For every
  * query head and row: O = softmax(scale * q K^T restricted to visible keys) V, and
  * LSE = log of the softmax denominator (natural log, including the scale).
  * Supported: dtype BF16 with D = 128 (bf16 in/out, fp32 accumulation) and dtype F32
  * with D = 64; Hq % Hkv == 0.  q,k,v,o are device pointers of `dtype`; lse is fp32.
- * A row with no visible key (only possible with near_w = 0) gets O = 0, LSE = -inf.
- * Errors: INVALID_ARG, UNSUPPORTED, PLAN_MISMATCH (plan tiling must be
- * cowa_tile_sizes(COWA_OP_FWD)), HIP. */
+ * o_lo (bf16 only, may be NULL): receives O - bf16(O) rounded to bf16, the part of the
+ * fp32 result that the bf16 O drops, in O's layout.  A training caller keeps it with O
+ * and LSE and passes it to cowa_bwd, which then forms Delta = dO . O from O to about 16
+ * significant bits instead of 8.
+ * A row with no visible key (only possible with near_w = 0, or with Lq > Lk for the
+ * first Lq - Lk rows) gets O = 0, LSE = -inf.
+ * Errors: INVALID_ARG (also for o_lo with dtype F32), UNSUPPORTED, PLAN_MISMATCH (plan
+ * tiling must be cowa_tile_sizes(COWA_OP_FWD)), HIP. */
 int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan,
-             const void* q, const void* k, const void* v, void* o, float* lse,
+             const void* q, const void* k, const void* v, void* o, float* lse, void* o_lo,
              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward from the saved LSE (training backward; same pattern as the forward):
+/* Backward from the saved LSE: the pattern serves training forward and backward alike
+ * (beyondmarketintelligence.com post, second paragraph; "CoWindow Attention" abstract),
+ * with the gradients of the same masked softmax attention:
  *   Delta_i = dO_i . O_i,  P = exp(scale q.k - LSE),  dS = P (dO.v - Delta)
  *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO   (dK, dV summed over the
  *   query heads of each KV head).
+ * o_lo: the residual cowa_fwd wrote (may be NULL: Delta then uses the bf16 O alone).
  * `stages` selects the kernels to run (COWA_BWD_ALL for the whole backward): DELTA
- * writes Delta, the row scales of Q and the fp16 copy of Q into the workspace; DQ and
- * DKDV read them from there, so a caller that runs them separately (for example on two
- * streams) must run DELTA first on the same workspace.  dK is formed from dS and Q in
- * fp16: each row of Q is divided by a power of two that puts its max |q| in [1, 2),
- * which copies every entry of at least 2^-14 times the row's max exactly, and dS is
- * scaled by the same power; the result stays finite while |dS| times the row's max |q|
- * stays below 2^15.  dQ is written by DQ, dK and dV by DKDV; no output is accumulated
- * into.
+ * writes Delta, the scales and fp16 copies of Q, dO and K and the launch-wide maxima into
+ * the workspace; DQ and DKDV read them from there, so a caller that runs them separately
+ * (for example on two streams) must run DELTA first on the same workspace.
+ * Precision: every product runs on MFMA with fp32 accumulation.  S, dP, dV and dK take
+ * fp16 operands: Q and dO rows and K (per launch in the dQ kernel, per 128-key block in
+ * the dK/dV kernel) and V (per 128-key block) are divided by powers of two that put their
+ * largest magnitude in [1, 2), which copies every bf16 value of at least 2^-14 of that
+ * largest magnitude exactly; P enters dV and dQ's dS and dK's dS enter their products
+ * rounded once to fp16 (11 significant bits), each scaled by a power of two chosen from
+ * launch-wide bounds (|dO_i| |v_j| + |Delta_i| for dS) so that it stays below 2^14.  The
+ * scales are undone exactly at the end.  A row whose dO is much smaller than the largest
+ * dO row of the launch (by more than about 2^10) contributes its smallest probabilities
+ * to dV at reduced (subnormal fp16) precision.  Inputs whose magnitudes lie within
+ * 2^-60 .. 2^60 keep every scale inside the fp32 range.
+ * dQ is written by DQ, dK and dV by DKDV; no output is accumulated into.
  * Supported: dtype BF16, D = 128.  All tensors bf16 except lse (fp32).  The plan must
  * hold both row and column lists at cowa_tile_sizes(COWA_OP_BWD).  workspace must be
  * at least cowa_workspace_size(COWA_OP_BWD) bytes, 256-byte aligned.
@@ -190,13 +207,16 @@ int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan,
  * WORKSPACE_TOO_SMALL, PLAN_MISMATCH, HIP. */
 enum { COWA_BWD_DELTA = 1, COWA_BWD_DQ = 2, COWA_BWD_DKDV = 4, COWA_BWD_ALL = 7 };
 int cowa_bwd(const cowa_problem* p, const cowa_plan_dev* plan,
-             const void* q, const void* k, const void* v, const void* o, const float* lse,
-             const void* dout, void* dq, void* dk, void* dv, int stages,
+             const void* q, const void* k, const void* v, const void* o, const void* o_lo,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv, int stages,
              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Decode: one new query token per sequence (p->Lq == 1) over a KV cache of p->Lk
  * positions that already holds the new token's K/V; the query sits at position Lk-1,
- * so the bottom-right distance is d = Lk - 1 - j, the same definition as the forward.
+ * so the bottom-right distance is d = Lk - 1 - j, the same definition as the forward
+ * (one distance for training, prefill and decoding: slinene.github.io ai-papers-daily
+ * page, method key point 2; each KV head reads only its window's blocks: same page,
+ * method key point 3).
  * Each KV head reads only its visible blocks.  q/o: [B, 1, Hq, D] bf16;
  * k_cache/v_cache: [B, Lk, Hkv, D] bf16; lse: [B, Hq] fp32 or NULL.
  * Supported: dtype BF16, D = 128.  workspace: cowa_workspace_size(COWA_OP_DECODE).

@@ -71,10 +71,11 @@ def _load():
                                         ctypes.POINTER(ctypes.c_size_t)]
     lib.cowa_workspace_size.restype = ctypes.c_int
     lib.cowa_fwd.argtypes = [ctypes.POINTER(cowa_problem), ctypes.POINTER(cowa_plan_dev),
-                             _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
+                             _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
     lib.cowa_fwd.restype = ctypes.c_int
     lib.cowa_bwd.argtypes = [ctypes.POINTER(cowa_problem), ctypes.POINTER(cowa_plan_dev),
-                             _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_int, _p, ctypes.c_size_t, _p]
+                             _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_int, _p, ctypes.c_size_t,
+                             _p]
     lib.cowa_bwd.restype = ctypes.c_int
     lib.cowa_decode.argtypes = [ctypes.POINTER(cowa_problem), ctypes.POINTER(cowa_plan_dev),
                                 _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]

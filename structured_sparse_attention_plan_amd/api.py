@@ -109,51 +109,74 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _check_tensor(name, t, shape, dtype):
-    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
-        raise ValueError(f"{name}: expected contiguous {dtype} device tensor of shape {tuple(shape)}, "
-                         f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} "
-                         f"device={t.device}")
+def _check_tensor(name, t, shape, dtype, device=None):
+    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda
+            or (device is not None and t.device != device)):
+        raise ValueError(f"{name}: expected contiguous {dtype} device tensor of shape {tuple(shape)}"
+                         f"{'' if device is None else ' on ' + str(device)}, got {t.dtype} "
+                         f"{tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}")
 
 
-def fwd(q, k, v, win, scale=None, plan=None, out=None, lse=None):
-    """Forward: q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] -> (o like q, lse [B,Hq,Lq] fp32)."""
+def _workspace(name, ws, nbytes, device):
+    """A caller's workspace: a contiguous uint8 tensor of at least nbytes on the device
+    (the library checks the size and the 256-byte alignment again)."""
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device != device or ws.numel() < nbytes:
+        raise ValueError(f"{name}: expected a contiguous uint8 tensor of at least {nbytes} bytes on "
+                         f"{device}, got {ws.dtype} of {ws.numel()} elements on {ws.device}")
+    return ws
+
+
+def fwd(q, k, v, win, scale=None, plan=None, out=None, lse=None, o_lo=None):
+    """Forward: q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] -> (o like q, lse [B,Hq,Lq] fp32).
+    o_lo (a tensor like q, bf16 only): filled with O's bf16 rounding residual, for bwd."""
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     scale = D ** -0.5 if scale is None else scale
     prob = problem(B, Lq, Lk, Hq, Hkv, D, q.dtype, scale, win)
     _check_tensor("q", q, (B, Lq, Hq, D), q.dtype)
-    _check_tensor("k", k, (B, Lk, Hkv, D), q.dtype)
-    _check_tensor("v", v, (B, Lk, Hkv, D), q.dtype)
+    _check_tensor("k", k, (B, Lk, Hkv, D), q.dtype, q.device)
+    _check_tensor("v", v, (B, Lk, Hkv, D), q.dtype, q.device)
     plan = build_plan("fwd", prob, q.device) if plan is None else plan
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor("out", out, (B, Lq, Hq, D), q.dtype, q.device)
+    _check_tensor("lse", lse, (B, Hq, Lq), torch.float32, q.device)
+    if o_lo is not None:
+        _check_tensor("o_lo", o_lo, (B, Lq, Hq, D), q.dtype, q.device)
     C.check("cowa_fwd", C.lib.cowa_fwd(ctypes.byref(prob), ctypes.byref(plan.struct), q.data_ptr(),
                                        k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                       None, 0, _stream(q.device)))
+                                       None if o_lo is None else o_lo.data_ptr(), None, 0,
+                                       _stream(q.device)))
     return out, lse
 
 
 def bwd(q, k, v, o, lse, dout, win, scale=None, plan=None, grads=None, workspace=None,
-        stages=C.COWA_BWD_ALL):
-    """Backward: -> (dq like q, dk like k, dv like v).  `stages` as in cowa_bwd."""
+        stages=C.COWA_BWD_ALL, o_lo=None):
+    """Backward: -> (dq like q, dk like k, dv like v).  `stages` as in cowa_bwd; o_lo is
+    the residual fwd wrote (optional)."""
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     scale = D ** -0.5 if scale is None else scale
     prob = problem(B, Lq, Lk, Hq, Hkv, D, q.dtype, scale, win)
     for name, t, shp in (("q", q, (B, Lq, Hq, D)), ("k", k, (B, Lk, Hkv, D)), ("v", v, (B, Lk, Hkv, D)),
                          ("o", o, (B, Lq, Hq, D)), ("dout", dout, (B, Lq, Hq, D))):
-        _check_tensor(name, t, shp, q.dtype)
-    _check_tensor("lse", lse, (B, Hq, Lq), torch.float32)
+        _check_tensor(name, t, shp, q.dtype, q.device)
+    _check_tensor("lse", lse, (B, Hq, Lq), torch.float32, q.device)
+    if o_lo is not None:
+        _check_tensor("o_lo", o_lo, (B, Lq, Hq, D), q.dtype, q.device)
     plan = build_plan("bwd", prob, q.device) if plan is None else plan
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
-    nbytes = workspace_size("bwd", prob)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check_tensor("dq", dq, (B, Lq, Hq, D), q.dtype, q.device)
+    _check_tensor("dk", dk, (B, Lk, Hkv, D), q.dtype, q.device)
+    _check_tensor("dv", dv, (B, Lk, Hkv, D), q.dtype, q.device)
+    workspace = _workspace("workspace", workspace, workspace_size("bwd", prob), q.device)
     C.check("cowa_bwd", C.lib.cowa_bwd(ctypes.byref(prob), ctypes.byref(plan.struct), q.data_ptr(),
-                                       k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                       k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       None if o_lo is None else o_lo.data_ptr(), lse.data_ptr(),
                                        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                        int(stages), workspace.data_ptr(), workspace.numel(),
                                        _stream(q.device)))
@@ -167,14 +190,14 @@ def decode(q, k_cache, v_cache, win, scale=None, plan=None, out=None, lse=None, 
     scale = D ** -0.5 if scale is None else scale
     prob = problem(B, Lq, Lk, Hq, Hkv, D, q.dtype, scale, win)
     _check_tensor("q", q, (B, 1, Hq, D), q.dtype)
-    _check_tensor("k_cache", k_cache, (B, Lk, Hkv, D), q.dtype)
-    _check_tensor("v_cache", v_cache, (B, Lk, Hkv, D), q.dtype)
+    _check_tensor("k_cache", k_cache, (B, Lk, Hkv, D), q.dtype, q.device)
+    _check_tensor("v_cache", v_cache, (B, Lk, Hkv, D), q.dtype, q.device)
     plan = build_plan("decode", prob, q.device) if plan is None else plan
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
-    nbytes = workspace_size("decode", prob)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check_tensor("out", out, (B, 1, Hq, D), q.dtype, q.device)
+    _check_tensor("lse", lse, (B, Hq), torch.float32, q.device)
+    workspace = _workspace("workspace", workspace, workspace_size("decode", prob), q.device)
     C.check("cowa_decode", C.lib.cowa_decode(ctypes.byref(prob), ctypes.byref(plan.struct),
                                              q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                              out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
@@ -191,17 +214,26 @@ def decode_varlen(q, k_cache, v_cache, seqlens, win, scale=None, out=None, lse=N
     scale = D ** -0.5 if scale is None else scale
     prob = problem(B, Lq, Lk, Hq, Hkv, D, q.dtype, scale, win)
     _check_tensor("q", q, (B, 1, Hq, D), q.dtype)
-    _check_tensor("k_cache", k_cache, (B, Lk, Hkv, D), q.dtype)
-    _check_tensor("v_cache", v_cache, (B, Lk, Hkv, D), q.dtype)
-    _check_tensor("seqlens", seqlens, (B,), torch.int32)
+    _check_tensor("k_cache", k_cache, (B, Lk, Hkv, D), q.dtype, q.device)
+    _check_tensor("v_cache", v_cache, (B, Lk, Hkv, D), q.dtype, q.device)
+    _check_tensor("seqlens", seqlens, (B,), torch.int32, q.device)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
-    nbytes = workspace_size("decode", prob)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check_tensor("out", out, (B, 1, Hq, D), q.dtype, q.device)
+    _check_tensor("lse", lse, (B, Hq), torch.float32, q.device)
+    workspace = _workspace("workspace", workspace, workspace_size("decode", prob), q.device)
     C.check("cowa_decode_varlen",
             C.lib.cowa_decode_varlen(ctypes.byref(prob), q.data_ptr(), k_cache.data_ptr(),
                                      v_cache.data_ptr(), seqlens.data_ptr(), out.data_ptr(),
                                      lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                      _stream(q.device)))
     return out, lse
+
+
+def fwd_bwd(q, k, v, dout, win, scale=None):
+    """Training step of the operator: forward keeping O's rounding residual, then the
+    backward from it -> (o, lse, dq, dk, dv)."""
+    o_lo = torch.empty_like(q)
+    o, lse = fwd(q, k, v, win, scale, o_lo=o_lo)
+    dq, dk, dv = bwd(q, k, v, o, lse, dout, win, scale, o_lo=o_lo)
+    return o, lse, dq, dk, dv

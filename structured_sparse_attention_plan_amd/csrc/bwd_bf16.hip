@@ -6,7 +6,7 @@
 // logsumexp:
 //   P = exp(scale q.k - LSE), Delta_i = dO_i . O_i, dP = dO V^T, dS = P (dP - Delta)
 //   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO
-// Three kernels, no atomics (deterministic):
+// Three kernels, deterministic (the only atomics take two maxima):
 //   delta  : Delta per (row, query head), and an fp16 copy of Q scaled per row by a
 //            power of two;
 //   dq     : one work item per (KV head, q-block of 128 / G tokens), walking the row list
@@ -45,39 +45,117 @@ __device__ __forceinline__ void pin_out(uint32_t& x) { asm volatile("" : "+v"(x)
 __device__ __forceinline__ void pin_out(float& x) { asm volatile("" : "+v"(x)); }
 
 // ------------------------------------------------------------------------ Delta
-// Per row (token, query head): Delta = dO . O, and the fp16 copy of q that the dK
-// product reads, q / 2^e with max |q| / 2^e in [1, 2) (2^e stored beside Delta).  Sixteen
-// lanes per row, 8 elements each.
+// Per row (token, query head): Delta = dO . O (with O's rounding residual when the forward
+// kept it), and the fp16 copies of q and dO that the products read, each row divided by
+// the power of two that puts its max |x| in [1, 2) (2^e for q, 2^f for dO; e is stored as
+// the scale 2^e and f as the exponent).  Sixteen lanes per row, 8 elements each.
+//
+// The same launch takes the launch-wide maxima the fp16 products need for their range
+// (kept as unsigned integers: the bit patterns of non-negative floats and biased
+// exponents order like the values), each atomic issued only when a wave's value exceeds
+// the recorded one, so few reach the one L2 line:
+//   [0] |dO_i| 2^e_i and [1] |Delta_i| 2^e_i (|.| the Euclidean norm over D): with |v_j|,
+//       |dS_ij| 2^e_i = P_ij |dO_i . v_j - Delta_i| 2^e_i <= |dO_i| 2^e_i |v_j| + |Delta_i| 2^e_i;
+//   [2] max f_i over rows with dO != 0 (the common scale of the dV product);
+//   [3] max |k| (the scale of the fp16 copy of K) and [4] max |v_j|^2, from extra work
+//       groups over the rows of K and V.
+// bwd_clear_kernel zeroes them first.
+__global__ __launch_bounds__(64) void bwd_clear_kernel(float* maxima) {
+  if (threadIdx.x < 8) maxima[threadIdx.x] = 0.f;
+}
+
+__device__ __forceinline__ void max_u32(unsigned* g, unsigned v) {
+  if (v > __atomic_load_n(g, __ATOMIC_RELAXED)) atomicMax(g, v);
+}
+
+// bf16 row chunk (8 values) -> fp16 bits of x / 2^e (exact while x / 2^e stays normal)
+__device__ __forceinline__ u32x4 f16_scaled(const u32x4& w, int e) {
+  u32x4 h;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    h[k] = pack_f16x2(__builtin_amdgcn_ldexpf(__uint_as_float(w[k] << 16), -e),
+                      __builtin_amdgcn_ldexpf(__uint_as_float(w[k] & 0xffff0000u), -e));
+  return h;
+}
+
+__device__ __forceinline__ float absmax8(const u32x4& w) {
+  float m = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[k] << 16)), fabsf(__uint_as_float(w[k] & 0xffff0000u))));
+  return m;
+}
+
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b, t, hq) flat
   const int li = threadIdx.x & 15;
   const int64_t nrows = (int64_t)a.B * a.Lq * a.Hq;
-  float acc = 0.f, qm = 0.f;
-  u32x4 qw = {0u, 0u, 0u, 0u};
+  const int64_t qgroups = (nrows + 15) / 16;
+  unsigned* g = (unsigned*)a.maxima;
+  if ((int64_t)blockIdx.x >= qgroups) {
+    // rows of K and V (b, j, h): max |k| and max |v_j|^2
+    const int64_t row = ((int64_t)blockIdx.x - qgroups) * 16 + (threadIdx.x >> 4);
+    float km = 0.f, vn = 0.f;
+    if (row < (int64_t)a.B * a.Lk * a.Hkv) {
+      const u32x4 kw = *(const u32x4*)((const __bf16*)a.k + row * D + 8 * li);
+      const u32x4 vw = *(const u32x4*)((const __bf16*)a.v + row * D + 8 * li);
+      km = absmax8(kw);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float v0 = __uint_as_float(vw[k] << 16), v1 = __uint_as_float(vw[k] & 0xffff0000u);
+        vn = fmaf(v0, v0, fmaf(v1, v1, vn));
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) vn += __shfl_xor(vn, m, 16);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      km = fmaxf(km, __shfl_xor(km, m));
+      vn = fmaxf(vn, __shfl_xor(vn, m));
+    }
+    if ((threadIdx.x & 63) == 0) {
+      max_u32(g + 3, __float_as_uint(km));
+      max_u32(g + 4, __float_as_uint(vn));
+    }
+    return;
+  }
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b, t, hq) flat
+  float acc = 0.f, qm = 0.f, dm = 0.f, dn = 0.f;
+  u32x4 qw = {0u, 0u, 0u, 0u}, dw = {0u, 0u, 0u, 0u};
   if (row < nrows) {
     const u32x4 ow = *(const u32x4*)((const __bf16*)a.o + row * D + 8 * li);
-    const u32x4 dw = *(const u32x4*)((const __bf16*)a.dout + row * D + 8 * li);
+    dw = *(const u32x4*)((const __bf16*)a.dout + row * D + 8 * li);
     qw = *(const u32x4*)((const __bf16*)a.q + row * D + 8 * li);
+    u32x4 lw = {0u, 0u, 0u, 0u};
+    if (a.o_lo) lw = *(const u32x4*)((const __bf16*)a.o_lo + row * D + 8 * li);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      acc = fmaf(__uint_as_float(ow[k] << 16), __uint_as_float(dw[k] << 16), acc);
-      acc = fmaf(__uint_as_float(ow[k] & 0xffff0000u), __uint_as_float(dw[k] & 0xffff0000u), acc);
-      qm = fmaxf(qm, fmaxf(fabsf(__uint_as_float(qw[k] << 16)), fabsf(__uint_as_float(qw[k] & 0xffff0000u))));
+      const float d0 = __uint_as_float(dw[k] << 16), d1 = __uint_as_float(dw[k] & 0xffff0000u);
+      const float o0 = __uint_as_float(ow[k] << 16) + __uint_as_float(lw[k] << 16);
+      const float o1 = __uint_as_float(ow[k] & 0xffff0000u) + __uint_as_float(lw[k] & 0xffff0000u);
+      acc = fmaf(o0, d0, acc);
+      acc = fmaf(o1, d1, acc);
+      dn = fmaf(d0, d0, fmaf(d1, d1, dn));
     }
+    qm = absmax8(qw);
+    dm = absmax8(dw);
   }
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) {
     acc += __shfl_xor(acc, m, 16);
+    dn += __shfl_xor(dn, m, 16);
     qm = fmaxf(qm, __shfl_xor(qm, m, 16));
+    dm = fmaxf(dm, __shfl_xor(dm, m, 16));
   }
+  const int qe = pow2_exponent(qm);
+  const int fe = pow2_exponent(dm);
+  float bn = 0.f, bd = 0.f;  // |dO| 2^e, |Delta| 2^e of this lane's row
+  unsigned fb = 0u;          // f + kExpBias of a row with dO != 0, else 0
   if (row < nrows) {
-    const int qe = pow2_exponent(qm);
-    u32x4 hw;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      hw[k] = pack_f16x2(__builtin_amdgcn_ldexpf(__uint_as_float(qw[k] << 16), -qe),
-                         __builtin_amdgcn_ldexpf(__uint_as_float(qw[k] & 0xffff0000u), -qe));
-    *(u32x4*)((uint16_t*)a.q16 + row * D + 8 * li) = hw;
+    bn = __builtin_amdgcn_ldexpf(sqrtf(dn), qe);
+    bd = __builtin_amdgcn_ldexpf(fabsf(acc), qe);
+    fb = dm > 0.f ? (unsigned)(fe + kExpBias) : 0u;
+    *(u32x4*)((uint16_t*)a.q16 + row * D + 8 * li) = f16_scaled(qw, qe);
+    *(u32x4*)((uint16_t*)a.do16 + row * D + 8 * li) = f16_scaled(dw, fe);
     if (li == 0) {
       const int hq = (int)(row % a.Hq);
       const int64_t bt = row / a.Hq;
@@ -86,8 +164,31 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
       const int64_t o = ((int64_t)b * a.Hq + hq) * a.Lq + t;
       a.delta[o] = acc;
       a.qscale[o] = __builtin_amdgcn_ldexpf(1.f, qe);
+      a.doexp[o] = (float)fe;
     }
   }
+#pragma unroll
+  for (int m = 16; m < 64; m <<= 1) {
+    bn = fmaxf(bn, __shfl_xor(bn, m));
+    bd = fmaxf(bd, __shfl_xor(bd, m));
+    fb = max(fb, (unsigned)__shfl_xor((int)fb, m));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    max_u32(g, __float_as_uint(bn));
+    max_u32(g + 1, __float_as_uint(bd));
+    max_u32(g + 2, fb);
+  }
+}
+
+// The fp16 copy of K read by the dQ kernel: K / 2^gK with max |k| / 2^gK in [1, 2) over
+// the launch (one scale, so the dQ product needs no per-key factor).
+__global__ __launch_bounds__(256) void bwd_k16_kernel(BwdArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int li = threadIdx.x & 15;
+  if (row >= (int64_t)a.B * a.Lk * a.Hkv) return;
+  const int ge = pow2_exponent(a.maxima[3]);
+  const u32x4 kw = *(const u32x4*)((const __bf16*)a.k + row * D + 8 * li);
+  *(u32x4*)((uint16_t*)a.k16 + row * D + 8 * li) = f16_scaled(kw, ge);
 }
 
 template <int V>
@@ -158,8 +259,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   const int off = a.Lk - a.Lq;
   const HeadBand band = head_band(a.win, h);
 
-  const __bf16* Q = (const __bf16*)a.q;
-  const __bf16* K = (const __bf16*)a.k;
+  const uint16_t* Q16 = (const uint16_t*)a.q16;
+  const uint16_t* K16 = (const uint16_t*)a.k16;
   const __bf16* V = (const __bf16*)a.v;
   const __bf16* dO = (const __bf16*)a.dout;
 
@@ -184,20 +285,47 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   const int hq = h * G + (r - rt * G);
   const bool rvalid = (rt < Bq) && (t < a.Lq);
   const int p = t + off;
-  float lse2 = INFINITY, dlt = 0.f;
+  // S = K16 Q16^T runs in fp16 on the scaled copies (K / 2^gK, q / 2^e_r), so the lane's
+  // exp2 factor is crow = scale log2(e) 2^(gK + e_r).  dS enters the dQ product in fp16
+  // as dS 2^s_r, with s_r chosen so that the row's bound |dO_r| max|v| + |Delta_r| on |dS|
+  // lands below 2^14 (four times inside the fp16 range): dS16 = P (dP fq - tq) with
+  // fq = 2^s_r and tq = Delta_r 2^s_r, and dQ = scale 2^(gK - s_r) dQ16.
+  const int gk = pow2_exponent(a.maxima[3]);
+  float lse2 = INFINITY, dlt = 0.f, crow = __builtin_amdgcn_ldexpf(a.scale_log2, gk), fq = 1.f, tq = 0.f;
+  float dq_out = 0.f;
   bf16x8 qf[8], df[8];
   if (rvalid) {
-    lse2 = a.lse[((int64_t)b * a.Hq + hq) * a.Lq + t] * kLog2e;
-    dlt = a.delta[((int64_t)b * a.Hq + hq) * a.Lq + t];
+    const int64_t ri = ((int64_t)b * a.Hq + hq) * a.Lq + t;
+    lse2 = a.lse[ri] * kLog2e;
+    dlt = a.delta[ri];
+    crow *= a.qscale[ri];
     const int64_t ro = (((int64_t)b * a.Lq + t) * a.Hq + hq) * D + 8 * h2;
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
-      qf[dd] = load16(Q + ro + 16 * dd);
+      qf[dd] = load16(Q16 + ro + 16 * dd);
       df[dd] = load16(dO + ro + 16 * dd);
     }
   } else {
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) qf[dd] = df[dd] = zero_bf16x8();
+  }
+  {
+    float dn = 0.f;  // |dO_r|^2: the two lane halves hold 64 dimensions each
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const u32x4 w = __builtin_bit_cast(u32x4, df[dd]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float d0 = __uint_as_float(w[q] << 16), d1 = __uint_as_float(w[q] & 0xffff0000u);
+        dn = fmaf(d0, d0, fmaf(d1, d1, dn));
+      }
+    }
+    dn += __shfl_xor(dn, 32);
+    const float bound = sqrtf(dn) * sqrtf(a.maxima[4]) + fabsf(dlt);
+    const int se = bound > 0.f ? min(100, max(-100, 13 - pow2_exponent(bound))) : 0;
+    fq = __builtin_amdgcn_ldexpf(1.f, se);
+    tq = dlt * fq;
+    dq_out = __builtin_amdgcn_ldexpf(a.scale, gk - se);
   }
   // held in AGPRs as the B operands of the S, dP products: the VGPRs hold those products'
   // accumulators
@@ -241,7 +369,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   __amdgpu_buffer_rsrc_t rk, rv;
   // the batch's K / V base and byte count are formed once; per tile only the offset
   const int64_t kv_bytes = (int64_t)a.Lk * HkvD * 2;
-  const char* const kbase = (const char*)(K + (int64_t)b * a.Lk * HkvD);
+  const char* const kbase = (const char*)(K16 + (int64_t)b * a.Lk * HkvD);
   const char* const vbase = (const char*)(V + (int64_t)b * a.Lk * HkvD);
   auto prepare_copy = [&](int ent, int tt, bool real) {
     const int64_t off = (int64_t)tile_j0(ent, tt) * (HkvD * 2);
@@ -287,11 +415,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     f32x16 sA[2], dA[2], sB[2], dB[2];  // S^T, dP^T of two consecutive tiles (2 key blocks)
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
-      mfma_bf16_va0(sA[k2], load16(sK0 + ofs_a(k2, 0)), qf[0]);
+      mfma_f16_va0(sA[k2], load16(sK0 + ofs_a(k2, 0)), qf[0]);
       mfma_bf16_va0(dA[k2], load16(sV0 + ofs_a(k2, 0)), df[0]);
 #pragma unroll
       for (int dd = 1; dd < 8; ++dd) {
-        mfma_bf16_va(sA[k2], load16(sK0 + ofs_a(k2, dd)), qf[dd]);
+        mfma_f16_va(sA[k2], load16(sK0 + ofs_a(k2, dd)), qf[dd]);
         mfma_bf16_va(dA[k2], load16(sV0 + ofs_a(k2, dd)), df[dd]);
       }
     }
@@ -343,7 +471,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
         if (x < 16) {
           const int k2 = x >> 3, hf = (x >> 2) & 1, db = x & 3;
           const u32x4 w = {dsp[k2][hf][0], dsp[k2][hf][1], dsp[k2][hf][2], dsp[k2][hf][3]};
-          acc[db] = mfma32x32x16(opA[x], __builtin_bit_cast(bf16x8, w), acc[db]);
+          acc[db] = mfma32x32x16_f16(opA[x], __builtin_bit_cast(bf16x8, w), acc[db]);
         } else {
           // accumulators in VGPRs, each chain starting from zero (dd = 0)
           const int y = x - 16, k2 = y & 1, dd = y >> 2;
@@ -351,8 +479,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
             if (dd == 0) mfma_bf16_va0(nd[k2], opA[x], df[0]);
             else mfma_bf16_va(nd[k2], opA[x], df[dd]);
           } else {
-            if (dd == 0) mfma_bf16_va0(ns[k2], opA[x], qf[0]);
-            else mfma_bf16_va(ns[k2], opA[x], qf[dd]);
+            if (dd == 0) mfma_f16_va0(ns[k2], opA[x], qf[0]);
+            else mfma_f16_va(ns[k2], opA[x], qf[dd]);
           }
         }
         if (x >= 4 && x < 12) copy(x - 4, kd, vd);
@@ -361,27 +489,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
         // are packed to bf16 in steps 32..47.  Inputs are taken (pin) one step before use
         // and results fenced (pin_out) one step after they are made: a read right at a pin
         // or a fence right after an exp costs a wait state each.
-        if (x < 32) pr[x >> 4][x & 15] = __builtin_amdgcn_exp2f(fmaf(csv[x & 1], a.scale_log2, -lse2));
+        if (x < 32) pr[x >> 4][x & 15] = __builtin_amdgcn_exp2f(fmaf(csv[x & 1], crow, -lse2));
         if (x + 1 < 32) csv[(x + 1) & 1] = pin(cs[(x + 1) >> 4][(x + 1) & 15]);
         if (x >= 1 && x <= 32) pin_out(pr[(x - 1) >> 4][(x - 1) & 15]);
         if (x >= 4 && x < 36) {
           const int e = x - 4, k2 = e >> 4, i = e & 15;
-          dsv[k2][i] = pr[k2][i] * (cdv[e & 1] - dlt);
+          dsv[k2][i] = pr[k2][i] * fmaf(cdv[e & 1], fq, -tq);
         }
         if (x >= 3 && x < 35) {
           const int e = x - 3;
           cdv[e & 1] = pin(cd[e >> 4][e & 15]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // dS pair q (elements 2 q, 2 q + 1) packed to bf16 at step 2 q + 7, after this
+        // dS pair q (elements 2 q, 2 q + 1) packed to fp16 at step 2 q + 7, after this
         // step's own VALU work (its second element was fenced at the end of the previous
         // step: a read right after the fence would cost a wait state), and fenced in turn
         // a step later; pair q sits in word q % 4 of half (q / 4) % 2 of block q / 8
         if (x >= 7 && x <= 37 && (x & 1)) {
           const int q = (x - 7) >> 1, k2 = q >> 3, hf = (q >> 2) & 1, w = q & 3;
-          const float x0 = dsv[k2][2 * (q & 7)], x1 = dsv[k2][2 * (q & 7) + 1];
-          const bf16x2 v = {(__bf16)x0, (__bf16)x1};
-          npk[k2][hf][w] = __builtin_bit_cast(uint32_t, v);
+          npk[k2][hf][w] = pack_f16x2(dsv[k2][2 * (q & 7)], dsv[k2][2 * (q & 7) + 1]);
         }
         if (x >= 8 && x <= 38 && (x & 1) == 0) {
           const int q = (x - 8) >> 1;
@@ -427,7 +553,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
       const int k2 = x >> 3, hf = (x >> 2) & 1, db = x & 3;
       const bf16x8 ka = join(lds_read_tr4(kl + ofs_t(k2, hf, 0, db)), lds_read_tr4(kl + ofs_t(k2, hf, 1, db)));
       const u32x4 w = {dsp[k2][hf][0], dsp[k2][hf][1], dsp[k2][hf][2], dsp[k2][hf][3]};
-      acc[db] = mfma32x32x16(ka, __builtin_bit_cast(bf16x8, w), acc[db]);
+      acc[db] = mfma32x32x16_f16(ka, __builtin_bit_cast(bf16x8, w), acc[db]);
     }
   }
 
@@ -437,8 +563,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const bf16x4 v = to_bf16x4(acc[db][4 * q4] * a.scale, acc[db][4 * q4 + 1] * a.scale,
-                                   acc[db][4 * q4 + 2] * a.scale, acc[db][4 * q4 + 3] * a.scale);
+        const bf16x4 v = to_bf16x4(acc[db][4 * q4] * dq_out, acc[db][4 * q4 + 1] * dq_out,
+                                   acc[db][4 * q4 + 2] * dq_out, acc[db][4 * q4 + 3] * dq_out);
         *(u32x2*)(dq + 32 * db + 8 * q4) = __builtin_bit_cast(u32x2, v);
       }
   }
@@ -462,12 +588,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 //   P = exp2(S16 c_r - LSE_r log2 e)   with c_r = scale log2(e) 2^(e_r + e_K),
 //   dS16 = 2^e_r dS = P (2^e_r dP - 2^e_r Delta_r),   so dS16^T Q16 = dS^T Q.
 constexpr int QTILE = ROWS * D;  // one q-block of Q (or dO) in LDS
-
-// (x0, x1) -> packed bf16 pair, round to nearest even.
-__device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
-  const bf16x2 h = {(__bf16)x0, (__bf16)x1};
-  return __builtin_bit_cast(uint32_t, h);
-}
 
 // bf16 x -> fp16 bits of x / 2^e (exact while |x| / 2^e is in the fp16 normal range).
 __device__ __forceinline__ bf16x8 bf16_to_f16_scaled(const bf16x8& x, int e) {
@@ -493,6 +613,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sLT1[4 * ROWS];
   __shared__ int sRt[ROWS];  // row -> token in the q-block
   __shared__ float sKmax[4];  // max |k| of each wave's keys
+  __shared__ float sVmax[4];  // max over each wave's keys of |v_j|^2
+  __shared__ float sVabs[4];  // max |v| of each wave's keys
   auto tiles = [&](auto bufc) -> __bf16* {
     if constexpr (decltype(bufc)::value == 0) return sQD0;
     else return sQD1;
@@ -518,7 +640,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const uint16_t* Q16 = (const uint16_t*)a.q16;
   const __bf16* K = (const __bf16*)a.k;
   const __bf16* V = (const __bf16*)a.v;
-  const __bf16* dO = (const __bf16*)a.dout;
+  const uint16_t* dO16 = (const uint16_t*)a.do16;
 
   if (tid < ROWS) sRt[tid] = tid / G;
   // Rows of the last q-block past Lq are outside the copies' range: their LDS keeps what
@@ -588,13 +710,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // loaded values are only touched when stored to LDS (after the wait that precedes the
   // q-block's first use), so the loads do not stall the wave when they are issued.
   const int my_rt = tid / G, my_g = tid - my_rt * G;
-  float plse = 0.f, pdel = 0.f, pqs = 1.f, ck = a.scale_log2;
+  float plse = 0.f, pdel = 0.f, pqs = 1.f, pdx = 0.f, ck = a.scale_log2;
+  // dS range scale of this item (2^sc, see below) and the dK output factor scale 2^-sc;
+  // the exponent eV of the item's fp16 V; the dV product's common exponent F
+  float dsc = 1.f, dk_out = a.scale;
+  int ev = 0;
+  const unsigned fbias = ((const unsigned*)a.maxima)[2];
+  const int fcommon = fbias ? (int)fbias - kExpBias : 0;
   bool pvalid = false;
   // LSE, Delta and Q row scales of this KV head's G query heads, [G, Lq] each
   const int64_t lt_base = ((int64_t)b * a.Hq + h * G) * a.Lq;
   const __amdgpu_buffer_rsrc_t r_lse = make_rsrc(a.lse + lt_base, (int64_t)G * a.Lq * 4);
   const __amdgpu_buffer_rsrc_t r_del = make_rsrc(a.delta + lt_base, (int64_t)G * a.Lq * 4);
   const __amdgpu_buffer_rsrc_t r_qs = make_rsrc(a.qscale + lt_base, (int64_t)G * a.Lq * 4);
+  const __amdgpu_buffer_rsrc_t r_dx = make_rsrc(a.doexp + lt_base, (int64_t)G * a.Lq * 4);
 
   const int e0 = load_uniform(a.col_ptr, item);
   const int n_ent = load_uniform(a.col_ptr, item + 1) - e0;
@@ -607,7 +736,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __amdgpu_buffer_rsrc_t rq_n, rd_n;
   const int64_t qd_bytes = (int64_t)a.Lq * HqD * 2;
   const char* const qbase = (const char*)(Q16 + (int64_t)b * a.Lq * HqD);
-  const char* const dobase = (const char*)(dO + (int64_t)b * a.Lq * HqD);
+  const char* const dobase = (const char*)(dO16 + (int64_t)b * a.Lq * HqD);
   auto prepare_entry = [&](int qb, bool real) {
     const int t0 = qb * Bq;
     const int64_t off = (int64_t)t0 * (HqD * 2);
@@ -620,6 +749,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       plse = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_lse, vo, 0, 0));
       pdel = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_del, vo, 0, 0));
       pqs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_qs, vo, 0, 0));
+      pdx = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dx, vo, 0, 0));
     }
   };
   auto copy = [&](int i, auto bufc) {
@@ -629,13 +759,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // Rows with no token or no visible key: LSE +inf (P = 0), c_r > 0 (so that a masked
   // S = -inf still gives P = 0), and 0 for the dS scale and Delta.  ck = scale log2(e)
   // 2^e_K.
+  //
+  // The dV and dP products take dO in fp16 (row r divided by 2^f_r, f_r from doexp) and V
+  // in fp16 (divided by 2^eV per item), so dP16 = dP 2^-(f_r + eV), and P enters dV as
+  // P16 = P 2^e_r' with e_r' = min(f_r - F, 0) (F the largest f_r: P16 <= 1), which the
+  // exp2 takes through its LSE term.  Then dV = 2^F sum P16 dO16, and
+  //   dS 2^(e_r + sc) = P16 (dP16 2^(f_r + eV - e_r') - Delta 2^-e_r') 2^(e_r + sc),
+  // so the two dS constants become f = 2^(e_r + sc + f_r + eV - e_r'), t = Delta 2^(e_r + sc - e_r').
   auto store_lse = [&](auto bufc) {
     if (tid < ROWS) {
       float* lt = lts(bufc);
-      lt[tid] = (pvalid && plse != -INFINITY) ? plse * kLog2e : INFINITY;
+      const int fr = (int)pdx;
+      const int er = min(fr - fcommon, 0);
+      lt[tid] = (pvalid && plse != -INFINITY) ? plse * kLog2e - (float)er : INFINITY;
       lt[ROWS + tid] = pvalid ? ck * pqs : ck;
-      lt[2 * ROWS + tid] = pvalid ? pqs : 0.f;
-      lt[3 * ROWS + tid] = pvalid ? pdel * pqs : 0.f;
+      lt[2 * ROWS + tid] = pvalid ? __builtin_amdgcn_ldexpf(pqs * dsc, fr + ev - er) : 0.f;
+      lt[3 * ROWS + tid] = pvalid ? __builtin_amdgcn_ldexpf(pdel * (pqs * dsc), -er) : 0.f;
     }
   };
   // boundary q-block: the window predicate per element (S = -inf where hidden)
@@ -696,26 +835,58 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // K of the work item in fp16, divided by 2^e_K (max |k| over its 128 keys then in
     // [1, 2)): each wave's max goes through LDS
     {
-      float km = 0.f;
+      float km = 0.f, vm = 0.f;
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
-        const u32x4 w = __builtin_bit_cast(u32x4, kf[dd]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          km = fmaxf(km, fmaxf(fabsf(__uint_as_float(w[q] << 16)), fabsf(__uint_as_float(w[q] & 0xffff0000u))));
+        km = fmaxf(km, absmax8(__builtin_bit_cast(u32x4, kf[dd])));
+        vm = fmaxf(vm, absmax8(__builtin_bit_cast(u32x4, vf[dd])));
       }
 #pragma unroll
-      for (int m = 1; m < 64; m <<= 1) km = fmaxf(km, __shfl_xor(km, m));
-      if (lane == 0) sKmax[wave] = km;
+      for (int m = 1; m < 64; m <<= 1) {
+        km = fmaxf(km, __shfl_xor(km, m));
+        vm = fmaxf(vm, __shfl_xor(vm, m));
+      }
+      if (lane == 0) {
+        sKmax[wave] = km;
+        sVabs[wave] = vm;
+      }
+      // |v_j|^2 of this lane's key (the two lane halves hold 64 dimensions each), max
+      // over the wave's 32 keys
+      float vn = 0.f;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const u32x4 w = __builtin_bit_cast(u32x4, vf[dd]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float v0 = __uint_as_float(w[q] << 16), v1 = __uint_as_float(w[q] & 0xffff0000u);
+          vn = fmaf(v0, v0, fmaf(v1, v1, vn));
+        }
+      }
+      vn += __shfl_xor(vn, 32);
+#pragma unroll
+      for (int m = 1; m < 32; m <<= 1) vn = fmaxf(vn, __shfl_xor(vn, m));
+      if (lane == 0) sVmax[wave] = vn;
     }
     wait_loads_and_barrier();
     {
       const int ek = pow2_exponent(fmaxf(fmaxf(sKmax[0], sKmax[1]), fmaxf(sKmax[2], sKmax[3])));
       ck = a.scale_log2 * __builtin_amdgcn_ldexpf(1.f, ek);
+      ev = pow2_exponent(fmaxf(fmaxf(sVabs[0], sVabs[1]), fmaxf(sVabs[2], sVabs[3])));
+      // dS enters the dK product as dS 2^e_r 2^sc in fp16, with 2^sc chosen per item so
+      // that the bound |dO_i| 2^e_r |v|max + |Delta_i| 2^e_r (launch-wide row maxima from
+      // the Delta kernel, |v|max over this item's keys) is below 2^14, four times inside
+      // the fp16 range; dK is multiplied by 2^-sc at the end.  The scale is a power of
+      // two, so it changes no value beyond the fp16 rounding it protects.
+      const float vmax = sqrtf(fmaxf(fmaxf(sVmax[0], sVmax[1]), fmaxf(sVmax[2], sVmax[3])));
+      const float bound = a.maxima[0] * vmax + a.maxima[1];
+      const int sc = bound > 0.f ? min(100, max(-100, 13 - pow2_exponent(bound))) : 0;
+      dsc = __builtin_amdgcn_ldexpf(1.f, sc);
+      dk_out = a.scale * __builtin_amdgcn_ldexpf(1.f, -sc);
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
         kf[dd] = bf16_to_f16_scaled(kf[dd], ek);
-        asm volatile("" : "+a"(kf[dd]));
+        vf[dd] = bf16_to_f16_scaled(vf[dd], ev);
+        asm volatile("" : "+a"(kf[dd]), "+a"(vf[dd]));
       }
     }
     store_lse(IC<0>{});
@@ -739,7 +910,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
         s = mfma32x32x16_f16(load16(sQD0 + ofs_a(dd)), kf[dd], s);
-        wA.dp = mfma32x32x16(load16(sQD0 + QTILE + ofs_a(dd)), vf[dd], wA.dp);
+        wA.dp = mfma32x32x16_f16(load16(sQD0 + QTILE + ofs_a(dd)), vf[dd], wA.dp);
       }
       if (ent_c & 1) mask(s, 0, ent_c >> 1);
       const float* lt = sLT0 + 4 * h2;
@@ -827,8 +998,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int x = 0; x < 16; ++x) {
         const int dd = x >> 1;
         if (x == 0) mfma_f16_va0(sn, qa[0], kf[0]);
-        else if (x == 1) mfma_bf16_va0(nxt.dp, da[0], vf[0]);
-        else if (x & 1) mfma_bf16_va(nxt.dp, da[dd], vf[dd]);
+        else if (x == 1) mfma_f16_va0(nxt.dp, da[0], vf[0]);
+        else if (x & 1) mfma_f16_va(nxt.dp, da[dd], vf[dd]);
         else mfma_f16_va(sn, qa[dd], kf[dd]);
         if ((x & 1) && dd + 4 < 8) {
           qa[dd + 4] = load16(t1 + ofs_a(dd + 4));
@@ -850,7 +1021,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         // ahead of the slot's dS
         if (x & 1) {
           const int q = x >> 1;
-          wpa[q >> 2][q & 3] = pack_bf16x2(prv[(x - 1) % 3], prv[x % 3]);
+          wpa[q >> 2][q & 3] = pack_f16x2(prv[(x - 1) % 3], prv[x % 3]);
         } else if (x >= 2) {
           const int q = (x - 2) >> 1;
           pin_out(wpa[q >> 2][q & 3]);
@@ -895,7 +1066,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         // MFMA x: half hf = x / 8; dV (x even) and dK (x odd) for db = (x % 8) / 2
         const int hf = x >> 3, db = (x & 7) >> 1;
         if (x & 1) accK[db] = mfma32x32x16_f16(sa[hf], qt[hf][db], accK[db]);
-        else accV[db] = mfma32x32x16(pa[hf], dt[hf][db], accV[db]);
+        else accV[db] = mfma32x32x16_f16(pa[hf], dt[hf][db], accV[db]);
         // transposed operands of half 1, each read right after its half-0 register is last
         // used: dO^T (db) after MFMA 2 db, read at 2 db + 1; Q^T (db) after MFMA 2 db + 1,
         // read at 2 db + 2
@@ -956,6 +1127,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0f70);
   }
 
+  const float dv_out = __builtin_amdgcn_ldexpf(1.f, fcommon);
   // element i of accK[db] / accV[db]: key 32 wave + 8 (i / 4) + 4 h2 + i % 4, dim 32 db + n
   __bf16* dK = (__bf16*)a.dk;
   __bf16* dV = (__bf16*)a.dv;
@@ -966,8 +1138,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const int jj = kb * BK + wave * 32 + 8 * (i >> 2) + 4 * h2 + (i & 3);
       if (jj < a.Lk) {
         const int64_t o = (((int64_t)b * a.Lk + jj) * a.Hkv + h) * D + 32 * db + n;
-        dK[o] = (__bf16)(accK[db][i] * a.scale);
-        dV[o] = (__bf16)accV[db][i];
+        dK[o] = (__bf16)(accK[db][i] * dk_out);
+        dV[o] = (__bf16)(accV[db][i] * dv_out);
       }
     }
 }
@@ -978,7 +1150,13 @@ hipError_t launch_bwd_bf16_d128(const BwdArgs& a, int stages, hipStream_t s) {
   hipError_t err = hipSuccess;
   if (stages & COWA_BWD_DELTA) {
     const int64_t nrows = (int64_t)a.B * a.Lq * a.Hq;
-    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, s, a);
+    const int64_t nkv = (int64_t)a.B * a.Lk * a.Hkv;
+    hipLaunchKernelGGL(bwd_clear_kernel, dim3(1), dim3(64), 0, s, a.maxima);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((nrows + 15) / 16 + (nkv + 15) / 16)), dim3(256),
+                       0, s, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(bwd_k16_kernel, dim3((unsigned)((nkv + 15) / 16)), dim3(256), 0, s, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (stages & COWA_BWD_DQ) {

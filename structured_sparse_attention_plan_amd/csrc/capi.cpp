@@ -108,6 +108,30 @@ int decode_splits(const cowa_problem* p) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? COWA_OK : COWA_ERR_HIP; }
 
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Byte offsets of the backward workspace: three fp32 arrays per (query head, row) (Delta,
+// the row scales of Q, the row exponents of dO), 256 bytes of launch-wide maxima, then
+// the fp16 copies of Q and dO ([B, Lq, Hq, D]) and of K ([B, Lk, Hkv, D]).
+struct BwdLayout {
+  size_t delta, qscale, doexp, maxima, q16, do16, k16, total;
+};
+BwdLayout bwd_layout(const cowa_problem* p) {
+  const size_t rows = (size_t)p->B * p->Hq * p->Lq;
+  const size_t rowf = round256(rows * sizeof(float));
+  const size_t rowh = round256(rows * p->D * 2);
+  BwdLayout l;
+  l.delta = 0;
+  l.qscale = rowf;
+  l.doexp = 2 * rowf;
+  l.maxima = 3 * rowf;
+  l.q16 = l.maxima + 256;
+  l.do16 = l.q16 + rowh;
+  l.k16 = l.do16 + rowh;
+  l.total = l.k16 + round256((size_t)p->B * p->Lk * p->Hkv * p->D * 2);
+  return l;
+}
+
 }  // namespace
 
 extern "C" const char* cowa_status_string(int status) {
@@ -142,11 +166,9 @@ extern "C" int cowa_workspace_size(int op, const cowa_problem* p, size_t* bytes)
     case COWA_OP_FWD:
       *bytes = 0;
       break;
-    case COWA_OP_BWD: {  // Delta, the row scales of Q and the fp16 copy of Q
-      const size_t rows = (size_t)p->B * p->Hq * p->Lq;
-      *bytes = 2 * ((rows * sizeof(float) + 255) / 256 * 256) + rows * p->D * 2;
+    case COWA_OP_BWD:
+      *bytes = bwd_layout(p).total;
       break;
-    }
     default: {
       const size_t rows = (size_t)p->B * p->Hq * decode_splits(p);
       const size_t part = (rows * p->D * sizeof(float) + 255) / 256 * 256;
@@ -157,8 +179,8 @@ extern "C" int cowa_workspace_size(int op, const cowa_problem* p, size_t* bytes)
 }
 
 extern "C" int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan, const void* q, const void* k,
-                        const void* v, void* o, float* lse, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        const void* v, void* o, float* lse, void* o_lo, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   int st = check_problem(p);
@@ -166,6 +188,7 @@ extern "C" int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan, const 
   st = check_op_support(COWA_OP_FWD, p);
   if (st != COWA_OK) return st;
   if (!q || !k || !v || !o || !lse) return COWA_ERR_INVALID_ARG;
+  if (o_lo && p->dtype != COWA_DTYPE_BF16) return COWA_ERR_INVALID_ARG;
   st = check_plan(COWA_OP_FWD, p, plan, false);
   if (st != COWA_OK) return st;
 
@@ -174,6 +197,7 @@ extern "C" int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan, const 
   a.k = k;
   a.v = v;
   a.o = o;
+  a.o_lo = o_lo;
   a.lse = lse;
   a.row_ptr = plan->row_ptr;
   a.row_ent = plan->row_ent;
@@ -198,9 +222,9 @@ extern "C" int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan, const 
 }
 
 extern "C" int cowa_bwd(const cowa_problem* p, const cowa_plan_dev* plan, const void* q, const void* k,
-                        const void* v, const void* o, const float* lse, const void* dout, void* dq,
-                        void* dk, void* dv, int stages, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        const void* v, const void* o, const void* o_lo, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, int stages, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   int st = check_problem(p);
   if (st != COWA_OK) return st;
   st = check_op_support(COWA_OP_BWD, p);
@@ -219,15 +243,21 @@ extern "C" int cowa_bwd(const cowa_problem* p, const cowa_plan_dev* plan, const 
   a.k = k;
   a.v = v;
   a.o = o;
+  a.o_lo = o_lo;
   a.lse = lse;
   a.dout = dout;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  const size_t row_bytes = ((size_t)p->B * p->Hq * p->Lq * sizeof(float) + 255) / 256 * 256;
-  a.delta = (float*)workspace;
-  a.qscale = (float*)((char*)workspace + row_bytes);
-  a.q16 = (char*)workspace + 2 * row_bytes;
+  const BwdLayout wl = bwd_layout(p);
+  char* const ws = (char*)workspace;
+  a.delta = (float*)(ws + wl.delta);
+  a.qscale = (float*)(ws + wl.qscale);
+  a.doexp = (float*)(ws + wl.doexp);
+  a.maxima = (float*)(ws + wl.maxima);
+  a.q16 = ws + wl.q16;
+  a.do16 = ws + wl.do16;
+  a.k16 = ws + wl.k16;
   a.row_ptr = plan->row_ptr;
   a.row_ent = plan->row_ent;
   a.row_order = plan->row_order;

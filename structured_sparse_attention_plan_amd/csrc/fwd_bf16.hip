@@ -34,7 +34,9 @@
 // bytes with the 16-byte chunks XOR-swizzled by a function of the row, so both the
 // row-wise operand reads and the transposed V reads are free of bank conflicts, and the
 // addresses of one lane differ only in the XOR of the chunk bits.
-// Output: O / l in bf16 and LSE = ln 2 * (m + log2 l) in fp32.
+// Output: O / l in bf16 and LSE = ln 2 * (m + log2 l) in fp32; optionally the part of
+// the fp32 O that the bf16 rounding drops (O - bf16(O), rounded to bf16), from which the
+// backward forms Delta = dO . O to about 16 significant bits.
 //
 // MFMA lane layouts of v_mfma_f32_32x32x16_bf16 (n = lane % 32, h2 = lane / 32):
 //   A (32 x 16): A[n][8 h2 + e]   B (16 x 32): B[8 h2 + e][n]
@@ -564,14 +566,22 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     float lt = l[c] + __shfl_xor(l[c], 32);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (rvalid[c]) {
-      __bf16* op = O + (((int64_t)b * a.Lq + tok[c]) * a.Hq + hq[c]) * D + 4 * h2;
+      const int64_t oo = (((int64_t)b * a.Lq + tok[c]) * a.Hq + hq[c]) * D + 4 * h2;
+      __bf16* op = O + oo;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const bf16x4 v = to_bf16x4(acc[c][db][4 * q4] * inv, acc[c][db][4 * q4 + 1] * inv,
-                                     acc[c][db][4 * q4 + 2] * inv, acc[c][db][4 * q4 + 3] * inv);
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = acc[c][db][4 * q4 + e] * inv;
+          const bf16x4 v = to_bf16x4(x[0], x[1], x[2], x[3]);
           *(u32x2*)(op + 32 * db + 8 * q4) = __builtin_bit_cast(u32x2, v);
+          if (a.o_lo) {  // what the bf16 rounding dropped, itself rounded to bf16
+            const bf16x4 r = to_bf16x4(x[0] - (float)v[0], x[1] - (float)v[1], x[2] - (float)v[2],
+                                       x[3] - (float)v[3]);
+            *(u32x2*)((__bf16*)a.o_lo + oo + 32 * db + 8 * q4) = __builtin_bit_cast(u32x2, r);
+          }
         }
       if (h2 == 0)
         a.lse[((int64_t)b * a.Hq + hq[c]) * a.Lq + tok[c]] =

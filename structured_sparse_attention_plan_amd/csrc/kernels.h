@@ -20,6 +20,7 @@ struct FwdArgs {
   const void* k;
   const void* v;
   void* o;
+  void* o_lo;  // bf16 rounding residual of O (may be null)
   float* lse;
   const int32_t* row_ptr;
   const int32_t* row_ent;
@@ -37,6 +38,7 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const void* o;
+  const void* o_lo;  // bf16 rounding residual of O (may be null)
   const float* lse;
   const void* dout;
   void* dq;
@@ -44,7 +46,14 @@ struct BwdArgs {
   void* dv;
   float* delta;   // workspace [B, Hq, Lq]: Delta = dO . O per row
   float* qscale;  // workspace [B, Hq, Lq]: 2^e with max |q| / 2^e in [1, 2) per row
+  float* doexp;   // workspace [B, Hq, Lq]: f with max |dO| / 2^f in [1, 2) per row (0 if dO = 0)
   void* q16;      // workspace [B, Lq, Hq, D] fp16: q / qscale per row
+  void* do16;     // workspace [B, Lq, Hq, D] fp16: dO / 2^doexp per row
+  void* k16;      // workspace [B, Lk, Hkv, D] fp16: K / 2^gK, one gK per launch
+  // workspace: launch-wide maxima (bit patterns of non-negative floats, or biased
+  // exponents, compared as unsigned): [0] |dO_i| qscale_i, [1] |Delta_i| qscale_i,
+  // [2] doexp + kExpBias over rows with dO != 0, [3] max |k|, [4] max |v_j|^2
+  float* maxima;
   const int32_t* row_ptr;
   const int32_t* row_ent;
   const int32_t* row_order;
@@ -89,5 +98,6 @@ constexpr int kBwdRows = 128;  // query rows per backward q-block
 constexpr int kBwdBk = 128;
 constexpr int kDecBk = 64;
 constexpr int kDecSplitBlocks = 16;  // k-blocks per decode split (upper bound)
+constexpr int kExpBias = 256;        // bias of exponents kept as unsigned maxima
 
 }  // namespace cowa

@@ -46,8 +46,9 @@ def test_tile_sizes_and_workspace():
     assert api.tile_sizes("fwd", p) == (256 // 5, 64)
     assert api.tile_sizes("bwd", p) == (128 // 5, 128)
     assert api.workspace_size("fwd", p) == 0
-    # Delta and the row scales of Q (fp32 each), then the fp16 copy of Q
-    assert api.workspace_size("bwd", p) == 2 * 40 * 256 * 4 + 256 * 40 * 128 * 2
+    # Delta and the power-of-two scales of Q and dO (fp32 each), 256 bytes of launch-wide
+    # maxima, the fp16 copies of Q and dO, then that of K
+    assert api.workspace_size("bwd", p) == 3 * 40 * 256 * 4 + 256 + 2 * 256 * 40 * 128 * 2 + 256 * 8 * 128 * 2
     pd = _prob(Lq=1, Lk=4096)
     assert api.tile_sizes("decode", pd) == (1, 64)
     assert api.workspace_size("decode", pd) > 0
@@ -86,26 +87,31 @@ def test_entry_points_validate_before_launch():
     plan = _fake_plan(p, "fwd")
     x = ctypes.c_void_p(256)
     # null output
-    assert C.lib.cowa_fwd(ctypes.byref(p), ctypes.byref(plan), x, x, x, None, x, None, 0,
+    assert C.lib.cowa_fwd(ctypes.byref(p), ctypes.byref(plan), x, x, x, None, x, None, None, 0,
+                          None) == C.COWA_ERR_INVALID_ARG
+    # a rounding residual of O is bf16 only
+    pf = _prob(dtype=C.COWA_DTYPE_F32, D=64, Hq=4, Hkv=2)
+    plf = _fake_plan(pf, "fwd")
+    assert C.lib.cowa_fwd(ctypes.byref(pf), ctypes.byref(plf), x, x, x, x, x, x, None, 0,
                           None) == C.COWA_ERR_INVALID_ARG
     # plan built for another length / tiling / window
     for bad in (dict(Lq=128), dict(Bq=32)):
         pl = _fake_plan(p, "fwd", **bad)
-        assert C.lib.cowa_fwd(ctypes.byref(p), ctypes.byref(pl), x, x, x, x, x, None, 0,
+        assert C.lib.cowa_fwd(ctypes.byref(p), ctypes.byref(pl), x, x, x, x, x, None, None, 0,
                               None) == C.COWA_ERR_PLAN_MISMATCH
     pl = _fake_plan(p, "fwd")
     pl.win = api.make_window(256, 8, 5, 16)
-    assert C.lib.cowa_fwd(ctypes.byref(p), ctypes.byref(pl), x, x, x, x, x, None, 0,
+    assert C.lib.cowa_fwd(ctypes.byref(p), ctypes.byref(pl), x, x, x, x, x, None, None, 0,
                           None) == C.COWA_ERR_PLAN_MISMATCH
     # backward: workspace too small / misaligned
     pb = _fake_plan(p, "bwd")
-    assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, x, x, x, x, x, 7, x, 16,
-                          None) == C.COWA_ERR_WORKSPACE_TOO_SMALL
-    assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, x, x, x, x, x, 7,
-                          ctypes.c_void_p(260), 1 << 23, None) == C.COWA_ERR_INVALID_ARG
+    assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, None, x, x, x, x, x, 7, x,
+                          16, None) == C.COWA_ERR_WORKSPACE_TOO_SMALL
+    assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, x, x, x, x, x, x, 7,
+                          ctypes.c_void_p(260), 1 << 24, None) == C.COWA_ERR_INVALID_ARG
     for bad_stages in (0, 8):
-        assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, x, x, x, x, x,
-                              bad_stages, ctypes.c_void_p(256), 1 << 20,
+        assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, None, x, x, x, x, x,
+                              bad_stages, ctypes.c_void_p(256), 1 << 24,
                               None) == C.COWA_ERR_INVALID_ARG
     # decode: workspace too small
     pd = _prob(Lq=1, Lk=4096, win=api.make_window(4096, 8, 4, 16))
@@ -120,3 +126,19 @@ def test_entry_points_validate_before_launch():
     p2 = _prob(Lq=2, Lk=4096, win=api.make_window(4096, 8, 4, 16))
     assert C.lib.cowa_decode_varlen(ctypes.byref(p2), x, x, x, x, x, None, x, 1 << 30,
                                     None) == C.COWA_ERR_UNSUPPORTED
+
+
+def test_python_layer_rejects_host_and_misshapen_tensors():
+    """The Python layer checks every tensor it passes (inputs, caller-supplied outputs,
+    gradients, workspace) before calling into the library: host tensors, wrong shapes
+    and dtypes raise ValueError, so nothing reaches a kernel."""
+    import torch
+    win = api.make_window(64, 2, 4, 16)
+    q = torch.zeros((1, 64, 4, 128), dtype=torch.bfloat16)
+    k = torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        api.fwd(q, k, k, win)
+    with pytest.raises(ValueError):
+        api._check_tensor("lse", torch.zeros((1, 4, 63)), (1, 4, 64), torch.float32)
+    with pytest.raises(ValueError):
+        api._workspace("workspace", torch.zeros(16, dtype=torch.uint8), 32, torch.device("cpu"))

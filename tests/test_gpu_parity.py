@@ -93,6 +93,55 @@ def test_fwd_bf16_reference_moves(case):
     assert_bf16_close("LSE", lse, Lo)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(16, 8), (24, 8), (16, 2), (6, 2)])
+def test_fwd_bf16_group_sizes(Hq, Hkv):
+    """Group sizes G = 2, 3, 8 (and 3 with two KV heads): the q-block holds 256 / G tokens
+    (85 for G = 3, so one row of the 256 is unused)."""
+    L = 700
+    _case(f"fwd bf16 L={L} Hq={Hq} Hkv={Hkv} (G={Hq // Hkv})")
+    ow, win = _windows(L, Hkv, 16, 64)
+    q, k, v = inputs.attention_inputs(1, L, L, Hq, Hkv, 128, seed=13)
+    o, lse = api.fwd(q.to(DEV), k.to(DEV), v.to(DEV), win)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.attn_fwd(q, k, v, ow, 128 ** -0.5)
+    assert_bf16_close("O", o, Oo)
+    assert_bf16_close("LSE", lse, Lo)
+
+
+@pytest.mark.parametrize("Lq,Lk", [(500, 500), (700, 300)])
+def test_fwd_bf16_empty_rows(Lq, Lk):
+    """near = 0 and no prefix sink: under KV head h > 0 a query closer than the head's
+    band to key 0 sees nothing (O = 0, LSE = -inf); with Lq > Lk, the first Lq - Lk rows
+    lie before every key under the bottom-right distance and are empty under every head."""
+    _case(f"fwd bf16 empty rows Lq={Lq} Lk={Lk} sink=0 near=0")
+    Hq, Hkv = 16, 4
+    ow, win = _windows(Lk, Hkv, 0, 0)
+    q, k, v = inputs.attention_inputs(1, Lq, Lk, Hq, Hkv, 128, seed=14)
+    o, lse = api.fwd(q.to(DEV), k.to(DEV), v.to(DEV), win)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.attn_fwd(q, k, v, ow, 128 ** -0.5)
+    n_empty = int(np.isinf(Lo).sum())
+    print(f"  empty (row, head) pairs: {n_empty}", flush=True)
+    assert n_empty > 0
+    assert_bf16_close("O", o, Oo)
+    assert_bf16_close("LSE", lse, Lo)
+    assert torch.all(o.cpu()[torch.from_numpy(np.isinf(Lo).transpose(0, 2, 1).copy())] == 0)
+
+
+@pytest.mark.parametrize("Lq,Lk,sink,near", [(400, 400, 16, 64), (500, 300, 8, 40)])
+def test_fwd_bf16_more_queries_than_keys(Lq, Lk, sink, near):
+    """Lq > Lk: query row i sits at key position i - (Lq - Lk); rows before key 0 are
+    empty, the others see the usual window."""
+    _case(f"fwd bf16 Lq={Lq} Lk={Lk} sink={sink} near={near}")
+    ow, win = _windows(Lk, 8, sink, near)
+    q, k, v = inputs.attention_inputs(1, Lq, Lk, 40, 8, 128, seed=15)
+    o, lse = api.fwd(q.to(DEV), k.to(DEV), v.to(DEV), win)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.attn_fwd(q, k, v, ow, 128 ** -0.5)
+    assert_bf16_close("O", o, Oo)
+    assert_bf16_close("LSE", lse, Lo)
+
+
 def test_fwd_bf16_mid_4096_full():
     _case("fwd bf16 L=4096 Hq=40 Hkv=8 sink=128 near=512")
     L = 4096
@@ -130,17 +179,61 @@ def test_bwd_bf16_small_full(B, L, Hq, Hkv, sink, near, mode):
     ow, win = _windows(L, Hkv, sink, near, mode=mode)
     q, k, v, do = inputs.attention_inputs(B, L, L, Hq, Hkv, 128, seed=4, with_dout=True)
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
-    o, lse = api.fwd(qd, kd, vd, win)
-    dq, dk, dv = api.bwd(qd, kd, vd, o, lse, dod, win)
+    o, lse, dq, dk, dv = api.fwd_bwd(qd, kd, vd, dod, win)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attn_bwd(q, k, v, do, ow, 128 ** -0.5)
-    assert_bf16_close("dQ", dq, rq, value_scaled=True)
-    assert_bf16_close("dK", dk, rk, value_scaled=True)
-    assert_bf16_close("dV", dv, rv, value_scaled=True)
+    assert_bf16_close("dQ", dq, rq, gradient=True)
+    assert_bf16_close("dK", dk, rk, gradient=True)
+    assert_bf16_close("dV", dv, rv, gradient=True)
+
+
+@pytest.mark.parametrize("B,Lq,Lk,Hq,Hkv,sink,near", [
+    (1, 500, 500, 16, 8, 16, 64),    # G = 2
+    (1, 500, 500, 24, 8, 16, 64),    # G = 3: 42 tokens per q-block, two rows unused
+    (1, 500, 500, 16, 2, 16, 64),    # G = 8
+    (1, 400, 400, 16, 4, 0, 0),      # near = 0, no sink: empty rows under heads 1-3
+    (1, 500, 300, 40, 8, 8, 40),     # Lq > Lk: the first 200 rows are empty
+])
+def test_bwd_bf16_group_sizes_and_empty_rows(B, Lq, Lk, Hq, Hkv, sink, near):
+    _case(f"bwd bf16 B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} sink={sink} near={near}")
+    ow, win = _windows(Lk, Hkv, sink, near)
+    q, k, v, do = inputs.attention_inputs(B, Lq, Lk, Hq, Hkv, 128, seed=16, with_dout=True)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse, dq, dk, dv = api.fwd_bwd(qd, kd, vd, dod, win)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attn_bwd(q, k, v, do, ow, 128 ** -0.5)
+    assert_bf16_close("dQ", dq, rq, gradient=True)
+    assert_bf16_close("dK", dk, rk, gradient=True)
+    assert_bf16_close("dV", dv, rv, gradient=True)
+
+
+@pytest.mark.parametrize("do_exp,v_exp", [(12, 0), (-24, 0), (0, 6), (8, 5)])
+def test_bwd_bf16_gradient_ranges(do_exp, v_exp):
+    """dO multiplied by 2^do_exp (a loss-scaled or a tiny upstream gradient) and V by
+    2^v_exp: dS scales with both, and the fp16 dK product must neither overflow nor lose
+    its precision to subnormals.  Compared in the units of the unscaled problem, where
+    the bars are set (dQ and dK scale by 2^(do_exp + v_exp), dV by 2^do_exp)."""
+    L = 600
+    _case(f"bwd bf16 L={L} dO * 2^{do_exp}, V * 2^{v_exp}")
+    ow, win = _windows(L, 8, 16, 64)
+    q, k, v, do = inputs.attention_inputs(1, L, L, 40, 8, 128, seed=17, with_dout=True)
+    do = (do.float() * 2.0 ** do_exp).to(torch.bfloat16)
+    v = (v.float() * 2.0 ** v_exp).to(torch.bfloat16)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse, dq, dk, dv = api.fwd_bwd(qd, kd, vd, dod, win)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attn_bwd(q, k, v, do, ow, 128 ** -0.5)
+    sg, sv = 2.0 ** -(do_exp + v_exp), 2.0 ** -do_exp
+    for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert torch.isfinite(t).all(), f"{name} has non-finite entries"
+    assert_bf16_close("dQ (rescaled)", dq.double() * sg, rq * sg, gradient=True)
+    assert_bf16_close("dK (rescaled)", dk.double() * sg, rk * sg, gradient=True)
+    assert_bf16_close("dV (rescaled)", dv.double() * sv, rv * sv, gradient=True)
 
 
 def test_bwd_bf16_mid_2048_full():
-    _case("bwd bf16 L=2048 Hq=40 Hkv=8 sink=128 near=512")
+    """The backward without O's rounding residual (Delta from the bf16 O alone)."""
+    _case("bwd bf16 L=2048 Hq=40 Hkv=8 sink=128 near=512, no residual of O")
     L = 2048
     ow, win = _windows(L, 8, 128, 512)
     q, k, v, do = inputs.attention_inputs(1, L, L, 40, 8, 128, seed=5, with_dout=True)
@@ -149,9 +242,9 @@ def test_bwd_bf16_mid_2048_full():
     dq, dk, dv = api.bwd(qd, kd, vd, o, lse, dod, win)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attn_bwd(q, k, v, do, ow, 128 ** -0.5)
-    assert_bf16_close("dQ", dq, rq, value_scaled=True)
-    assert_bf16_close("dK", dk, rk, value_scaled=True)
-    assert_bf16_close("dV", dv, rv, value_scaled=True)
+    assert_bf16_close("dQ", dq, rq, gradient=True)
+    assert_bf16_close("dK", dk, rk, gradient=True)
+    assert_bf16_close("dV", dv, rv, gradient=True)
 
 
 @pytest.mark.parametrize("B,Lq,Lk,Hq,Hkv,sink,near,mode", [
@@ -165,13 +258,12 @@ def test_bwd_bf16_prefill_chunk(B, Lq, Lk, Hq, Hkv, sink, near, mode):
     ow, win = _windows(Lk, Hkv, sink, near, mode=mode)
     q, k, v, do = inputs.attention_inputs(B, Lq, Lk, Hq, Hkv, 128, seed=8, with_dout=True)
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
-    o, lse = api.fwd(qd, kd, vd, win)
-    dq, dk, dv = api.bwd(qd, kd, vd, o, lse, dod, win)
+    o, lse, dq, dk, dv = api.fwd_bwd(qd, kd, vd, dod, win)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attn_bwd(q, k, v, do, ow, 128 ** -0.5)
-    assert_bf16_close("dQ", dq, rq, value_scaled=True)
-    assert_bf16_close("dK", dk, rk, value_scaled=True)
-    assert_bf16_close("dV", dv, rv, value_scaled=True)
+    assert_bf16_close("dQ", dq, rq, gradient=True)
+    assert_bf16_close("dK", dk, rk, gradient=True)
+    assert_bf16_close("dV", dv, rv, gradient=True)
 
 
 @pytest.mark.parametrize("qexp", [9, -9])
@@ -186,14 +278,13 @@ def test_bwd_bf16_scaled_q(qexp):
     q = (q.float() * 2.0 ** qexp).to(torch.bfloat16)
     k = (k.float() * 2.0 ** -qexp).to(torch.bfloat16)
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
-    o, lse = api.fwd(qd, kd, vd, win)
-    dq, dk, dv = api.bwd(qd, kd, vd, o, lse, dod, win)
+    o, lse, dq, dk, dv = api.fwd_bwd(qd, kd, vd, dod, win)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attn_bwd(q, k, v, do, ow, 128 ** -0.5)
     # compare in the units of the unscaled problem, where the bars are set
-    assert_bf16_close("dQ * 2^qexp", dq.float() * 2.0 ** qexp, rq * 2.0 ** qexp, value_scaled=True)
-    assert_bf16_close("dK * 2^-qexp", dk.float() * 2.0 ** -qexp, rk * 2.0 ** -qexp, value_scaled=True)
-    assert_bf16_close("dV", dv, rv, value_scaled=True)
+    assert_bf16_close("dQ * 2^qexp", dq.float() * 2.0 ** qexp, rq * 2.0 ** qexp, gradient=True)
+    assert_bf16_close("dK * 2^-qexp", dk.float() * 2.0 ** -qexp, rk * 2.0 ** -qexp, gradient=True)
+    assert_bf16_close("dV", dv, rv, gradient=True)
 
 
 def test_chunked_prefill_matches_full_forward():
@@ -240,6 +331,22 @@ def test_decode_small(B, Lk, Hq, Hkv, sink, near, mode):
     o, lse = api.decode(q.to(DEV), k.to(DEV), v.to(DEV), win)
     torch.cuda.synchronize()
     Oo, Lo = oracle.decode(q, k, v, ow, 128 ** -0.5)
+    assert_bf16_close("O", o, Oo)
+    assert_bf16_close("LSE", lse, Lo[:, :, 0])
+
+
+def test_decode_empty_rows():
+    """near = 0, no sink: the query at position Lk - 1 sees only its head's band, and KV
+    heads whose band starts beyond it see nothing (O = 0, LSE = -inf)."""
+    B, Lk, Hq, Hkv = 2, 900, 16, 4
+    _case(f"decode empty rows B={B} Lk={Lk} Hq={Hq} Hkv={Hkv} sink=0 near=0")
+    ow = oracle.Window(0, 0, 0, 400)
+    win = api.window(0, 0, 0, 400)
+    q, k, v = inputs.attention_inputs(B, 1, Lk, Hq, Hkv, 128, seed=18)
+    o, lse = api.decode(q.to(DEV), k.to(DEV), v.to(DEV), win)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.decode(q, k, v, ow, 128 ** -0.5)
+    assert np.isinf(Lo).sum() > 0
     assert_bf16_close("O", o, Oo)
     assert_bf16_close("LSE", lse, Lo[:, :, 0])
 
@@ -293,3 +400,27 @@ def test_decode_equals_forward_last_row():
     dl = (lsed - lse[:, :, -1]).abs().max().item()
     print(f"  max|O_dec - O_fwd[-1]|={d:.3e} max|dLSE|={dl:.3e}", flush=True)
     assert d <= 1e-2 and dl <= 1e-3
+
+
+def test_fwd_residual_is_what_bf16_rounding_drops():
+    """The forward's optional residual: O and LSE are bit-identical with and without it,
+    and O + residual is closer to the oracle than O (the residual is the rounding error
+    of the bf16 O, itself rounded to bf16)."""
+    L = 900
+    _case(f"fwd residual of O, L={L}")
+    ow, win = _windows(L, 8, 16, 64)
+    q, k, v = inputs.attention_inputs(1, L, L, 40, 8, 128, seed=19)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o1, l1 = api.fwd(qd, kd, vd, win)
+    o_lo = torch.empty_like(qd)
+    o2, l2 = api.fwd(qd, kd, vd, win, o_lo=o_lo)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    Oo, _ = oracle.attn_fwd(q, k, v, ow, 128 ** -0.5)
+    e_hi, _ = errors(o2, Oo)
+    e_sum, _ = errors(o2.double() + o_lo.double(), Oo)
+    print(f"  max|O - oracle|={e_hi:.3e}  max|O + residual - oracle|={e_sum:.3e}", flush=True)
+    # the residual never exceeds half an ulp of O's bf16 value (2^-9 relative)
+    lo, hi = o_lo.double().abs(), o2.double().abs()
+    assert bool((lo <= hi * 2.0 ** -8 + 1e-30).all())
+    assert e_sum < e_hi
