@@ -242,6 +242,25 @@ int cowa_decode_varlen(const cowa_problem* p, const void* q, const void* k_cache
                        const void* v_cache, const int32_t* seqlens_k, void* o, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, checks and results as cowa_decode (bit-identical outputs), but the split
+ * partials live in a library-owned device array of COWA_DECODE_SCRATCH_BYTES bytes per
+ * GPU, which each GPU the library runs on holds until the process ends; its address is
+ * looked up (hipGetSymbolAddress) on the first call made on a device, with that device
+ * current, which must be the device of `stream`.  Nothing is allocated and nothing needs
+ * to start at zero: every partial is written before it is read.  All calls on one GPU
+ * share its array, so calls that overlap in time on one GPU (different streams, or
+ * different host threads) race; calls on one stream are ordered and safe.
+ * Errors: as cowa_decode, and WORKSPACE_TOO_SMALL (before any device work) when
+ * cowa_workspace_size(COWA_OP_DECODE, p) exceeds COWA_DECODE_SCRATCH_BYTES (it is about
+ * B * Hq * 32 * 520 bytes at 131072 cache positions: B * Hq up to about 1000); HIP when
+ * the address lookup fails. */
+#define COWA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+int cowa_decode_noalloc(const cowa_problem* p, const cowa_plan_dev* plan,
+                        const void* q, const void* k_cache, const void* v_cache,
+                        void* o, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "cowa.h"
 #include "kernels.h"
@@ -351,4 +352,59 @@ extern "C" int cowa_decode_varlen(const cowa_problem* p, const void* q, const vo
   a.scale_log2 = p->scale * 1.44269504088896340736f;
   a.win = dev_window(p->win);
   return hip_status(launch_decode_bf16_d128(a, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------- no-allocation decode
+// The decode's split partials in a file-scope device array instead of a caller workspace.
+// In host code `scratch` names a host-side stand-in, not device memory: its device address
+// comes from hipGetSymbolAddress, once per device with that device current, and only that
+// address is ever handed to a kernel.
+namespace {
+
+constexpr size_t kScratchBytes = COWA_DECODE_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of `scratch` (looked up on the first call made on
+// the device), or null with *err set.
+void* scratch_on_current_device(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int cowa_decode_noalloc(const cowa_problem* p, const cowa_plan_dev* plan, const void* q,
+                                   const void* k_cache, const void* v_cache, void* o, float* lse,
+                                   void* stream) {
+  int st = check_problem(p);
+  if (st != COWA_OK) return st;
+  st = check_op_support(COWA_OP_DECODE, p);
+  if (st != COWA_OK) return st;
+  if (!q || !k_cache || !v_cache || !o) return COWA_ERR_INVALID_ARG;
+  st = check_plan(COWA_OP_DECODE, p, plan, false);
+  if (st != COWA_OK) return st;
+  size_t need = 0;
+  cowa_workspace_size(COWA_OP_DECODE, p, &need);
+  if (need > kScratchBytes) return COWA_ERR_WORKSPACE_TOO_SMALL;
+  hipError_t err;
+  void* ws = scratch_on_current_device(&err);
+  if (!ws) return COWA_ERR_HIP;
+  return cowa_decode(p, plan, q, k_cache, v_cache, o, lse, ws, kScratchBytes, stream);
 }

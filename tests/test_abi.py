@@ -142,3 +142,21 @@ def test_python_layer_rejects_host_and_misshapen_tensors():
         api._check_tensor("lse", torch.zeros((1, 4, 63)), (1, 4, 64), torch.float32)
     with pytest.raises(ValueError):
         api._workspace("workspace", torch.zeros(16, dtype=torch.uint8), 32, torch.device("cpu"))
+
+
+def test_decode_noalloc_rejects_problems_beyond_its_array():
+    """cowa_decode_noalloc checks the problem's partials against its fixed device array
+    before touching the device: a batch whose partials exceed COWA_DECODE_SCRATCH_BYTES
+    gets WORKSPACE_TOO_SMALL (the plan's pointers are never read)."""
+    pd = _prob(B=2048, Lq=1, Lk=4096, win=api.make_window(4096, 8, 4, 16))
+    need = api.workspace_size("decode", pd)
+    assert need > C.COWA_DECODE_SCRATCH_BYTES
+    pld = _fake_plan(pd, "decode")
+    x = ctypes.c_void_p(256)
+    assert C.lib.cowa_decode_noalloc(ctypes.byref(pd), ctypes.byref(pld), x, x, x, x, None,
+                                     None) == C.COWA_ERR_WORKSPACE_TOO_SMALL
+    # and it validates like cowa_decode (null output)
+    ps = _prob(B=2, Lq=1, Lk=4096, win=api.make_window(4096, 8, 4, 16))
+    pls = _fake_plan(ps, "decode")
+    assert C.lib.cowa_decode_noalloc(ctypes.byref(ps), ctypes.byref(pls), x, x, x, None, None,
+                                     None) == C.COWA_ERR_INVALID_ARG
