@@ -218,7 +218,8 @@ def extras(seed, main_fb_ms, main_fwd_ms, main_bwd_ms, main_dec_ms, main_E, main
     """Secondary workloads timed with the same kernels: the 32K forward, the 32K coverage
     ablation (complementary / duplicated / dense bands, forward + backward), dense causal
     attention at 128K (forward + backward and decode) for the CoWA-vs-dense ratios, a
-    variable-length decode over the 128K caches, and the fp32 1K forward."""
+    variable-length decode over the 128K caches, the decode over window-only caches, and
+    the fp32 1K forward."""
     import torch
     from structured_sparse_attention_plan_amd import api, inputs
     from structured_sparse_attention_plan_amd import _cowa as C
@@ -295,6 +296,28 @@ def extras(seed, main_fb_ms, main_fwd_ms, main_bwd_ms, main_dec_ms, main_E, main
         "us_per_step": var_us, "visible_kv_bytes": var_bytes,
         "gbps": var_bytes / (var_us * 1e-6) / 1e9,
         "hbm_frac": var_bytes / (var_us * 1e-6) / (HBM_PEAK_GBPS * 1e9)}
+    # window-only caches (each KV head keeps the sink and the positions it can still see),
+    # filled from the same full caches by one 131072-token append per sequence, then the
+    # same decode step as the headline one
+    wc = api.WindowCache(DEC_B, HKV, D, L, win_c, dev)
+    wc.append(kc, vc, torch.zeros(DEC_B, dtype=torch.int32, device=dev))
+    full = torch.full((DEC_B,), L, dtype=torch.int32, device=dev)
+    ow_, lw_ = wc.decode(qd, full, D ** -0.5, out=torch.empty_like(od), lse=torch.empty_like(lsed),
+                         workspace=wsd)
+    op_, lp_ = api.decode(qd, kc, vc, win_c, D ** -0.5)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ow_, op_) and torch.equal(lw_, lp_))
+    wc_us = 1e3 * _events_ms(lambda: wc.decode(qd, full, D ** -0.5, out=od, lse=lsed, workspace=wsd), 10, 3)
+    caps = [wc.head_offset[h + 1] - wc.head_offset[h] for h in range(HKV)]
+    out["decode_window_cache_16x128k"] = {
+        "us_per_step": wc_us, "gbps": main_dec_bytes / (wc_us * 1e-6) / 1e9,
+        "hbm_frac": main_dec_bytes / (wc_us * 1e-6) / (HBM_PEAK_GBPS * 1e9),
+        "equals_planned_decode_bitwise": same,
+        "rows_held_per_head": caps, "rows_full_cache_per_head": L,
+        "bytes_held": wc.nbytes(), "bytes_full_caches": 2 * DEC_B * L * HKV * D * 2,
+        "saving_all_heads": DEC_B * 2 * L * HKV * D * 2 / wc.nbytes(),
+        "saving_head0": L / caps[0]}
+    del wc, ow_, lw_, op_, lp_
     del qd, kc, vc
     torch.cuda.empty_cache()
     out["dense_128k"] = dense

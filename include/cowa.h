@@ -242,6 +242,57 @@ int cowa_decode_varlen(const cowa_problem* p, const void* q, const void* k_cache
                        const void* v_cache, const int32_t* seqlens_k, void* o, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- window-only cache
+ * Each rank needs only the KV cache of its own window (slinene.github.io ai-papers-daily
+ * page, practical note 3).  Under the bottom-right distance a decode query at position p
+ * sees, under KV head h, the prefix sink and the keys at distance p - j in the near window
+ * or in the head's band; distances only grow as tokens are appended, so a key (past the
+ * sink) that is R_h = max(near_w, hi_h) or more positions behind the newest token is never
+ * seen by head h again, while a nearer one is seen now or once the band reaches it (for
+ * h > 0 that includes the keys between the near window and the band).  The cache of head
+ * h therefore holds the sink and a ring of the last R_h positions:
+ *   slot(j) = j                 for j < min(sink, Lmax)
+ *           = sink + (j mod R_h) otherwise
+ * (R_h = Lmax and no separate sink when sink + R_h >= Lmax: the whole history).  hi_h is
+ * the band's upper distance (Lmax in dense mode).  Heads follow one another in the slot
+ * dimension; per sequence the caches take cowa_wcache_layout's `slots` rows of D values.
+ * At 131072 positions (sink 128, near 4096, 8 bands of 15872) head 0 holds 20096 rows
+ * and head 7 all 131072: 605056 rows for the 8 heads against 1048576 for full caches. */
+typedef struct cowa_wcache {
+  int32_t B, Hkv, D;  /* sequences, KV heads, head dim (128)                          */
+  int32_t Lmax;       /* positions the cache serves (the window's Lmax)               */
+  cowa_window win;
+  void* k;            /* device [B, slots, D] bf16                                     */
+  void* v;            /* device [B, slots, D] bf16                                     */
+} cowa_wcache;
+
+/* Slots per sequence (*slots) and, if head_offset is not NULL, the first slot of each
+ * head (head_offset[h], h = 0..Hkv; head_offset[Hkv] = *slots).
+ * Errors: INVALID_ARG (NULL win/slots, Hkv < 1, Lmax < 1, bad window), UNSUPPORTED
+ * (Lmax > 2^30). */
+int cowa_wcache_layout(const cowa_window* win, int32_t Hkv, int32_t Lmax, int64_t* head_offset,
+                       int64_t* slots);
+
+/* Append T tokens per sequence: k_new/v_new [B, T, Hkv, D] bf16 hold the K/V rows of
+ * positions pos0[b] .. pos0[b] + T - 1 of sequence b (pos0: device int32 [B]).  Each head
+ * stores the positions it can still see; of the positions of one chunk that share a ring
+ * slot only the last is written, so T may exceed the ring (a whole prefill in one call).
+ * Positions must be appended in order, each once; positions outside [0, Lmax) are
+ * ignored.  Errors: INVALID_ARG, UNSUPPORTED (D != 128), HIP. */
+int cowa_wcache_append(const cowa_wcache* c, const void* k_new, const void* v_new, int32_t T,
+                       const int32_t* pos0, void* stream);
+
+/* Decode over window-only caches: as cowa_decode_varlen (sequence b has length
+ * seqlens[b], its query at position seqlens[b] - 1, clamped to [0, Lmax]) with each key
+ * read from its head's slot; the same blocks in the same order, so the result equals
+ * cowa_decode_varlen's over full caches holding the same rows, bit for bit.  p->Lk must
+ * be c->Lmax, and p's B, Hkv, D and window those of c.  workspace:
+ * cowa_workspace_size(COWA_OP_DECODE, p).  Errors: INVALID_ARG, UNSUPPORTED,
+ * WORKSPACE_TOO_SMALL, HIP. */
+int cowa_wcache_decode(const cowa_problem* p, const cowa_wcache* c, const void* q,
+                       const int32_t* seqlens, void* o, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* Decode without a workspace, for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
  * arguments, checks and results as cowa_decode (bit-identical outputs), but the split

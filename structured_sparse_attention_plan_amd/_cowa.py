@@ -24,7 +24,7 @@ COWA_BWD_DELTA, COWA_BWD_DQ, COWA_BWD_DKDV, COWA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTS = ("cowa_status_string", "cowa_window_make", "cowa_plan_blocks", "cowa_tile_sizes",
            "cowa_workspace_size", "cowa_fwd", "cowa_bwd", "cowa_decode", "cowa_decode_varlen",
-           "cowa_decode_noalloc")
+           "cowa_wcache_layout", "cowa_wcache_append", "cowa_wcache_decode", "cowa_decode_noalloc")
 COWA_DECODE_SCRATCH_BYTES = 16 << 20
 
 _i32 = ctypes.c_int32
@@ -52,6 +52,11 @@ class cowa_plan_dev(ctypes.Structure):
 class cowa_problem(ctypes.Structure):
     _fields_ = [("B", _i32), ("Lq", _i32), ("Lk", _i32), ("Hq", _i32), ("Hkv", _i32), ("D", _i32),
                 ("dtype", _i32), ("scale", ctypes.c_float), ("win", cowa_window)]
+
+
+class cowa_wcache(ctypes.Structure):
+    _fields_ = [("B", _i32), ("Hkv", _i32), ("D", _i32), ("Lmax", _i32), ("win", cowa_window),
+                ("k", _p), ("v", _p)]
 
 
 def _load():
@@ -85,6 +90,14 @@ def _load():
     lib.cowa_decode_varlen.argtypes = [ctypes.POINTER(cowa_problem), _p, _p, _p, _p, _p, _p, _p,
                                        ctypes.c_size_t, _p]
     lib.cowa_decode_varlen.restype = ctypes.c_int
+    lib.cowa_wcache_layout.argtypes = [ctypes.POINTER(cowa_window), _i32, _i32, ctypes.POINTER(_i64),
+                                       ctypes.POINTER(_i64)]
+    lib.cowa_wcache_layout.restype = ctypes.c_int
+    lib.cowa_wcache_append.argtypes = [ctypes.POINTER(cowa_wcache), _p, _p, _i32, _p, _p]
+    lib.cowa_wcache_append.restype = ctypes.c_int
+    lib.cowa_wcache_decode.argtypes = [ctypes.POINTER(cowa_problem), ctypes.POINTER(cowa_wcache), _p, _p,
+                                       _p, _p, _p, ctypes.c_size_t, _p]
+    lib.cowa_wcache_decode.restype = ctypes.c_int
     lib.cowa_decode_noalloc.argtypes = [ctypes.POINTER(cowa_problem), ctypes.POINTER(cowa_plan_dev),
                                         _p, _p, _p, _p, _p, _p]
     lib.cowa_decode_noalloc.restype = ctypes.c_int

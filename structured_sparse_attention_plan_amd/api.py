@@ -237,3 +237,57 @@ def fwd_bwd(q, k, v, dout, win, scale=None):
     o, lse = fwd(q, k, v, win, scale, o_lo=o_lo)
     dq, dk, dv = bwd(q, k, v, o, lse, dout, win, scale, o_lo=o_lo)
     return o, lse, dq, dk, dv
+
+
+def wcache_layout(win, Hkv, Lmax):
+    """cowa_wcache_layout -> (slots per sequence, first slot of each head [Hkv + 1])."""
+    offs = (ctypes.c_int64 * (Hkv + 1))()
+    slots = ctypes.c_int64()
+    C.check("cowa_wcache_layout", C.lib.cowa_wcache_layout(ctypes.byref(win), Hkv, Lmax, offs,
+                                                          ctypes.byref(slots)))
+    return slots.value, list(offs)
+
+
+class WindowCache:
+    """Window-only KV caches of B sequences (cowa_wcache): per KV head the prefix sink and
+    the ring of positions the head can still see, K and V [B, slots, D] bf16 on `device`."""
+
+    def __init__(self, B, Hkv, D, Lmax, win, device, dtype=torch.bfloat16):
+        self.slots, self.head_offset = wcache_layout(win, Hkv, Lmax)
+        self.B, self.Hkv, self.D, self.Lmax, self.win = B, Hkv, D, Lmax, win
+        self.k = torch.zeros((B, self.slots, D), dtype=dtype, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.struct = C.cowa_wcache(B, Hkv, D, Lmax, win, self.k.data_ptr(), self.v.data_ptr())
+
+    def nbytes(self):
+        return 2 * self.k.numel() * self.k.element_size()
+
+    def append(self, k_new, v_new, pos0):
+        """Append T tokens per sequence: k_new/v_new [B, T, Hkv, D] at positions
+        pos0[b] .. pos0[b] + T - 1 (pos0: int32 [B] on the device)."""
+        B, T = k_new.shape[0], k_new.shape[1]
+        _check_tensor("k_new", k_new, (self.B, T, self.Hkv, self.D), self.k.dtype, self.k.device)
+        _check_tensor("v_new", v_new, (self.B, T, self.Hkv, self.D), self.k.dtype, self.k.device)
+        _check_tensor("pos0", pos0, (self.B,), torch.int32, self.k.device)
+        C.check("cowa_wcache_append",
+                C.lib.cowa_wcache_append(ctypes.byref(self.struct), k_new.data_ptr(), v_new.data_ptr(), T,
+                                         pos0.data_ptr(), _stream(self.k.device)))
+
+    def decode(self, q, seqlens, scale=None, out=None, lse=None, workspace=None):
+        """Decode of q [B,1,Hq,D]: sequence b has length seqlens[b] (int32 [B] on the
+        device), its query at position seqlens[b] - 1 -> (o, lse [B,Hq])."""
+        B, Lq, Hq, D = q.shape
+        scale = D ** -0.5 if scale is None else scale
+        prob = problem(B, 1, self.Lmax, Hq, self.Hkv, D, q.dtype, scale, self.win)
+        _check_tensor("q", q, (self.B, 1, Hq, self.D), self.k.dtype, self.k.device)
+        _check_tensor("seqlens", seqlens, (self.B,), torch.int32, self.k.device)
+        out = torch.empty_like(q) if out is None else out
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+        _check_tensor("out", out, (B, 1, Hq, D), q.dtype, q.device)
+        _check_tensor("lse", lse, (B, Hq), torch.float32, q.device)
+        workspace = _workspace("workspace", workspace, workspace_size("decode", prob), q.device)
+        C.check("cowa_wcache_decode",
+                C.lib.cowa_wcache_decode(ctypes.byref(prob), ctypes.byref(self.struct), q.data_ptr(),
+                                         seqlens.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                         workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+        return out, lse

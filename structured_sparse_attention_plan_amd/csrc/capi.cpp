@@ -9,6 +9,7 @@
 
 #include "cowa.h"
 #include "kernels.h"
+#include "wcache.h"
 #include "window.h"
 
 namespace {
@@ -108,6 +109,17 @@ int decode_splits(const cowa_problem* p) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? COWA_OK : COWA_ERR_HIP; }
+
+// Blocks per decode split: the longest list a query at any position can have (the sink's blocks, the near window and the band each spanning at most
+// one block more than their length in blocks), so that split sizes follow the work.
+int32_t decode_split_blocks(const cowa_problem* p, int nsplit) {
+  const int64_t nkb = (p->Lk + kDecBk - 1) / kDecBk;
+  const int64_t bw = p->win.band_mode == COWA_BAND_DENSE ? (int64_t)p->Lk : (int64_t)p->win.lr;
+  int64_t tmax = ((int64_t)p->win.sink + kDecBk - 1) / kDecBk + ((int64_t)p->win.near_w + kDecBk - 1) / kDecBk + 1 +
+                 (bw + kDecBk - 1) / kDecBk + 1;
+  if (tmax > nkb) tmax = nkb;
+  return (int32_t)((tmax + nsplit - 1) / nsplit);
+}
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -303,6 +315,7 @@ extern "C" int cowa_decode(const cowa_problem* p, const cowa_plan_dev* plan, con
   a.o = o;
   a.lse = lse;
   a.nsplit = decode_splits(p);
+  a.split_blocks = decode_split_blocks(p, a.nsplit);
   const size_t rows = (size_t)p->B * p->Hq * a.nsplit;
   a.part = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + (rows * p->D * sizeof(float) + 255) / 256 * 256);
@@ -343,6 +356,7 @@ extern "C" int cowa_decode_varlen(const cowa_problem* p, const void* q, const vo
   a.part = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + (rows * p->D * sizeof(float) + 255) / 256 * 256);
   a.seqlens = seqlens_k;
+  a.split_blocks = decode_split_blocks(p, a.nsplit);
   a.B = p->B;
   a.Lk = p->Lk;
   a.Hq = p->Hq;
@@ -351,6 +365,89 @@ extern "C" int cowa_decode_varlen(const cowa_problem* p, const void* q, const vo
   a.Bk = kDecBk;
   a.scale_log2 = p->scale * 1.44269504088896340736f;
   a.win = dev_window(p->win);
+  return hip_status(launch_decode_bf16_d128(a, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------- window-only cache
+extern "C" int cowa_wcache_layout(const cowa_window* win, int32_t Hkv, int32_t Lmax, int64_t* head_offset,
+                                  int64_t* slots) {
+  if (!win || !slots || Hkv < 1 || Lmax < 1 || !window_valid(*win)) return COWA_ERR_INVALID_ARG;
+  if (Lmax > (1 << 30)) return COWA_ERR_UNSUPPORTED;
+  if (head_offset)
+    for (int h = 0; h <= Hkv; ++h) head_offset[h] = wcache_offset(*win, h, Lmax);
+  *slots = wcache_offset(*win, Hkv, Lmax);
+  return COWA_OK;
+}
+
+namespace {
+int check_wcache(const cowa_wcache* c) {
+  if (!c || !c->k || !c->v) return COWA_ERR_INVALID_ARG;
+  if (c->B < 1 || c->Hkv < 1 || c->Lmax < 1 || !window_valid(c->win)) return COWA_ERR_INVALID_ARG;
+  if (c->D != 128 || c->B > 65535 || c->Lmax > (1 << 30)) return COWA_ERR_UNSUPPORTED;
+  return COWA_OK;
+}
+}  // namespace
+
+extern "C" int cowa_wcache_append(const cowa_wcache* c, const void* k_new, const void* v_new, int32_t T,
+                                  const int32_t* pos0, void* stream) {
+  int st = check_wcache(c);
+  if (st != COWA_OK) return st;
+  if (!k_new || !v_new || !pos0 || T < 0) return COWA_ERR_INVALID_ARG;
+  WcacheAppendArgs a{};
+  a.k = c->k;
+  a.v = c->v;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.pos0 = pos0;
+  a.B = c->B;
+  a.T = T;
+  a.Hkv = c->Hkv;
+  a.Lmax = c->Lmax;
+  a.wslots = wcache_offset(c->win, c->Hkv, c->Lmax);
+  a.cwin = c->win;
+  return hip_status(launch_wcache_append(a, (hipStream_t)stream));
+}
+
+extern "C" int cowa_wcache_decode(const cowa_problem* p, const cowa_wcache* c, const void* q,
+                                  const int32_t* seqlens, void* o, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  int st = check_problem(p);
+  if (st != COWA_OK) return st;
+  st = check_op_support(COWA_OP_DECODE, p);
+  if (st != COWA_OK) return st;
+  st = check_wcache(c);
+  if (st != COWA_OK) return st;
+  if (c->B != p->B || c->Hkv != p->Hkv || c->D != p->D || c->Lmax != p->Lk || !same_window(c->win, p->win))
+    return COWA_ERR_INVALID_ARG;
+  if (!q || !seqlens || !o) return COWA_ERR_INVALID_ARG;
+  size_t need = 0;
+  cowa_workspace_size(COWA_OP_DECODE, p, &need);
+  if (!workspace || workspace_bytes < need) return COWA_ERR_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)workspace & 255) != 0) return COWA_ERR_INVALID_ARG;
+
+  DecodeArgs a{};
+  a.q = q;
+  a.k = c->k;
+  a.v = c->v;
+  a.o = o;
+  a.lse = lse;
+  a.nsplit = decode_splits(p);
+  const size_t rows = (size_t)p->B * p->Hq * a.nsplit;
+  a.part = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + (rows * p->D * sizeof(float) + 255) / 256 * 256);
+  a.seqlens = seqlens;
+  a.split_blocks = decode_split_blocks(p, a.nsplit);
+  a.B = p->B;
+  a.Lk = p->Lk;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.G = p->Hq / p->Hkv;
+  a.Bk = kDecBk;
+  a.scale_log2 = p->scale * 1.44269504088896340736f;
+  a.win = dev_window(p->win);
+  a.window_mode = 1;
+  a.wslots = wcache_offset(c->win, c->Hkv, c->Lmax);
+  a.cwin = c->win;
   return hip_status(launch_decode_bf16_d128(a, (hipStream_t)stream));
 }
 

@@ -16,6 +16,7 @@
 // query head and split; a second kernel merges the splits (log-sum-exp) into O and LSE.
 
 #include "device_common.h"
+#include "wcache.h"
 
 namespace cowa {
 namespace {
@@ -117,8 +118,12 @@ __device__ __forceinline__ int run_block(const BlockRuns& r, int e) {
   return kb;
 }
 
-template <int G, bool VAR>
+// MODE: 0 full caches with the planner's row list; 1 full caches, each sequence's
+// visible blocks derived from its length (varlen); 2 window-only caches (wcache.h), blocks
+// derived from the length as in mode 1, each key read from its head's slot.
+template <int G, int MODE>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+  constexpr bool VAR = MODE != 0;
   __shared__ float sm[SLOTS][G];
   __shared__ float sl[SLOTS][G];
   __shared__ float so[SLOTS][G][D];
@@ -163,12 +168,29 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     e0 = a.row_ptr[h];
     e1 = a.row_ptr[h + 1];
   }
-  const int chunk = (e1 - e0 + a.nsplit - 1) / a.nsplit;
+  // The split size is fixed per launch (the longest list a query can have over nsplit,
+  // enlarged if this list is longer), so a short list (a short sequence, a head whose
+  // band lies before the sequence start) fills fewer splits instead of spreading thin over
+  // all of them, and every busy work group streams about the same bytes.  Planned and
+  // plan-free decodes of the same query then split alike (equal results, bit for bit).
+  const int ceil_split = (e1 - e0 + a.nsplit - 1) / a.nsplit;
+  const int chunk = max(a.split_blocks, ceil_split);
   const int s0 = e0 + split * chunk;
   const int s1 = min(e1, s0 + chunk);
-  const __bf16* Kb = (const __bf16*)a.k + ((int64_t)b * a.Lk * a.Hkv + h) * D + 8 * li;
-  const __bf16* Vb = (const __bf16*)a.v + ((int64_t)b * a.Lk * a.Hkv + h) * D + 8 * li;
-  const int64_t rstride = (int64_t)a.Hkv * D;
+  // full caches: row j of head h at [b, j, h]; window caches: head h's slot of j in
+  // [b, wslots, D], the ring offset of a block's first key taken once per block
+  WinRing ring{0, 0};
+  int64_t hbase = 0;
+  if constexpr (MODE == 2) {
+    ring = wcache_ring(a.cwin, h, a.Lk);
+    hbase = wcache_offset(a.cwin, h, a.Lk);
+  }
+  const int rs = (int)ring.sink_slots, rr_ = (int)ring.ring;
+  const __bf16* Kb = MODE == 2 ? (const __bf16*)a.k + ((int64_t)b * a.wslots + hbase) * D + 8 * li
+                               : (const __bf16*)a.k + ((int64_t)b * a.Lk * a.Hkv + h) * D + 8 * li;
+  const __bf16* Vb = MODE == 2 ? (const __bf16*)a.v + ((int64_t)b * a.wslots + hbase) * D + 8 * li
+                               : (const __bf16*)a.v + ((int64_t)b * a.Lk * a.Hkv + h) * D + 8 * li;
+  const int64_t rstride = MODE == 2 ? (int64_t)D : (int64_t)a.Hkv * D;
 
   for (int e = s0; e < s1; ++e) {
     // varlen: every block takes the per-key check (no FULL/PARTIAL flags without a plan)
@@ -177,11 +199,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const bool partial = ent & 1;
     u32x4 kw[4], vw[4];
     bool ok[4];
+    const int m0 = (MODE == 2 && rr_ > 0) ? (kb * BK) % rr_ : 0;  // ring position of the block's first key
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int j = kb * BK + rr * SLOTS + slot;
+      const int off_in = rr * SLOTS + slot;
+      const int j = kb * BK + off_in;
       ok[rr] = j < Lb;
-      const int jj = ok[rr] ? j : 0;
+      int jj = ok[rr] ? j : 0;
+      if constexpr (MODE == 2) {
+        // slot of key j: j inside the sink, else sink + (j mod ring); keys a head never
+        // sees (no ring) read slot 0 and are masked below
+        int m = m0 + off_in;
+        if (rr_ >= BK) m -= (m >= rr_) ? rr_ : 0;
+        else if (rr_ > 0) m %= rr_;
+        jj = (jj < rs) ? jj : (rr_ > 0 ? rs + m : 0);
+        if (!ok[rr]) jj = 0;
+      }
       kw[rr] = *(const u32x4*)(Kb + jj * rstride);
       vw[rr] = *(const u32x4*)(Vb + jj * rstride);
       if (partial) ok[rr] = ok[rr] && visible(p, j, Lb, a.win.sink, a.win.near_w, band);
@@ -295,10 +328,13 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
 
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-  if (a.seqlens)
-    hipLaunchKernelGGL((decode_split_kernel<G, true>), dim3(a.nsplit, a.Hkv, a.B), dim3(256), 0, s, a);
+  const dim3 grid(a.nsplit, a.Hkv, a.B);
+  if (a.window_mode)
+    hipLaunchKernelGGL((decode_split_kernel<G, 2>), grid, dim3(256), 0, s, a);
+  else if (a.seqlens)
+    hipLaunchKernelGGL((decode_split_kernel<G, 1>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<G, false>), dim3(a.nsplit, a.Hkv, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<G, 0>), grid, dim3(256), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(D), 0, s, a);
@@ -319,5 +355,39 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t s) {
 }
 
 bool decode_supports_group(int G) { return G == 1 || G == 2 || G == 4 || G == 5 || G == 8; }
+
+// ---------------------------------------------------------------------- window cache append
+// Row (b, t, h) of the new tokens (position pos0[b] + t) goes to head h's slot.  Of the
+// chunk's positions that share a ring slot only the last one is written (the others are
+// R_h or more behind the chunk's newest token, so head h never sees them again), which
+// keeps the writes of one launch disjoint.  Sixteen lanes per 256-byte row.
+namespace {
+__global__ __launch_bounds__(256) void wcache_append_kernel(WcacheAppendArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int li = threadIdx.x & 15;
+  if (row >= (int64_t)a.B * a.T * a.Hkv) return;
+  const int h = (int)(row % a.Hkv);
+  const int64_t bt = row / a.Hkv;
+  const int t = (int)(bt % a.T);
+  const int b = (int)(bt / a.T);
+  const int64_t p0 = a.pos0[b];
+  const int64_t j = p0 + t;
+  if (j < 0 || j >= a.Lmax) return;
+  const WinRing r = wcache_ring(a.cwin, h, a.Lmax);
+  const bool keep = j < r.sink_slots || (r.ring > 0 && j >= p0 + a.T - r.ring);
+  if (!keep) return;
+  const int64_t dst = ((int64_t)b * a.wslots + wcache_offset(a.cwin, h, a.Lmax) + wcache_slot(r, j)) * D + 8 * li;
+  const int64_t src = row * D + 8 * li;
+  *(u32x4*)((__bf16*)a.k + dst) = *(const u32x4*)((const __bf16*)a.k_new + src);
+  *(u32x4*)((__bf16*)a.v + dst) = *(const u32x4*)((const __bf16*)a.v_new + src);
+}
+}  // namespace
+
+hipError_t launch_wcache_append(const WcacheAppendArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.B * a.T * a.Hkv;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(wcache_append_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 }  // namespace cowa

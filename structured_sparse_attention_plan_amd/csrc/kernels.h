@@ -5,6 +5,8 @@
 
 #include <cstdint>
 
+#include "cowa.h"
+
 namespace cowa {
 
 // Window of one problem as the kernels read it: per KV head h the band is
@@ -77,17 +79,34 @@ struct DecodeArgs {
   float* part_ml;    // workspace: [B, Hq, nsplit, 2] (max in log2 units, sum)
   const int32_t* row_ptr;
   const int32_t* row_ent;
-  const int32_t* seqlens;  // varlen decode: [B] cache lengths (no plan); else null
+  const int32_t* seqlens;  // varlen / window-cache decode: [B] cache lengths (no plan); else null
   int32_t B, Lk, Hq, Hkv, G;
   int32_t Bk, nsplit;
+  int32_t split_blocks;  // varlen / window cache: visible blocks per split (at least)
   float scale_log2;
   DevWindow win;
+  // window-only cache (wcache.h): k, v are [B, wslots, D]; null window_mode: full caches
+  int32_t window_mode;
+  int64_t wslots;
+  cowa_window cwin;
+};
+
+struct WcacheAppendArgs {
+  void* k;  // window caches [B, wslots, D]
+  void* v;
+  const void* k_new;  // [B, T, Hkv, D]
+  const void* v_new;
+  const int32_t* pos0;  // [B] position of each sequence's first new token
+  int32_t B, T, Hkv, Lmax;
+  int64_t wslots;
+  cowa_window cwin;
 };
 
 hipError_t launch_fwd_f32_d64(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16_d128(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16_d128(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t s);  // varlen when a.seqlens
+hipError_t launch_wcache_append(const WcacheAppendArgs& a, hipStream_t s);
 bool decode_supports_group(int G);
 
 // Tile shapes of each kernel family (tokens per q-block, keys per k-block).

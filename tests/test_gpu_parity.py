@@ -388,6 +388,85 @@ def test_decode_varlen_full_lengths_equal_decode():
     assert n_o == 0 and n_l == 0
 
 
+@pytest.mark.parametrize("mode,sink,near", [("complementary", 16, 64), ("duplicated", 16, 64),
+                                            ("dense", 8, 32), ("complementary", 0, 100)])
+def test_wcache_appends_then_decode(mode, sink, near):
+    """Window-only caches filled by appends of uneven chunks (5, 1000, three single tokens,
+    769, 1223), some sequences skipped by positions past Lmax, so the three sequences end
+    at lengths 3000, 1777 and 5.  Decoding over them equals the variable-length decode over
+    full caches holding the same rows bit for bit (same blocks, same order), and the oracle
+    decode of each truncated sequence; checked after the middle append too."""
+    B, Lmax, Hq, Hkv = 3, 3000, 40, 8
+    _case(f"window cache appends + decode {mode} sink={sink} near={near}")
+    ow, win = _windows(Lmax, Hkv, sink, near, mode=mode)
+    q, k, v = inputs.attention_inputs(B, 1, Lmax, Hq, Hkv, 128, seed=30)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    cache = api.WindowCache(B, Hkv, 128, Lmax, win, DEV)
+    print(f"  slots per sequence {cache.slots} (full cache {Hkv * Lmax})", flush=True)
+    skip = Lmax + 7  # a position past the cache: the sequence takes no token
+    lens = [0, 0, 0]
+
+    def append(T, take):
+        pos0 = [lens[b] if take[b] else skip for b in range(B)]
+        kn = torch.zeros((B, T, Hkv, 128), dtype=torch.bfloat16, device=DEV)
+        vn = torch.zeros_like(kn)
+        for b in range(B):
+            if take[b]:
+                kn[b] = kd[b, lens[b]:lens[b] + T]
+                vn[b] = vd[b, lens[b]:lens[b] + T]
+                lens[b] += T
+        cache.append(kn, vn, torch.tensor(pos0, dtype=torch.int32, device=DEV))
+
+    def check(tag):
+        seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        ow_, lw_ = cache.decode(qd, seq)
+        of, lf = api.decode_varlen(qd, kd, vd, seq, win)
+        torch.cuda.synchronize()
+        n_o, n_l = int((ow_ != of).sum().item()), int((lw_ != lf).sum().item())
+        print(f"  {tag} lengths {lens}: differs from full-cache varlen at O {n_o}, LSE {n_l}", flush=True)
+        assert n_o == 0 and n_l == 0
+        for b, n in enumerate(lens):
+            Oo, Lo = oracle.decode(q[b:b + 1], k[b:b + 1, :n], v[b:b + 1, :n], ow, 128 ** -0.5)
+            assert_bf16_close(f"O[{b}] (len {n})", ow_[b:b + 1], Oo)
+            assert_bf16_close(f"LSE[{b}]", lw_[b:b + 1], Lo[:, :, 0])
+
+    append(5, [1, 1, 1])
+    append(1000, [1, 1, 0])
+    check("after 1005")
+    for _ in range(3):
+        append(1, [1, 1, 0])
+    append(769, [1, 1, 0])
+    append(1223, [1, 0, 0])
+    check("final")
+
+
+def test_wcache_whole_prefill_in_one_append():
+    """A whole 5000-token prefill appended in one call (the chunk exceeds every head's
+    ring: only the positions each head can still see are written), then 8 single-token
+    appends, each followed by a decode equal bit for bit to the planned decode over the
+    full cache of that length."""
+    B, Lmax, Hq, Hkv = 2, 5008, 40, 8
+    _case(f"window cache: one {Lmax - 8}-token append, then 8 decode steps")
+    ow, win = _windows(Lmax, Hkv, 128, 256)
+    q, k, v = (t.to(DEV) for t in inputs.attention_inputs(B, 9, Lmax, Hq, Hkv, 128, seed=31))
+    cache = api.WindowCache(B, Hkv, 128, Lmax, win, DEV)
+    n = Lmax - 8
+    cache.append(k[:, :n].contiguous(), v[:, :n].contiguous(), torch.zeros(B, dtype=torch.int32, device=DEV))
+    for step in range(9):
+        L = n + step
+        qs = q[:, step:step + 1].contiguous()
+        ow_, lw_ = cache.decode(qs, torch.full((B,), L, dtype=torch.int32, device=DEV))
+        # the planned decode of a length-L sequence, with the window of the capacity
+        of, lf = api.decode_varlen(qs, k, v, torch.full((B,), L, dtype=torch.int32, device=DEV), win)
+        torch.cuda.synchronize()
+        assert torch.equal(ow_, of) and torch.equal(lw_, lf), f"step {step}"
+        if step < 8:
+            cache.append(k[:, L:L + 1].contiguous(), v[:, L:L + 1].contiguous(),
+                         torch.full((B,), L, dtype=torch.int32, device=DEV))
+    Oo, Lo = oracle.decode(q[:, 8:9].cpu(), k.cpu(), v.cpu(), ow, 128 ** -0.5)
+    assert_bf16_close("O (last step)", ow_, Oo)
+
+
 def test_decode_equals_forward_last_row():
     _case("decode vs forward last row L=3000")
     L = 3000
