@@ -141,11 +141,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int Lb = VAR ? min(max(a.seqlens[b], 0), a.Lk) : a.Lk;
   const int p = Lb - 1;
 
-  // query rows of the G heads, 8 dims per lane, as fp32
+  // query rows of the G heads, 8 dims per lane, as fp32, times scale log2(e): the scores
+  // come out in base-2 units
   float q[G][8];
   const __bf16* Qb = (const __bf16*)a.q + ((int64_t)b * a.Hq + h * G) * D + 8 * li;
 #pragma unroll
-  for (int gi = 0; gi < G; ++gi) unpack8(*(const u32x4*)(Qb + gi * D), q[gi]);
+  for (int gi = 0; gi < G; ++gi) {
+    unpack8(*(const u32x4*)(Qb + gi * D), q[gi]);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) q[gi][x] *= a.scale_log2;
+  }
 
   float m[G], l[G], o[G][8];
 #pragma unroll
@@ -199,7 +204,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const bool partial = ent & 1;
     u32x4 kw[4], vw[4];
     bool ok[4];
-    const int m0 = (MODE == 2 && rr_ > 0) ? (kb * BK) % rr_ : 0;  // ring position of the block's first key
+    // window caches: a block past the sink with a ring of at least a block maps onto one
+    // or two runs of the ring: slot rs + m0 + offset, less the ring once it wraps
+    const int kb0 = __builtin_amdgcn_readfirstlane(kb) * BK;
+    const bool ring_fast = MODE == 2 && rr_ >= BK && kb0 >= rs;
+    const int m0 = ring_fast ? kb0 % rr_ : 0;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int off_in = rr * SLOTS + slot;
@@ -207,12 +216,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       ok[rr] = j < Lb;
       int jj = ok[rr] ? j : 0;
       if constexpr (MODE == 2) {
-        // slot of key j: j inside the sink, else sink + (j mod ring); keys a head never
-        // sees (no ring) read slot 0 and are masked below
-        int m = m0 + off_in;
-        if (rr_ >= BK) m -= (m >= rr_) ? rr_ : 0;
-        else if (rr_ > 0) m %= rr_;
-        jj = (jj < rs) ? jj : (rr_ > 0 ? rs + m : 0);
+        if (ring_fast) {
+          const int m = m0 + off_in;
+          jj = rs + (m >= rr_ ? m - rr_ : m);
+        } else {
+          // slot of key j: j inside the sink, else sink + (j mod ring); keys a head never
+          // sees (no ring) read slot 0 and are masked below
+          jj = (jj < rs) ? jj : (rr_ > 0 ? rs + jj % rr_ : 0);
+        }
         if (!ok[rr]) jj = 0;
       }
       kw[rr] = *(const u32x4*)(Kb + jj * rstride);
@@ -230,27 +241,41 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int x = 0; x < 8; ++x) acc = fmaf(q[gi][x], kx[x], acc);
         acc = sum16(acc);
-        s[rr][gi] = ok[rr] ? acc * a.scale_log2 : -INFINITY;
+        s[rr][gi] = ok[rr] ? acc : -INFINITY;
       }
     }
+    // running max per (slot, head): O and l are rescaled only in blocks where some
+    // lane's max rises (after the first few blocks, rarely); a max of -inf (no visible key
+    // yet) gives probabilities of 0 through a reference of 0
+    bool rises = false;
+    float mnew[G];
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       const float mt = fmaxf(fmaxf(s[0][gi], s[1][gi]), fmaxf(s[2][gi], s[3][gi]));
-      const float mn = fmaxf(m[gi], mt);
-      if (mn == -INFINITY) continue;
-      const float alpha = (m[gi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[gi] - mn);
-      m[gi] = mn;
-      l[gi] *= alpha;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) o[gi][x] *= alpha;
+      mnew[gi] = fmaxf(m[gi], mt);
+      rises |= mnew[gi] > m[gi];
     }
+    if (__builtin_amdgcn_ballot_w64(rises) != 0) {
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const float alpha = (m[gi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[gi] - mnew[gi]);
+        const bool up = mnew[gi] > m[gi];
+        m[gi] = mnew[gi];
+        l[gi] = up ? l[gi] * alpha : l[gi];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) o[gi][x] = up ? o[gi][x] * alpha : o[gi][x];
+      }
+    }
+    float mref[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) mref[gi] = m[gi] == -INFINITY ? 0.f : m[gi];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       float vx[8];
       unpack8(vw[rr], vx);
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
-        const float pr = (m[gi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[rr][gi] - m[gi]);
+        const float pr = __builtin_amdgcn_exp2f(s[rr][gi] - mref[gi]);
         l[gi] += pr;
 #pragma unroll
         for (int x = 0; x < 8; ++x) o[gi][x] = fmaf(pr, vx[x], o[gi][x]);
