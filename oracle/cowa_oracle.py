@@ -311,6 +311,74 @@ def decode(q, k_cache, v_cache, win, scale):
     return attn_fwd(q, k_cache, v_cache, win, scale, rows=[0])
 
 
+# --------------------------------------------------------------------------- MALA
+
+# MassAlloc Attention, the companion operator the pages describe alongside CoWA
+# (beyondmarketintelligence.com post, second paragraph and takeaway; crimsonlingua.com
+# news item, fifth paragraph): it keeps the full QK scoring of causal attention and uses
+# the softmax's own statistics to decide whether the rest of a tile's computation is
+# done, skipping it in low-contribution regions.  Readings taken here (the pages give no
+# formula): the statistics are the exact row statistics of the full scoring (the softmax
+# over every visible key); the contribution of a tile (KV head h, q-block of Bq tokens
+# times the G query heads of h, k-block of Bk keys) to a row is the row's probability
+# mass in the tile's keys; the tile is skipped when that mass is below tau for every row
+# of the tile, and a skipped tile adds nothing to O while the denominator stays the full
+# one (O_i = sum over kept tiles of P_ij v_j, P the full softmax).  tau = 0 keeps every
+# tile: exact attention.
+
+def _mala_rows(q, k, win, scale, h, rows, G, Lq):
+    """Full-softmax probabilities P [G, R, Lk] of the given rows under KV head h."""
+    m = mask_rows(rows, Lq, k.shape[1], h, win)
+    P = []
+    for qh in range(h * G, (h + 1) * G):
+        s = scale * (q[0, rows, qh, :] @ k[0, :, h, :].T)
+        p, _ = _masked_softmax_row_stats(s, m)
+        P.append(p)
+    return np.stack(P)
+
+
+def mala_tile_mass(q, k, win, scale, Bq, Bk):
+    """Largest row mass of every tile: mass[h, qb, kb] = max over the tile's rows (its Bq
+    tokens and G query heads) of sum over the tile's keys of P_ij.  B must be 1."""
+    q, k = _f64(q), _f64(k)
+    B, Lq, Hq, D = q.shape
+    _, Lk, Hkv, _ = k.shape
+    assert B == 1
+    G = Hq // Hkv
+    nqb, nkb = -(-Lq // Bq), -(-Lk // Bk)
+    mass = np.zeros((Hkv, nqb, nkb))
+    for h in range(Hkv):
+        for qb in range(nqb):
+            rows = np.arange(qb * Bq, min(Lq, (qb + 1) * Bq))
+            P = _mala_rows(q, k, win, scale, h, rows, G, Lq)
+            for kb in range(nkb):
+                mass[h, qb, kb] = P[:, :, kb * Bk:(kb + 1) * Bk].sum(axis=2).max()
+    return mass
+
+
+def mala_fwd(q, k, v, win, scale, tau, Bq, Bk, kept=None):
+    """MALA forward: O [1, Lq, Hq, D] and the full LSE [1, Hq, Lq]; kept[h, qb, kb]
+    (bool) is taken from the tile masses (mass >= tau) unless given.  -> O, LSE, kept"""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Lq, Hq, D = q.shape
+    _, Lk, Hkv, _ = k.shape
+    assert B == 1
+    G = Hq // Hkv
+    if kept is None:
+        kept = mala_tile_mass(q, k, win, scale, Bq, Bk) >= tau
+    _, LSE = attn_fwd(q, k, v, win, scale)
+    O = np.zeros((1, Lq, Hq, D))
+    nqb = -(-Lq // Bq)
+    for h in range(Hkv):
+        for qb in range(nqb):
+            rows = np.arange(qb * Bq, min(Lq, (qb + 1) * Bq))
+            P = _mala_rows(q, k, win, scale, h, rows, G, Lq)
+            keep_keys = np.repeat(np.asarray(kept[h, qb], dtype=bool), Bk)[:Lk]
+            for gi, qh in enumerate(range(h * G, (h + 1) * G)):
+                O[0, rows, qh, :] = (P[gi] * keep_keys[None, :]) @ v[0, :, h, :]
+    return O, LSE, kept
+
+
 # --------------------------------------------------------------------------- tiles
 
 def tile_lists(Lq, Lk, Hkv, Bq, Bk, win):

@@ -390,3 +390,91 @@ def test_config1_tile_counts():
     per_head = [sum(len(e) for e in lists[h]) for h in range(2)]
     partial = sum(1 for h in range(2) for e in lists[h] for _, f in e if not f)
     assert per_head == [121, 79] and partial == 57
+
+
+# ----------------------------------------------------------------------------- MALA
+
+def _mala_inputs(Lq, Hq, Hkv, D, seed):
+    return _rand((1, Lq, Hq, D), seed), _rand((1, Lq, Hkv, D), seed + 1), _rand((1, Lq, Hkv, D), seed + 2)
+
+
+@pytest.mark.parametrize("mode", [oracle.DENSE, oracle.COMPLEMENTARY])
+def test_mala_tau_zero_is_exact_attention(mode):
+    """tau = 0 keeps every tile: MALA is then the textbook masked attention (torch SDPA in
+    float64 with the explicit mask)."""
+    L, Hq, Hkv, D = 70, 6, 2, 8
+    win = W.for_length(L, Hkv, 3, 9, 0, mode=mode)
+    q, k, v = _mala_inputs(L, Hq, Hkv, D, 70)
+    O, LSE, kept = oracle.mala_fwd(q, k, v, win, 0.3, 0.0, 8, 16)
+    assert kept.all()
+    ref = _sdpa(q, k, v, _masks(L, L, Hq, Hkv, win), 0.3)
+    np.testing.assert_allclose(O, ref.numpy(), atol=1e-12)
+
+
+def test_mala_tau_above_one_skips_every_tile():
+    """A row's mass in a tile never exceeds 1, so tau > 1 skips every tile: O = 0, and LSE
+    is still the logsumexp of the full scoring."""
+    L, Hq, Hkv, D = 50, 4, 2, 8
+    win = W.for_length(L, Hkv, 2, 6, 0, mode=oracle.DENSE)
+    q, k, v = _mala_inputs(L, Hq, Hkv, D, 80)
+    O, LSE, kept = oracle.mala_fwd(q, k, v, win, 0.25, 1.0001, 8, 8)
+    assert not kept.any()
+    assert np.all(O == 0)
+    s = torch.einsum("bihd,bjhd->bhij", q, k.repeat_interleave(Hq // Hkv, dim=2)) * 0.25
+    s = s.masked_fill(~torch.as_tensor(_masks(L, L, Hq, Hkv, win))[None], float("-inf"))
+    np.testing.assert_allclose(LSE, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12)
+
+
+def test_mala_brute_force_tiles_and_output():
+    """Scalar loops over every tile, row and key: each row's probability (exp of the
+    scaled score over the sum of exps of its visible keys), the tile's largest row mass,
+    the keep decision at tau, and O as the sum over kept tiles of P v."""
+    L, Hq, Hkv, D, Bq, Bk = 20, 4, 2, 4, 4, 4
+    win = W.for_length(L, Hkv, 2, 5, 0, mode=oracle.DENSE)
+    q, k, v = _mala_inputs(L, Hq, Hkv, D, 90)
+    scale, tau = 0.6, 0.08
+    G = Hq // Hkv
+    qn, kn, vn = q.numpy(), k.numpy(), v.numpy()
+    prob = np.zeros((Hq, L, L))
+    for qh in range(Hq):
+        h = qh // G
+        for i in range(L):
+            vis = [j for j in range(L) if j <= i]  # dense: causal
+            ex = {j: math.exp(scale * sum(qn[0, i, qh, d] * kn[0, j, h, d] for d in range(D))) for j in vis}
+            tot = sum(ex.values())
+            for j in vis:
+                prob[qh, i, j] = ex[j] / tot
+    mass = oracle.mala_tile_mass(q, k, win, scale, Bq, Bk)
+    O, _, kept = oracle.mala_fwd(q, k, v, win, scale, tau, Bq, Bk)
+    want_O = np.zeros((L, Hq, D))
+    for h in range(Hkv):
+        for qb in range(L // Bq):
+            for kb in range(L // Bk):
+                rm = [sum(prob[qh, i, j] for j in range(kb * Bk, kb * Bk + Bk))
+                      for qh in range(h * G, h * G + G) for i in range(qb * Bq, qb * Bq + Bq)]
+                assert mass[h, qb, kb] == pytest.approx(max(rm), abs=1e-12)
+                assert kept[h, qb, kb] == (max(rm) >= tau)
+                if max(rm) >= tau:
+                    for qh in range(h * G, h * G + G):
+                        for i in range(qb * Bq, qb * Bq + Bq):
+                            for j in range(kb * Bk, kb * Bk + Bk):
+                                want_O[i, qh] += prob[qh, i, j] * vn[0, j, h]
+    assert 0 < kept.sum() < kept.size
+    np.testing.assert_allclose(O[0], want_O, atol=1e-12)
+
+
+def test_mala_row_masses_sum_to_one_and_error_bound():
+    """With one row per tile (a q-block of one token, one query head per KV head) the
+    tile masses of a row are its probability split over the k-blocks: they sum to 1.  A
+    row loses at most its dropped mass times max |v| per dimension."""
+    L, H, D = 64, 2, 8
+    win = W.for_length(L, H, 4, 8, 0)
+    q, k, v = _mala_inputs(L, H, H, D, 100)
+    mass = oracle.mala_tile_mass(q, k, win, 0.4, 1, 8)
+    np.testing.assert_allclose(mass.sum(axis=2), 1.0, atol=1e-12)
+    O, _, kept = oracle.mala_fwd(q, k, v, win, 0.4, 0.05, 1, 8)
+    Oe, _ = oracle.attn_fwd(q, k, v, win, 0.4)
+    dropped = (mass * ~kept).sum(axis=2)               # [H, L]
+    err = np.abs(O - Oe).max(axis=3)[0]                 # [L, H]
+    assert np.all(err <= dropped.T * np.abs(v.numpy()).max() + 1e-12)
+    assert dropped.max() > 0
