@@ -177,6 +177,27 @@ int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan,
              const void* q, const void* k, const void* v, void* o, float* lse, void* o_lo,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/* MALA forward (MassAlloc Attention, the companion operator the pages describe beside
+ * CoWA: beyondmarketintelligence.com post, second paragraph and takeaway; crimsonlingua.com
+ * news item, fifth paragraph): the QK scoring stays full, and the softmax's own
+ * statistics decide whether the rest of a tile's work is done.  Readings fixed here: a
+ * first pass scores every visible key and writes the exact LSE; the second pass takes
+ * each row's probability mass in every tile (KV head, q-block of the forward's tiling,
+ * k-block) from P = exp(scale q.k - LSE) and issues the tile's PV products only when some
+ * row of the tile puts at least `tau` of its mass there; O = sum over kept tiles of P V,
+ * the denominator staying the full one.  tau = 0 keeps every tile (exact attention); a
+ * row loses at most its dropped mass times max |v| per dimension.  The window is the
+ * visibility the scoring covers (COWA_BAND_DENSE: full causal scoring, as the pages
+ * describe MALA; the CoWA windows give MALA on top of CoWA).
+ * q,k,v,o bf16 as in cowa_fwd, D = 128; lse fp32 [B, Hq, Lq] (written: the full LSE).
+ * kept (may be NULL; B = 1 only): int32 per entry of the plan's row lists, set to 1 where
+ * the tile's PV was done and 0 where it was skipped.  The plan is a forward plan
+ * (cowa_tile_sizes(COWA_OP_FWD)).  Errors: INVALID_ARG (also for tau < 0 or NaN, and kept
+ * with B > 1), UNSUPPORTED (not BF16 / D = 128), PLAN_MISMATCH, HIP. */
+int cowa_mala_fwd(const cowa_problem* p, const cowa_plan_dev* plan, float tau,
+                  const void* q, const void* k, const void* v, void* o, float* lse,
+                  int32_t* kept, void* stream);
+
 /* Backward from the saved LSE: the pattern serves training forward and backward alike
  * (beyondmarketintelligence.com post, second paragraph; "CoWindow Attention" abstract),
  * with the gradients of the same masked softmax attention:

@@ -337,9 +337,10 @@ def _mala_rows(q, k, win, scale, h, rows, G, Lq):
     return np.stack(P)
 
 
-def mala_tile_mass(q, k, win, scale, Bq, Bk):
+def mala_tile_mass(q, k, win, scale, Bq, Bk, qblocks=None):
     """Largest row mass of every tile: mass[h, qb, kb] = max over the tile's rows (its Bq
-    tokens and G query heads) of sum over the tile's keys of P_ij.  B must be 1."""
+    tokens and G query heads) of sum over the tile's keys of P_ij.  B must be 1.  With
+    `qblocks`, only those q-blocks are filled (the others stay 0)."""
     q, k = _f64(q), _f64(k)
     B, Lq, Hq, D = q.shape
     _, Lk, Hkv, _ = k.shape
@@ -348,7 +349,7 @@ def mala_tile_mass(q, k, win, scale, Bq, Bk):
     nqb, nkb = -(-Lq // Bq), -(-Lk // Bk)
     mass = np.zeros((Hkv, nqb, nkb))
     for h in range(Hkv):
-        for qb in range(nqb):
+        for qb in (range(nqb) if qblocks is None else qblocks):
             rows = np.arange(qb * Bq, min(Lq, (qb + 1) * Bq))
             P = _mala_rows(q, k, win, scale, h, rows, G, Lq)
             for kb in range(nkb):
@@ -356,21 +357,26 @@ def mala_tile_mass(q, k, win, scale, Bq, Bk):
     return mass
 
 
-def mala_fwd(q, k, v, win, scale, tau, Bq, Bk, kept=None):
+def mala_fwd(q, k, v, win, scale, tau, Bq, Bk, kept=None, qblocks=None):
     """MALA forward: O [1, Lq, Hq, D] and the full LSE [1, Hq, Lq]; kept[h, qb, kb]
-    (bool) is taken from the tile masses (mass >= tau) unless given.  -> O, LSE, kept"""
+    (bool) is taken from the tile masses (mass >= tau) unless given.  With `qblocks`, only
+    the rows of those q-blocks are computed (O and LSE stay 0 elsewhere).
+    -> O, LSE, kept"""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Lq, Hq, D = q.shape
     _, Lk, Hkv, _ = k.shape
     assert B == 1
     G = Hq // Hkv
-    if kept is None:
-        kept = mala_tile_mass(q, k, win, scale, Bq, Bk) >= tau
-    _, LSE = attn_fwd(q, k, v, win, scale)
-    O = np.zeros((1, Lq, Hq, D))
     nqb = -(-Lq // Bq)
+    qbs = list(range(nqb)) if qblocks is None else list(qblocks)
+    if kept is None:
+        kept = mala_tile_mass(q, k, win, scale, Bq, Bk, qblocks=qblocks) >= tau
+    rows_all = np.concatenate([np.arange(qb * Bq, min(Lq, (qb + 1) * Bq)) for qb in qbs])
+    LSE = np.zeros((1, Hq, Lq))
+    LSE[:, :, rows_all] = attn_fwd(q, k, v, win, scale, rows=rows_all)[1]
+    O = np.zeros((1, Lq, Hq, D))
     for h in range(Hkv):
-        for qb in range(nqb):
+        for qb in qbs:
             rows = np.arange(qb * Bq, min(Lq, (qb + 1) * Bq))
             P = _mala_rows(q, k, win, scale, h, rows, G, Lq)
             keep_keys = np.repeat(np.asarray(kept[h, qb], dtype=bool), Bk)[:Lk]

@@ -152,6 +152,30 @@ def fwd(q, k, v, win, scale=None, plan=None, out=None, lse=None, o_lo=None):
     return out, lse
 
 
+def mala_fwd(q, k, v, win, tau, scale=None, plan=None, out=None, lse=None, kept=None):
+    """MALA forward (cowa_mala_fwd): -> (o like q, lse [B,Hq,Lq] fp32).  kept: optional
+    int32 tensor of the plan's nnz entries, filled with the per-tile keep decisions."""
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    scale = D ** -0.5 if scale is None else scale
+    prob = problem(B, Lq, Lk, Hq, Hkv, D, q.dtype, scale, win)
+    _check_tensor("q", q, (B, Lq, Hq, D), q.dtype)
+    _check_tensor("k", k, (B, Lk, Hkv, D), q.dtype, q.device)
+    _check_tensor("v", v, (B, Lk, Hkv, D), q.dtype, q.device)
+    plan = build_plan("fwd", prob, q.device) if plan is None else plan
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor("out", out, (B, Lq, Hq, D), q.dtype, q.device)
+    _check_tensor("lse", lse, (B, Hq, Lq), torch.float32, q.device)
+    if kept is not None:
+        _check_tensor("kept", kept, (max(1, plan.info.nnz),), torch.int32, q.device)
+    C.check("cowa_mala_fwd", C.lib.cowa_mala_fwd(
+        ctypes.byref(prob), ctypes.byref(plan.struct), float(tau), q.data_ptr(), k.data_ptr(),
+        v.data_ptr(), out.data_ptr(), lse.data_ptr(), None if kept is None else kept.data_ptr(),
+        _stream(q.device)))
+    return out, lse
+
+
 def bwd(q, k, v, o, lse, dout, win, scale=None, plan=None, grads=None, workspace=None,
         stages=C.COWA_BWD_ALL, o_lo=None):
     """Backward: -> (dq like q, dk like k, dv like v).  `stages` as in cowa_bwd; o_lo is

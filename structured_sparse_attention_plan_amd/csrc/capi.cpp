@@ -234,6 +234,46 @@ extern "C" int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan, const 
   return hip_status(launch_fwd_bf16_d128(a, s));
 }
 
+extern "C" int cowa_mala_fwd(const cowa_problem* p, const cowa_plan_dev* plan, float tau, const void* q,
+                             const void* k, const void* v, void* o, float* lse, int32_t* kept,
+                             void* stream) {
+  int st = check_problem(p);
+  if (st != COWA_OK) return st;
+  if (p->dtype != COWA_DTYPE_BF16) return COWA_ERR_UNSUPPORTED;
+  st = check_op_support(COWA_OP_FWD, p);
+  if (st != COWA_OK) return st;
+  if (!q || !k || !v || !o || !lse || !(tau >= 0.f)) return COWA_ERR_INVALID_ARG;
+  st = check_plan(COWA_OP_FWD, p, plan, false);
+  if (st != COWA_OK) return st;
+  FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.row_ptr = plan->row_ptr;
+  a.row_ent = plan->row_ent;
+  a.row_order = plan->row_order;
+  a.B = p->B;
+  a.Lq = p->Lq;
+  a.Lk = p->Lk;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.G = p->Hq / p->Hkv;
+  a.nqb = plan->info.nqb;
+  a.nkb = plan->info.nkb;
+  a.n_items = p->Hkv * plan->info.nqb;
+  a.Bq = plan->info.Bq;
+  a.Bk = plan->info.Bk;
+  a.scale = p->scale;
+  a.scale_log2 = p->scale * 1.44269504088896340736f;
+  a.win = dev_window(p->win);
+  a.mala_tau = tau;
+  a.kept = (p->B == 1) ? kept : nullptr;
+  if (kept && p->B != 1) return COWA_ERR_INVALID_ARG;
+  return hip_status(launch_mala_fwd_bf16_d128(a, (hipStream_t)stream));
+}
+
 extern "C" int cowa_bwd(const cowa_problem* p, const cowa_plan_dev* plan, const void* q, const void* k,
                         const void* v, const void* o, const void* o_lo, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, int stages, void* workspace,

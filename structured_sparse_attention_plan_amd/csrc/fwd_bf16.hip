@@ -105,6 +105,11 @@ __device__ __forceinline__ void mfma_v0(f32x16& acc, const bf16x8& a, const bf16
 }
 
 
+// MODE 0: the CoWA forward.  MODE 1: scoring only (no PV): LSE over every visible key.
+// MODE 2: the MALA pass, given that LSE: P = exp(scale s - LSE) exactly normalised, a
+// tile's PV is issued only when some row of the work item puts at least tau of its
+// probability mass in it, O = sum of the kept P V (no division), LSE left as it is.
+template <int MODE>
 __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 sQ[ROWS * D];
   // K and V double buffers, one array per buffer: the tile parity is known at compile
@@ -114,6 +119,8 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 sK1[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV0[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV1[TILE];
+  // MALA: the largest row mass of each wave in the last two tiles (by tile parity)
+  __shared__ float sMass[2][WAVES];
   auto kbuf = [&](auto c) __attribute__((always_inline)) -> __bf16* {
     if constexpr ((decltype(c)::value & 1) == 0) return sK0;
     else return sK1;
@@ -360,6 +367,16 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   // buffers of K(t) and V(t-2), which every wave finished with in iteration t-1.
   f32x16 sx[2][KB2][CB];
   bf16x8 pf[2][KB2][CB][2];
+  // MALA: the keep decision of tile `tile` from the waves' masses of that tile, uniform
+  // across the work group (read after the barrier that follows their writes)
+  auto mala_keep = [&](int tile) __attribute__((always_inline)) {
+    const float* mp = sMass[tile & 1];
+    const float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+    const bool keep = __builtin_amdgcn_readfirstlane(mx >= a.mala_tau ? 1 : 0) != 0;
+    if (a.kept && tid == 0) a.kept[e0 + tile] = keep ? 1 : 0;
+    return keep;
+  };
+
   auto iteration = [&](auto parity, int t) __attribute__((always_inline)) {
     constexpr int PAR = decltype(parity)::value;
     f32x16(&sc)[KB2][CB] = sx[PAR];      // S(t)
@@ -367,6 +384,9 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     bf16x8(&pfc)[KB2][CB][2] = pf[PAR];
     const bf16x8(&pfp)[KB2][CB][2] = pf[PAR ^ 1];
     wait_loads_and_barrier();  // K(t+1), V(t-1) resident; every wave is done with t-1
+    // MALA: PV of tile t-1 only when the tile is kept (none before the first tile)
+    bool keep_pv = MODE == 0;
+    if constexpr (MODE == 2) keep_pv = t > 0 && mala_keep(t - 1);
     const __amdgpu_buffer_rsrc_t rk = tile_copy_rsrc(kbase, ent2, t + 2 < nt);
     const __amdgpu_buffer_rsrc_t rv = tile_copy_rsrc(vbase, ent0, true);
     __bf16* const kdst = kbuf(IC<PAR>{});          // K(t+2)
@@ -394,8 +414,10 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     };
     load_step(0, kq[0]);
     bf16x8 vf[3];
-    vf[0] = vfrag(vt, vofs, 0, 0, 0);
-    vf[1] = vfrag(vt, vofs, 0, 0, 1);
+    if constexpr (MODE == 0) {
+      vf[0] = vfrag(vt, vofs, 0, 0, 0);
+      vf[1] = vfrag(vt, vofs, 0, 0, 1);
+    }
     mask_rows(sc, 0, ent_t);
     mask_rows(sc, 1, ent_t);
 
@@ -414,6 +436,13 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
         pin_out(dst);
       }
     };
+    // the block of 64 slots, with (PV = 1) or without (PV = 0) the O^T += V^T P^T products
+    auto slots = [&](auto pvc) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pvc)::value != 0;
+    if constexpr (PV && MODE == 2) {
+      vf[0] = vfrag(vt, vofs, 0, 0, 0);
+      vf[1] = vfrag(vt, vofs, 0, 0, 1);
+    }
     float xin = (sc[0][0][0]);
     static_for<0, 64>([&](auto slot) __attribute__((always_inline)) {
       constexpr int s = decltype(slot)::value;
@@ -424,7 +453,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
         // the first product of an accumulator (dd = 0) starts from zero
         if constexpr (dd == 0) mfma_v0(sn[k2][c], kq[dd & 1][k2], kq[dd & 1][2 + c]);
         else mfma_v(sn[k2][c], kq[dd & 1][k2], kq[dd & 1][2 + c]);
-      } else {
+      } else if constexpr (PV) {
         // MFMA k = s / 2 covers operand group g = k / 2 ((k2, hf) = g / 4, db = g % 4)
         // and row block c = k % 2; the V^T operand of group g + 2 is read at the first
         // MFMA of group g
@@ -439,7 +468,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
       if constexpr ((s & 7) == 5) {
         constexpr int u = s >> 3;  // 0..7: K(t+2) copies, then V(t) copies
         if constexpr (u < 4) copy_tile(rk, u, kdst);
-        else copy_tile(rv, u - 4, vdst);
+        else if constexpr (MODE != 1) copy_tile(rv, u - 4, vdst);  // scoring reads no V
       }
       __builtin_amdgcn_sched_barrier(0);
       {
@@ -459,8 +488,28 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+    };
+    if constexpr (MODE == 0) slots(IC<1>{});
+    else if constexpr (MODE == 1) slots(IC<0>{});
+    else {
+      if (keep_pv) slots(IC<1>{});
+      else slots(IC<0>{});
+    }
     fold(IC<62>{});
     fold(IC<63>{});
+
+    if constexpr (MODE == 2) {
+      // the tile's row masses (both lane halves of a column), their max over the wave's
+      // 64 rows for the keep decision at the next barrier; no reference to move: P is
+      // normalised by the given LSE
+      float mx = 0.f;
+#pragma unroll
+      for (int c = 0; c < CB; ++c) mx = fmaxf(mx, sum[c] + swap_halves(sum[c]));
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      if (lane == 0) sMass[PAR][wave] = mx;
+      return;
+    }
 
     // reference check on the column sums (both lane halves)
     float alpha[CB] = {1.f, 1.f};
@@ -538,34 +587,47 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     wait_loads_and_barrier();
     // S(0), masked, sets the first reference: its column max (exact P = 1 for the
     // column's top key, so a column that sees one key reproduces its V row), or 0 for a
-    // column with no visible key in tile 0
+    // column with no visible key in tile 0.  MALA: the reference is the given LSE (P
+    // exactly normalised; +inf for rows without a token or a visible key: P = 0)
     scores(sx[0]);
     mask_rows(sx[0], 0, ent0);
     mask_rows(sx[0], 1, ent0);
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
-      float mx = -INFINITY;
+      if constexpr (MODE == 2) {
+        const float lv = rvalid[c] ? a.lse[((int64_t)b * a.Hq + hq[c]) * a.Lq + tok[c]] : -INFINITY;
+        m[c] = lv == -INFINITY ? INFINITY : lv * kLog2e;
+      } else {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) mx = fmaxf(mx, sx[0][e >> 4][c][e & 15]);
-      const float mt = fmaxf(mx, swap_halves(mx)) * a.scale_log2;
-      m[c] = mt > -INFINITY ? mt : 0.f;
+        for (int e = 0; e < 32; ++e) mx = fmaxf(mx, sx[0][e >> 4][c][e & 15]);
+        const float mt = fmaxf(mx, swap_halves(mx)) * a.scale_log2;
+        m[c] = mt > -INFINITY ? mt : 0.f;
+      }
     }
     for (int t = 0; t < nt; t += 2) {
       iteration(IC<0>{}, t);
       if (t + 1 < nt) iteration(IC<1>{}, t + 1);
     }
     wait_loads_and_barrier();  // V(nt-1) resident
-    if ((nt - 1) & 1) last_pv(IC<1>{});
-    else last_pv(IC<0>{});
+    if constexpr (MODE != 1) {
+      if (MODE == 0 || mala_keep(nt - 1)) {
+        if ((nt - 1) & 1) last_pv(IC<1>{});
+        else last_pv(IC<0>{});
+      }
+    }
   }
 
-  // ---- finalize: l summed over the two lane halves of a column
+  // ---- finalize: l summed over the two lane halves of a column (MALA: P was normalised,
+  // O is the plain sum; scoring writes only LSE)
   __bf16* O = (__bf16*)a.o;
 #pragma unroll
   for (int c = 0; c < CB; ++c) {
     float lt = l[c] + __shfl_xor(l[c], 32);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (rvalid[c]) {
+    const float inv = MODE == 2 ? 1.f : lt > 0.f ? 1.f / lt : 0.f;
+    if (MODE == 1 && rvalid[c] && h2 == 0)
+      a.lse[((int64_t)b * a.Hq + hq[c]) * a.Lq + tok[c]] = lt > 0.f ? (m[c] + log2f(lt)) * kLn2 : -INFINITY;
+    if (MODE != 1 && rvalid[c]) {
       const int64_t oo = (((int64_t)b * a.Lq + tok[c]) * a.Hq + hq[c]) * D + 4 * h2;
       __bf16* op = O + oo;
 #pragma unroll
@@ -583,7 +645,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
             *(u32x2*)((__bf16*)a.o_lo + oo + 32 * db + 8 * q4) = __builtin_bit_cast(u32x2, r);
           }
         }
-      if (h2 == 0)
+      if (MODE == 0 && h2 == 0)
         a.lse[((int64_t)b * a.Hq + hq[c]) * a.Lq + tok[c]] =
             lt > 0.f ? (m[c] + log2f(lt)) * kLn2 : -INFINITY;
     }
@@ -594,7 +656,16 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
 
 hipError_t launch_fwd_bf16_d128(const FwdArgs& a, hipStream_t s) {
   dim3 grid(a.n_items, a.B);
-  hipLaunchKernelGGL(fwd_bf16_d128_kernel, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(fwd_bf16_d128_kernel<0>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mala_fwd_bf16_d128(const FwdArgs& a, hipStream_t s) {
+  dim3 grid(a.n_items, a.B);
+  hipLaunchKernelGGL(fwd_bf16_d128_kernel<1>, grid, dim3(256), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(fwd_bf16_d128_kernel<2>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

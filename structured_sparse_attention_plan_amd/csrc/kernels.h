@@ -33,6 +33,8 @@ struct FwdArgs {
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   DevWindow win;
+  float mala_tau;    // MALA: keep a tile when some row's probability mass in it is >= tau
+  int32_t* kept;     // MALA: per row-list entry, 1 if the tile's PV was done (may be null)
 };
 
 struct BwdArgs {
@@ -104,6 +106,7 @@ struct WcacheAppendArgs {
 
 hipError_t launch_fwd_f32_d64(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16_d128(const FwdArgs& a, hipStream_t s);
+hipError_t launch_mala_fwd_bf16_d128(const FwdArgs& a, hipStream_t s);  // scoring, then the gated pass
 hipError_t launch_bwd_bf16_d128(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t s);  // varlen when a.seqlens
 hipError_t launch_wcache_append(const WcacheAppendArgs& a, hipStream_t s);

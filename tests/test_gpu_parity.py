@@ -503,3 +503,100 @@ def test_fwd_residual_is_what_bf16_rounding_drops():
     lo, hi = o_lo.double().abs(), o2.double().abs()
     assert bool((lo <= hi * 2.0 ** -8 + 1e-30).all())
     assert e_sum < e_hi
+
+
+# ----------------------------------------------------------------------------- MALA
+
+def _plan_tiles(plan):
+    """(h, qb, kb) of every entry of a device plan's row lists, in entry order."""
+    rp = plan.host.arrays["row_ptr"]
+    ent = plan.host.arrays["row_ent"]
+    nqb = plan.info.nqb
+    out = []
+    for item in range(len(rp) - 1):
+        h, qb = divmod(item, nqb)
+        for e in range(rp[item], rp[item + 1]):
+            out.append((h, qb, int(ent[e]) >> 1))
+    return out
+
+
+def mala_check(q, k, v, ow, win, tau, qblocks=None, Bk=64):
+    """Run the MALA forward and compare: the keep decisions with the oracle's (bit for bit
+    except for tiles whose oracle mass lies within 1e-4 of tau, where the fp32 and fp64
+    sums may fall either side), O with the oracle evaluated with the kernel's decisions,
+    and LSE with the full scoring."""
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    prob = api.problem(B, L, L, Hq, Hkv, D, torch.bfloat16, D ** -0.5, win)
+    plan = api.build_plan("fwd", prob, DEV)
+    Bq = plan.info.Bq
+    kept = torch.full((max(1, plan.info.nnz),), -1, dtype=torch.int32, device=DEV)
+    o, lse = api.mala_fwd(qd, kd, vd, win, tau, plan=plan, kept=kept)
+    torch.cuda.synchronize()
+    tiles = _plan_tiles(plan)
+    kg = kept.cpu().numpy()[:len(tiles)]
+    assert set(np.unique(kg)) <= {0, 1}, "every listed tile gets a decision"
+    mass = oracle.mala_tile_mass(q, k, ow, D ** -0.5, Bq, Bk, qblocks=qblocks)
+    nqb = plan.info.nqb
+    kept_gpu = np.ones((Hkv, nqb, -(-L // Bk)), dtype=bool)  # unlisted tiles see nothing
+    n_cmp = n_amb = 0
+    for (h, qb, kb), g in zip(tiles, kg):
+        kept_gpu[h, qb, kb] = bool(g)
+        if qblocks is not None and qb not in qblocks:
+            continue
+        if abs(mass[h, qb, kb] - tau) <= 1e-4:
+            n_amb += 1
+            continue
+        n_cmp += 1
+        assert bool(g) == (mass[h, qb, kb] >= tau), (h, qb, kb, mass[h, qb, kb], g)
+    n_kept = int(kg.sum())
+    print(f"  tau={tau}: {n_kept} of {len(tiles)} tiles kept; {n_cmp} decisions compared, "
+          f"{n_amb} within 1e-4 of tau", flush=True)
+    Oo, Lo, _ = oracle.mala_fwd(q, k, v, ow, D ** -0.5, tau, Bq, Bk, kept=kept_gpu, qblocks=qblocks)
+    if qblocks is None:
+        assert_bf16_close("O", o, Oo)
+        assert_bf16_close("LSE", lse, Lo)
+    else:
+        rows = np.concatenate([np.arange(qb * Bq, min(L, (qb + 1) * Bq)) for qb in qblocks])
+        idx = torch.as_tensor(rows, device=DEV)
+        assert_bf16_close("O[sampled q-blocks]", o[:, idx], Oo[:, rows])
+        assert_bf16_close("LSE[sampled q-blocks]", lse[:, :, idx], Lo[:, :, rows])
+    return o, lse, n_kept, len(tiles)
+
+
+@pytest.mark.parametrize("L,Hq,Hkv,mode,tau", [
+    (700, 40, 8, "dense", 0.0),
+    (700, 40, 8, "dense", 0.02),
+    (700, 40, 8, "dense", 0.1),
+    (700, 40, 8, "dense", 1.5),
+    (900, 16, 2, "dense", 0.05),
+    (1000, 40, 8, "complementary", 0.05),
+])
+def test_mala_fwd(L, Hq, Hkv, mode, tau):
+    _case(f"MALA fwd L={L} Hq={Hq} Hkv={Hkv} {mode} tau={tau}")
+    ow, win = _windows(L, Hkv, 16, 64, mode=mode)
+    q, k, v = inputs.attention_inputs(1, L, L, Hq, Hkv, 128, seed=40)
+    o, lse, n_kept, n_tiles = mala_check(q, k, v, ow, win, tau)
+    if tau == 0.0:
+        assert n_kept == n_tiles
+    if tau > 1.0:
+        assert n_kept == 0 and bool((o == 0).all())
+    else:
+        assert 0 < n_kept
+
+
+def test_mala_fwd_32k_dense_sampled_qblocks():
+    """Full causal MALA at 32K tokens: decisions of 16 sampled q-blocks (all heads, every
+    key block) and their rows' O and LSE against the oracle."""
+    L, Hq, Hkv = 32768, 40, 8
+    _case(f"MALA fwd L={L} dense tau=0.004, sampled q-blocks")
+    ow = oracle.Window.for_length(L, Hkv, 128, 2048, 0, mode="dense")
+    win = api.window(ow.sink, ow.near, ow.gap, ow.lr, "dense")
+    q, k, v = inputs.attention_inputs(1, L, L, Hq, Hkv, 128, seed=41, device=DEV)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    Bq = 256 // (Hq // Hkv)
+    nqb = -(-L // Bq)
+    rng = np.random.default_rng(141)
+    qblocks = sorted({0, 1, nqb - 1} | set(int(x) for x in rng.choice(nqb, 13, replace=False)))
+    mala_check(qc, kc, vc, ow, win, 0.004, qblocks=qblocks)
