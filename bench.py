@@ -214,6 +214,36 @@ def _events_ms(fn, steps, warmup):
     return float(sum(a.elapsed_time(b) for a, b in ts) / len(ts))
 
 
+def mala_32k(seed, taus=(0.0, 0.002, 0.004, 0.01)):
+    """MALA forward (cowa_mala_fwd) at 32768 tokens with full causal scoring: ms per call
+    (scoring pass + gated pass) and the share of tiles whose PV was done, per tau, beside
+    the dense causal forward (cowa_fwd) and the scoring pass alone."""
+    import torch
+    from structured_sparse_attention_plan_amd import api, inputs
+    dev, L = "cuda:0", 32768
+    win = api.make_window(L, HKV, SINK, 2048, 0, "dense")
+    pf = api.problem(1, L, L, HQ, HKV, D, torch.bfloat16, D ** -0.5, win)
+    plan = api.build_plan("fwd", pf, dev)
+    q, k, v = inputs.attention_inputs(1, L, L, HQ, HKV, D, seed=seed, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, HQ, L), dtype=torch.float32, device=dev)
+    kept = torch.empty(plan.info.nnz, dtype=torch.int32, device=dev)
+    E = plan.info.edges * (HQ // HKV)
+    r = {"window": "dense (full causal scoring)", "edges": E, "tiles": plan.info.nnz,
+         "dense_fwd_ms": _events_ms(lambda: api.fwd(q, k, v, win, plan=plan, out=o, lse=lse), 5, 2)}
+    r["mala_scoring_only_tau_above_1_ms"] = _events_ms(
+        lambda: api.mala_fwd(q, k, v, win, 2.0, plan=plan, out=o, lse=lse), 5, 2)
+    r["by_tau"] = {}
+    for tau in taus:
+        ms = _events_ms(lambda: api.mala_fwd(q, k, v, win, tau, plan=plan, out=o, lse=lse, kept=kept), 5, 2)
+        torch.cuda.synchronize()
+        r["by_tau"][str(tau)] = {"ms": ms, "kept_share": float(kept.float().mean().item()),
+                                 "vs_dense_fwd": r["dense_fwd_ms"] / ms}
+    del q, k, v, o, lse, kept
+    torch.cuda.empty_cache()
+    return r
+
+
 def extras(seed, main_fb_ms, main_fwd_ms, main_bwd_ms, main_dec_ms, main_E, main_dec_bytes):
     """Secondary workloads timed with the same kernels: the 32K forward, the 32K coverage
     ablation (complementary / duplicated / dense bands, forward + backward), dense causal
@@ -262,6 +292,9 @@ def extras(seed, main_fb_ms, main_fwd_ms, main_bwd_ms, main_dec_ms, main_E, main
     # 32K prefill forward
     out["fwd_32k"] = fwd_bwd(32768, 2048, "complementary", bwd=False, steps=10, warmup=3)
     out["fwd_32k"]["frac_of_mfma_peak"] = out["fwd_32k"]["fwd_tflops"] / MFMA_BF16_PEAK_TFLOPS
+    # MALA at 32K, full causal scoring (dense window, as the pages describe it): the two
+    # passes at several tau, the kept share of the tiles, against the dense causal forward
+    out["mala_32k"] = mala_32k(seed)
     # coverage ablation at 32K, forward + backward
     abl = {m: fwd_bwd(32768, 2048, m, steps=5, warmup=2)
            for m in ("complementary", "duplicated", "dense")}

@@ -429,6 +429,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     auto fold = [&](auto pi) __attribute__((always_inline)) {
       constexpr int p = decltype(pi)::value, pc = p >> 5, pe = p & 31;
       sum[pc] += pb[p & 7];
+      if constexpr (MODE == 1) return;  // scoring only: no PV operand
       if constexpr ((p & 1) == 1) pw[(p & 7) >> 1] = bf16_pair(pb[(p - 1) & 7], pb[p & 7]);
       if constexpr ((p & 7) == 7) {
         bf16x8& dst = pfc[pe >> 4][pc][(pe >> 3) & 1];
