@@ -36,7 +36,7 @@ DEC_B = 16
 # used only while these files are unchanged.
 KERNEL_SOURCES = {
     "fwd": ["fwd_bf16.hip"], "bwd_dq": ["bwd_bf16.hip"], "bwd_dkdv": ["bwd_bf16.hip"],
-    "decode": ["decode_bf16.hip"],
+    "decode": ["decode_bf16.hip", "wcache.h"],
 }
 COMMON_SOURCES = ["device_common.h", "kernels.h"]
 KERNEL_SYMBOL = {"fwd": "fwd_bf16_d128_kernel", "bwd_dq": "bwd_dq_kernel",
