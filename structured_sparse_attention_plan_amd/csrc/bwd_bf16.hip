@@ -10,8 +10,9 @@
 //   delta  : Delta per (row, query head), and an fp16 copy of Q scaled per row by a
 //            power of two;
 //   dq     : one work item per (KV head, q-block of 128 / G tokens), walking the row list
-//            of visible 128-key blocks: S^T, dP^T, dS^T on MFMA, dQ^T += K^T dS^T with
-//            K^T read by ds_read_b64_tr_b16 from the row-major LDS tile;
+//            of visible 128-key blocks: S^T, dP^T on MFMA, dS^T on the VALU,
+//            dQ^T += K^T dS^T with K^T read by ds_read_b64_tr_b16 from the row-major LDS
+//            tile; two work groups per CU;
 //   dkdv   : one work item per (KV head, 128-key block), walking the column list of
 //            visible q-blocks; each of the 4 waves keeps 32 keys of K and V in registers
 //            and accumulates dK, dV for them over all G query heads of the KV head:
@@ -213,33 +214,28 @@ __device__ __forceinline__ void mfma_bf16_va0(f32x16& acc, const bf16x8& a, cons
 }
 
 // ------------------------------------------------------------------------ dQ
-// One work item = (KV head, q-block of 128 rows), 4 waves x 32 rows; each lane owns one
-// query row (column of the transposed products) and keeps its Q and dO fragments in
-// AGPRs (the B operands of S^T and dP^T, whose accumulators are VGPRs).  The item walks
-// its row list as 64-key tiles t (two per listed 128-key
-// block).  Iteration t is one block of 48 MFMAs, the dQ^T += K^T dS^T products of tile
-// t-1 (16) then S^T = K Q^T and dP^T = V dO^T of tile t+1 (32), with the VALU work of
-// tile t (P, dS and their bf16 packing) spread between them by scheduling fences.  K
-// and V tiles are copied straight into LDS two tiles ahead: four K buffers (tiles t-1,
-// t+1 read, t+2 arriving) and two V buffers (t+1 read, t+2 arriving), each its own
-// array, indexed at compile time (the tile loop is unrolled by 4), so the compiler can
-// tell the reads from the copies in flight.
 constexpr int QBK = 64;          // keys per tile
 constexpr int QTL = QBK * D;     // elements per K or V tile (16 KB)
 
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
+// One work item = (KV head, q-block of 128 rows), 4 waves x 32 rows; each lane owns one
+// query row (column of the transposed products) and keeps its Q (fp16) and dO fragments
+// in AGPRs as the B operands of S^T and dP^T, whose accumulators are VGPRs.  The item
+// walks its row list as 64-key tiles (two per listed 128-key block).  Sized for two work
+// groups per CU (64 KB of LDS, at most 256 registers per wave), so each SIMD holds two
+// waves and interleaves one wave's MFMAs with the other's VALU work and LDS reads; the
+// compiler schedules the products (a hand-pipelined one-wave-per-SIMD version with 96 KB
+// of LDS took about 2.5% longer).  Per tile t (K(t), V(t) resident in buffer t % 2, the
+// direct copies of tile t + 1 in flight into the other): for each 32-key half, S^T = K Q^T
+// (fp16) and dP^T = V dO^T (bf16), then P and dS on the VALU, then dQ^T += K^T dS^T (fp16)
+// with K^T read by ds_read_b64_tr_b16 from the row-major tile.
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16384))) __bf16 sK0[QTL];
   __shared__ __attribute__((aligned(16384))) __bf16 sK1[QTL];
-  __shared__ __attribute__((aligned(16384))) __bf16 sK2[QTL];
-  __shared__ __attribute__((aligned(16384))) __bf16 sK3[QTL];
   __shared__ __attribute__((aligned(16384))) __bf16 sV0[QTL];
   __shared__ __attribute__((aligned(16384))) __bf16 sV1[QTL];
   auto kbuf = [&](auto c) -> __bf16* {
-    constexpr int i = decltype(c)::value & 3;
-    if constexpr (i == 0) return sK0;
-    else if constexpr (i == 1) return sK1;
-    else if constexpr (i == 2) return sK2;
-    else return sK3;
+    if constexpr ((decltype(c)::value & 1) == 0) return sK0;
+    else return sK1;
   };
   auto vbuf = [&](auto c) -> __bf16* {
     if constexpr ((decltype(c)::value & 1) == 0) return sV0;
@@ -248,7 +244,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: copy targets form on the SALU
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int h2 = lane >> 5;
   const int item = load_uniform(a.row_order, blockIdx.x);
@@ -264,32 +260,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   const __bf16* V = (const __bf16*)a.v;
   const __bf16* dO = (const __bf16*)a.dout;
 
-  // Key rows past Lk are outside the copies' range: their LDS keeps what it held.  Cleared
-  // once here, it only ever holds zeros or earlier finite rows, which the mask hides.
+  // key rows past Lk keep what LDS held: cleared once, they only hold zeros or earlier
+  // finite rows, which the mask hides
 #pragma unroll
   for (int i = 0; i < QTL / (256 * 8); ++i) {
     const int o = 8 * (tid + 256 * i);
     store16(sK0 + o, zero_bf16x8());
     store16(sK1 + o, zero_bf16x8());
-    store16(sK2 + o, zero_bf16x8());
-    store16(sK3 + o, zero_bf16x8());
     store16(sV0 + o, zero_bf16x8());
     store16(sV1 + o, zero_bf16x8());
   }
-  __syncthreads();  // cleared before any copy lands
+  __syncthreads();
 
-  // this lane's query row
+  // this lane's query row and its constants (as in bwd_dq_kernel)
   const int r = wave * 32 + n;
   const int rt = r / G;
   const int t = qb * Bq + rt;
   const int hq = h * G + (r - rt * G);
   const bool rvalid = (rt < Bq) && (t < a.Lq);
   const int p = t + off;
-  // S = K16 Q16^T runs in fp16 on the scaled copies (K / 2^gK, q / 2^e_r), so the lane's
-  // exp2 factor is crow = scale log2(e) 2^(gK + e_r).  dS enters the dQ product in fp16
-  // as dS 2^s_r, with s_r chosen so that the row's bound |dO_r| max|v| + |Delta_r| on |dS|
-  // lands below 2^14 (four times inside the fp16 range): dS16 = P (dP fq - tq) with
-  // fq = 2^s_r and tq = Delta_r 2^s_r, and dQ = scale 2^(gK - s_r) dQ16.
   const int gk = pow2_exponent(a.maxima[3]);
   float lse2 = INFINITY, dlt = 0.f, crow = __builtin_amdgcn_ldexpf(a.scale_log2, gk), fq = 1.f, tq = 0.f;
   float dq_out = 0.f;
@@ -310,7 +299,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     for (int dd = 0; dd < 8; ++dd) qf[dd] = df[dd] = zero_bf16x8();
   }
   {
-    float dn = 0.f;  // |dO_r|^2: the two lane halves hold 64 dimensions each
+    float dn = 0.f;
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
       const u32x4 w = __builtin_bit_cast(u32x4, df[dd]);
@@ -327,11 +316,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     tq = dlt * fq;
     dq_out = __builtin_amdgcn_ldexpf(a.scale, gk - se);
   }
-  // held in AGPRs as the B operands of the S, dP products: the VGPRs hold those products'
-  // accumulators
 #pragma unroll
   for (int dd = 0; dd < 8; ++dd) asm volatile("" : "+a"(qf[dd]), "+a"(df[dd]));
-  if (lse2 == -INFINITY) lse2 = INFINITY;  // a row with no visible key has P = 0
+  if (lse2 == -INFINITY) lse2 = INFINITY;
 
   f32x16 acc[4];
 #pragma unroll
@@ -339,20 +326,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  // LDS offsets (elements) inside a tile, as in the dK/dV kernel: operand reads of key row
-  // 32 k2 + n, columns 16 dd + 8 h2 (base XOR dd << 4); transposed reads of key rows
-  // 16 (2 k2 + hf) + vrow (+8), columns 32 db + vcol (base XOR db << 5).
   const int gg = lane >> 4, j16 = lane & 15;
   const int vrow = 4 * (gg >> 1) + (j16 >> 2);
   const int vcol = 16 * (gg & 1) + 4 * (j16 & 3);
-  int ofs_a0 = lds_swz(n, 8 * h2);
-  int ofs_t0[2] = {lds_swz(vrow, vcol), lds_swz(vrow + 8, vcol)};
+  const int ofs_a0 = lds_swz(n, 8 * h2);
+  const int ofs_t0[2] = {lds_swz(vrow, vcol), lds_swz(vrow + 8, vcol)};
   auto ofs_a = [&](int k2, int dd) { return 4096 * k2 + (ofs_a0 ^ (dd << 4)); };
   auto ofs_t = [&](int k2, int hf, int pp, int db) { return 2048 * (2 * k2 + hf) + (ofs_t0[pp] ^ (db << 5)); };
 
-  // Copies of a tile: wave w fills key rows 16 w .. 16 w + 15, 4 rows per copy; lane L of
-  // copy u fills row kr = 16 w + 4 u + L / 16, physical chunk L % 16 (logical chunk
-  // (L % 16) ^ lds_sw(kr)).  voff[u]: its byte offset from the tile's first key.
   const int HkvD = a.Hkv * D;
   uint32_t voff[4];
 #pragma unroll
@@ -360,201 +341,92 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     const int kr = 16 * wave + 4 * u + (lane >> 4);
     voff[u] = 2u * (uint32_t)(kr * HkvD + h * D + 8 * ((lane & 15) ^ lds_sw(kr)));
   }
-
   const int e0 = load_uniform(a.row_ptr, item);
   const int n_ent = load_uniform(a.row_ptr, item + 1) - e0;
   const int ntile = 2 * n_ent;
-  // first key of tile tt, and its entry; tiles past the list get an empty copy range
   auto tile_j0 = [&](int ent, int tt) { return (ent >> 1) * BK + (tt & 1) * QBK; };
-  __amdgpu_buffer_rsrc_t rk, rv;
-  // the batch's K / V base and byte count are formed once; per tile only the offset
   const int64_t kv_bytes = (int64_t)a.Lk * HkvD * 2;
   const char* const kbase = (const char*)(K16 + (int64_t)b * a.Lk * HkvD);
   const char* const vbase = (const char*)(V + (int64_t)b * a.Lk * HkvD);
-  auto prepare_copy = [&](int ent, int tt, bool real) {
-    const int64_t off = (int64_t)tile_j0(ent, tt) * (HkvD * 2);
-    rk = tile_rsrc(kbase, kv_bytes, off, real);
-    rv = tile_rsrc(vbase, kv_bytes, off, real);
-  };
-  auto copy = [&](int i, __bf16* kd, __bf16* vd) {  // copy i of 8 (u = i / 2, K then V)
-    const int u = i >> 1;
-    buf2lds((i & 1) ? rv : rk, voff[u], ((i & 1) ? vd : kd) + (16 * wave + 4 * u) * D);
-  };
-  // masked element: S = -inf where the key is hidden from the row
-  auto mask = [&](f32x16 (&s)[2], int j0) {
+  auto copy_tile = [&](int ent, int tt, __bf16* kd, __bf16* vd) {
+    const int64_t o = (int64_t)tile_j0(ent, tt) * (HkvD * 2);
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, kv_bytes, o, true);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase, kv_bytes, o, true);
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = j0 + 32 * k2 + 8 * (i >> 2) + 4 * h2 + (i & 3);
-        s[k2][i] = (rvalid & visible(p, j, a.Lk, a.win.sink, a.win.near_w, band)) ? s[k2][i] : -INFINITY;
-      }
+    for (int u = 0; u < 4; ++u) {
+      buf2lds(rk, voff[u], kd + (16 * wave + 4 * u) * D);
+      buf2lds(rv, voff[u], vd + (16 * wave + 4 * u) * D);
+    }
   };
 
   if (n_ent > 0) {
-    // entries of tiles t, t+1, t+2 (two tiles per entry).  The entry after them is
-    // fetched by a vector load (a scalar load would share its wait counter with the LDS
-    // operand reads) through a resource over this item's entries, so a fetch past the end
-    // reads 0 (only ever used for tiles that are not copied), and taken two tiles later.
     const __amdgpu_buffer_rsrc_t r_ent = make_rsrc(a.row_ent + e0, (int64_t)n_ent * 4);
-    int ent[3];
-    ent[0] = load_uniform(a.row_ent, e0);
-    ent[1] = ent[0];
-    ent[2] = n_ent > 1 ? load_uniform(a.row_ent, e0 + 1) : ent[0];
-    int ent_next = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * 2, 0);
+    int ent_cur = load_uniform(a.row_ent, e0);  // entry of tile tt
+    int ent_nxt = ent_cur;                      // entry of tile tt + 1
+    int ent_ahead = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * 1, 0);  // of tile 2
+    copy_tile(ent_cur, 0, sK0, sV0);
 
-    // prologue: tiles 0 and 1 resident; S, dP of tile 0
-    prepare_copy(ent[0], 0, true);
+    auto tile = [&](auto bufc, const int tt) {
+      constexpr int BUF = decltype(bufc)::value;
+      wait_loads_and_barrier();  // tile tt resident; every wave is done with tile tt - 1
+      if (tt + 1 < ntile) copy_tile(ent_nxt, tt + 1, kbuf(IC<BUF ^ 1>{}), vbuf(IC<BUF ^ 1>{}));
+      const __bf16* kt = kbuf(IC<BUF>{});
+      const __bf16* vt = vbuf(IC<BUF>{});
+      const int j0 = tile_j0(ent_cur, tt);
+      const bool partial = ent_cur & 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) copy(i, sK0, sV0);
-    prepare_copy(ent[1], 1, ntile > 1);
+      for (int k2 = 0; k2 < 2; ++k2) {
+        f32x16 sv, dv;
+        mfma_f16_va0(sv, load16(kt + ofs_a(k2, 0)), qf[0]);
+        mfma_bf16_va0(dv, load16(vt + ofs_a(k2, 0)), df[0]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) copy(i, sK1, sV1);
-    wait_loads_and_barrier();
-
-    f32x16 sA[2], dA[2], sB[2], dB[2];  // S^T, dP^T of two consecutive tiles (2 key blocks)
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      mfma_f16_va0(sA[k2], load16(sK0 + ofs_a(k2, 0)), qf[0]);
-      mfma_bf16_va0(dA[k2], load16(sV0 + ofs_a(k2, 0)), df[0]);
-#pragma unroll
-      for (int dd = 1; dd < 8; ++dd) {
-        mfma_f16_va(sA[k2], load16(sK0 + ofs_a(k2, dd)), qf[dd]);
-        mfma_bf16_va(dA[k2], load16(sV0 + ofs_a(k2, dd)), df[dd]);
-      }
-    }
-    uint32_t dsp[2][2][4];  // packed dS^T of the previous tile: [k2][hf] bf16x8 as 4 words
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) dsp[k2][hf][w] = 0u;
-
-    // One iteration for tile tt (tt % 4 = TC at compile time).  cur: S, dP of tile tt;
-    // nxt: S, dP of tile tt + 1 (computed here).
-    auto iteration = [&](auto tcc, const int tt, f32x16 (&cs)[2], f32x16 (&cd)[2], f32x16 (&ns)[2],
-                         f32x16 (&nd)[2]) {
-      constexpr int TC = decltype(tcc)::value;
-      wait_loads_and_barrier();  // tile tt + 1 resident; every wave done with tile tt - 1
-      // copies of tile tt + 2 (K into the buffer of tile tt - 2, V into that of tile tt)
-      prepare_copy(ent[2], tt + 2, tt + 2 < ntile);
-      __bf16* kd = kbuf(IC<(TC + 2) & 3>{});
-      __bf16* vd = vbuf(IC<TC & 1>{});
-      if (ent[0] & 1) mask(cs, tile_j0(ent[0], tt));
-      const __bf16* kq = kbuf(IC<(TC + 3) & 3>{});  // K of tile tt - 1 (dQ)
-      const __bf16* kn = kbuf(IC<(TC + 1) & 3>{});  // K of tile tt + 1 (S)
-      const __bf16* vn = vbuf(IC<(TC + 1) & 1>{});  // V of tile tt + 1 (dP)
-      float pr[2][16], dsv[2][16];
-      uint32_t npk[2][2][4];
-      // operands: transposed K of tile tt - 1 for the first 16 MFMAs, K / V rows of tile
-      // tt + 1 for the other 32, each read kLead MFMAs ahead
-      constexpr int kLead = 4;
-      bf16x8 opA[48];
-      auto load_op = [&](int x) {
-        if (x < 16) {
-          const int k2 = x >> 3, hf = (x >> 2) & 1, db = x & 3;
-          opA[x] = join(lds_read_tr4(kq + ofs_t(k2, hf, 0, db)), lds_read_tr4(kq + ofs_t(k2, hf, 1, db)));
-        } else {  // four chains (k2, S / dP) in rotation
-          const int y = x - 16, k2 = y & 1, dd = y >> 2;
-          opA[x] = load16((((y >> 1) & 1) ? vn : kn) + ofs_a(k2, dd));
+        for (int dd = 1; dd < 8; ++dd) {
+          mfma_f16_va(sv, load16(kt + ofs_a(k2, dd)), qf[dd]);
+          mfma_bf16_va(dv, load16(vt + ofs_a(k2, dd)), df[dd]);
         }
-      };
+        if (partial) {
 #pragma unroll
-      for (int x = 0; x < kLead; ++x) load_op(x);
-      float csv[2], cdv[2];  // S, dP elements taken one step before use
-      csv[0] = pin(cs[0][0]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int x = 0; x < 48; ++x) {
-        if (x + kLead < 48) load_op(x + kLead);
-        if (x < 16) {
-          const int k2 = x >> 3, hf = (x >> 2) & 1, db = x & 3;
-          const u32x4 w = {dsp[k2][hf][0], dsp[k2][hf][1], dsp[k2][hf][2], dsp[k2][hf][3]};
-          acc[db] = mfma32x32x16_f16(opA[x], __builtin_bit_cast(bf16x8, w), acc[db]);
-        } else {
-          // accumulators in VGPRs, each chain starting from zero (dd = 0)
-          const int y = x - 16, k2 = y & 1, dd = y >> 2;
-          if ((y >> 1) & 1) {
-            if (dd == 0) mfma_bf16_va0(nd[k2], opA[x], df[0]);
-            else mfma_bf16_va(nd[k2], opA[x], df[dd]);
-          } else {
-            if (dd == 0) mfma_f16_va0(ns[k2], opA[x], qf[0]);
-            else mfma_f16_va(ns[k2], opA[x], qf[dd]);
+          for (int i = 0; i < 16; ++i) {
+            const int j = j0 + 32 * k2 + 8 * (i >> 2) + 4 * h2 + (i & 3);
+            sv[i] = (rvalid & visible(p, j, a.Lk, a.win.sink, a.win.near_w, band)) ? sv[i] : -INFINITY;
           }
         }
-        if (x >= 4 && x < 12) copy(x - 4, kd, vd);
-        __builtin_amdgcn_sched_barrier(0);
-        // VALU of tile tt: element e = x (0..31) gets P in step x, dS in step x + 4; pairs
-        // are packed to bf16 in steps 32..47.  Inputs are taken (pin) one step before use
-        // and results fenced (pin_out) one step after they are made: a read right at a pin
-        // or a fence right after an exp costs a wait state each.
-        if (x < 32) pr[x >> 4][x & 15] = __builtin_amdgcn_exp2f(fmaf(csv[x & 1], crow, -lse2));
-        if (x + 1 < 32) csv[(x + 1) & 1] = pin(cs[(x + 1) >> 4][(x + 1) & 15]);
-        if (x >= 1 && x <= 32) pin_out(pr[(x - 1) >> 4][(x - 1) & 15]);
-        if (x >= 4 && x < 36) {
-          const int e = x - 4, k2 = e >> 4, i = e & 15;
-          dsv[k2][i] = pr[k2][i] * fmaf(cdv[e & 1], fq, -tq);
-        }
-        if (x >= 3 && x < 35) {
-          const int e = x - 3;
-          cdv[e & 1] = pin(cd[e >> 4][e & 15]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // dS pair q (elements 2 q, 2 q + 1) packed to fp16 at step 2 q + 7, after this
-        // step's own VALU work (its second element was fenced at the end of the previous
-        // step: a read right after the fence would cost a wait state), and fenced in turn
-        // a step later; pair q sits in word q % 4 of half (q / 4) % 2 of block q / 8
-        if (x >= 7 && x <= 37 && (x & 1)) {
-          const int q = (x - 7) >> 1, k2 = q >> 3, hf = (q >> 2) & 1, w = q & 3;
-          npk[k2][hf][w] = pack_f16x2(dsv[k2][2 * (q & 7)], dsv[k2][2 * (q & 7) + 1]);
-        }
-        if (x >= 8 && x <= 38 && (x & 1) == 0) {
-          const int q = (x - 8) >> 1;
-          pin_out(npk[q >> 3][(q >> 2) & 1][q & 3]);
-        }
-        if (x >= 5 && x <= 36) pin_out(dsv[(x - 5) >> 4][(x - 5) & 15]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
+        uint32_t w[2][4];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) dsp[k2][hf][w] = npk[k2][hf][w];
-      // advance the entry window at entry boundaries (two tiles per entry)
-      if (tt & 1) {
-        ent[0] = ent[2];
-        ent[1] = ent[2];
-        ent[2] = __builtin_amdgcn_readfirstlane(ent_next);
-        const int en = ((tt + 1) >> 1) + 2;  // entry of tile tt + 5
-        ent_next = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * en, 0);
+          for (int q = 0; q < 4; ++q) {
+            const int i0 = 8 * hf + 2 * q;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[i0], crow, -lse2));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[i0 + 1], crow, -lse2));
+            w[hf][q] = pack_f16x2(p0 * fmaf(dv[i0], fq, -tq), p1 * fmaf(dv[i0 + 1], fq, -tq));
+          }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{w[hf][0], w[hf][1], w[hf][2], w[hf][3]});
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const bf16x8 ka = join(lds_read_tr4(kt + ofs_t(k2, hf, 0, db)), lds_read_tr4(kt + ofs_t(k2, hf, 1, db)));
+            acc[db] = mfma32x32x16_f16(ka, dsb, acc[db]);
+          }
+        }
+      }
+      // advance the entries (tiles 2 e and 2 e + 1 share entry e): after an even tile the
+      // next tile's successor starts a new entry, fetched two tiles ago; after an odd tile
+      // it shares the next tile's entry
+      ent_cur = ent_nxt;
+      if ((tt & 1) == 0) {
+        ent_nxt = __builtin_amdgcn_readfirstlane(ent_ahead);
+        ent_ahead = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * ((tt >> 1) + 2), 0);
       } else {
-        ent[0] = ent[1];
+        ent_nxt = ent_cur;
       }
     };
-    int tt = 0;
-    for (; tt + 4 <= ntile; tt += 4) {
-      iteration(IC<0>{}, tt, sA, dA, sB, dB);
-      iteration(IC<1>{}, tt + 1, sB, dB, sA, dA);
-      iteration(IC<2>{}, tt + 2, sA, dA, sB, dB);
-      iteration(IC<3>{}, tt + 3, sB, dB, sA, dA);
+    for (int tt = 0; tt < ntile; tt += 2) {
+      tile(IC<0>{}, tt);
+      tile(IC<1>{}, tt + 1);  // ntile is even
     }
-    if (tt < ntile) {  // ntile is even: two more tiles
-      iteration(IC<0>{}, tt, sA, dA, sB, dB);
-      iteration(IC<1>{}, tt + 1, sB, dB, sA, dA);
-    }
-    // dQ of the last tile (its K sits in buffer (ntile - 1) % 4)
     __builtin_amdgcn_s_waitcnt(0x0f70);
-    const int lastc = (ntile - 1) & 3;
-    const __bf16* kl = lastc == 0 ? sK0 : lastc == 1 ? sK1 : lastc == 2 ? sK2 : sK3;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int k2 = x >> 3, hf = (x >> 2) & 1, db = x & 3;
-      const bf16x8 ka = join(lds_read_tr4(kl + ofs_t(k2, hf, 0, db)), lds_read_tr4(kl + ofs_t(k2, hf, 1, db)));
-      const u32x4 w = {dsp[k2][hf][0], dsp[k2][hf][1], dsp[k2][hf][2], dsp[k2][hf][3]};
-      acc[db] = mfma32x32x16_f16(ka, __builtin_bit_cast(bf16x8, w), acc[db]);
-    }
   }
 
   if (rvalid) {
