@@ -385,6 +385,40 @@ def mala_fwd(q, k, v, win, scale, tau, Bq, Bk, kept=None, qblocks=None):
     return O, LSE, kept
 
 
+def mala_bwd(q, k, v, do, win, scale, Bq, Bk, kept):
+    """Gradients of L = sum(O * dO) for the MALA forward with the tile decisions `kept`
+    held fixed (the function is smooth for fixed decisions): with P the full softmax and
+    K_ij = 1 where key j lies in a kept tile of row i,
+      dP_ij = K_ij dO_i . v_j,  Delta_i = sum_j P_ij dP_ij (= dO_i . O_i),
+      dS_ij = P_ij (dP_ij - Delta_i),  dV_j = sum_i K_ij P_ij dO_i,
+      dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i
+    (a skipped tile still passes -P Delta to dQ and dK through the full denominator).
+    B must be 1.  -> (dQ, dK, dV)"""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Lq, Hq, D = q.shape
+    _, Lk, Hkv, _ = k.shape
+    assert B == 1
+    G = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    nqb = -(-Lq // Bq)
+    for h in range(Hkv):
+        for qb in range(nqb):
+            rows = np.arange(qb * Bq, min(Lq, (qb + 1) * Bq))
+            P = _mala_rows(q, k, win, scale, h, rows, G, Lq)
+            keep_keys = np.repeat(np.asarray(kept[h, qb], dtype=np.float64), Bk)[:Lk]
+            for gi, qh in enumerate(range(h * G, (h + 1) * G)):
+                p = P[gi]
+                dp = (do[0, rows, qh, :] @ v[0, :, h, :].T) * keep_keys[None, :]
+                delta = (p * dp).sum(axis=1, keepdims=True)
+                ds = p * (dp - delta)
+                dq[0, rows, qh, :] = scale * (ds @ k[0, :, h, :])
+                dk[0, :, h, :] += scale * (ds.T @ q[0, rows, qh, :])
+                dv[0, :, h, :] += (p * keep_keys[None, :]).T @ do[0, rows, qh, :]
+    return dq, dk, dv
+
+
 # --------------------------------------------------------------------------- tiles
 
 def tile_lists(Lq, Lk, Hkv, Bq, Bk, win):

@@ -218,3 +218,35 @@ def test_decode_matches_forward_last_row_128k():
     dl = (lsed - lse[:, :, -1]).abs().max().item()
     print(f"  max|O_dec - O_fwd[-1]|={d:.3e} max|dLSE|={dl:.3e}", flush=True)
     assert d <= 1e-2 and dl <= 1e-3
+
+
+def test_decode_varlen_and_window_cache_16x128k():
+    """The variable-length and window-cache decodes in the setting the benchmark times:
+    16 caches of 131072 positions, sequence b of length 65536 + 4096 b (varlen) and of the
+    full length (window caches filled from the full caches by one append each).  Varlen
+    against the oracle on sequences 0, 9 and 15; the window-cache decode equal to the
+    planned decode bit for bit, and against the oracle on sequences 3 and 15."""
+    B, L, sink, near = 16, 131072, 128, 4096
+    _case("decode varlen and window caches, 16 x 131072")
+    ow = oracle.Window.for_length(L, HKV, sink, near, 0)
+    win = api.window(ow.sink, ow.near, ow.gap, ow.lr)
+    q, k, v = inputs.attention_inputs(B, 1, L, HQ, HKV, D, seed=45, device=DEV)
+    lens = [65536 + 4096 * b for b in range(B)]
+    ov, lv = api.decode_varlen(q, k, v, torch.tensor(lens, dtype=torch.int32, device=DEV), win)
+    wc = api.WindowCache(B, HKV, D, L, win, DEV)
+    wc.append(k, v, torch.zeros(B, dtype=torch.int32, device=DEV))
+    ow_, lw_ = wc.decode(q, torch.full((B,), L, dtype=torch.int32, device=DEV))
+    op, lp = api.decode(q, k, v, win)
+    torch.cuda.synchronize()
+    n_o, n_l = int((ow_ != op).sum().item()), int((lw_ != lp).sum().item())
+    print(f"  window cache vs planned decode: O differs at {n_o}, LSE at {n_l}", flush=True)
+    assert n_o == 0 and n_l == 0
+    for b in (0, 9, 15):
+        n = lens[b]
+        Oo, Lo = oracle.decode(q[b:b + 1].cpu(), k[b:b + 1, :n].cpu(), v[b:b + 1, :n].cpu(), ow, SCALE)
+        assert_bf16_close(f"varlen O[b={b}] (len {n})", ov[b:b + 1], Oo)
+        assert_bf16_close(f"varlen LSE[b={b}]", lv[b:b + 1], Lo[:, :, 0])
+    for b in (3, 15):
+        Oo, Lo = oracle.decode(q[b:b + 1].cpu(), k[b:b + 1].cpu(), v[b:b + 1].cpu(), ow, SCALE)
+        assert_bf16_close(f"window cache O[b={b}]", ow_[b:b + 1], Oo)
+        assert_bf16_close(f"window cache LSE[b={b}]", lw_[b:b + 1], Lo[:, :, 0])

@@ -478,3 +478,50 @@ def test_mala_row_masses_sum_to_one_and_error_bound():
     err = np.abs(O - Oe).max(axis=3)[0]                 # [L, H]
     assert np.all(err <= dropped.T * np.abs(v.numpy()).max() + 1e-12)
     assert dropped.max() > 0
+
+
+def test_mala_bwd_tau_zero_is_the_attention_backward():
+    """With every tile kept the MALA gradients are those of masked attention (autograd of
+    torch SDPA in float64)."""
+    L, Hq, Hkv, D = 40, 4, 2, 8
+    win = W.for_length(L, Hkv, 3, 6, 0, mode=oracle.DENSE)
+    q, k, v = _mala_inputs(L, Hq, Hkv, D, 110)
+    do = _rand((1, L, Hq, D), 113)
+    kept = np.ones((Hkv, L // 8, L // 8), dtype=bool)
+    dq, dk, dv = oracle.mala_bwd(q, k, v, do, win, 0.3, 8, 8, kept)
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    (_sdpa(qa, ka, va, _masks(L, L, Hq, Hkv, win), 0.3) * do).sum().backward()
+    np.testing.assert_allclose(dq, qa.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, ka.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, va.grad.numpy(), atol=1e-12)
+
+
+def test_mala_bwd_finite_differences_with_fixed_decisions():
+    """Central finite differences of sum(O * dO) for the MALA forward with its decisions
+    held fixed (taken once at tau = 0.12, several tiles skipped)."""
+    L, Hq, Hkv, D, Bq, Bk = 16, 2, 1, 4, 4, 4
+    win = W.for_length(L, Hkv, 1, 3, 0, mode=oracle.DENSE)
+    q, k, v = _mala_inputs(L, Hq, Hkv, D, 120)
+    do = _rand((1, L, Hq, D), 123)
+    scale = 0.8
+    _, _, kept = oracle.mala_fwd(q, k, v, win, scale, 0.12, Bq, Bk)
+    assert 0 < (~kept).sum()
+    dq, dk, dv = oracle.mala_bwd(q, k, v, do, win, scale, Bq, Bk, kept)
+
+    def loss(q_, k_, v_):
+        O, _, _ = oracle.mala_fwd(q_, k_, v_, win, scale, 0.12, Bq, Bk, kept=kept)
+        return float((O * do.numpy()).sum())
+
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros(x.shape)
+        flat = x.reshape(-1)
+        for idx in range(flat.numel()):
+            old = float(flat[idx])
+            flat[idx] = old + eps
+            fp = loss(q, k, v)
+            flat[idx] = old - eps
+            fm = loss(q, k, v)
+            flat[idx] = old
+            num.reshape(-1)[idx] = (fp - fm) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=2e-8, err_msg=name)
