@@ -140,7 +140,7 @@ typedef struct cowa_plan_dev {
 
 /* ---------------------------------------------------------------- problem */
 enum { COWA_DTYPE_BF16 = 0, COWA_DTYPE_F32 = 1 };
-enum { COWA_OP_FWD = 0, COWA_OP_BWD = 1, COWA_OP_DECODE = 2 };
+enum { COWA_OP_FWD = 0, COWA_OP_BWD = 1, COWA_OP_DECODE = 2, COWA_OP_MALA_BWD = 3 };
 
 typedef struct cowa_problem {
   int32_t B, Lq, Lk, Hq, Hkv, D;
@@ -156,7 +156,9 @@ int cowa_tile_sizes(int op, const cowa_problem* p, int32_t* Bq, int32_t* Bk);
 /* Bytes of device workspace `op` needs for problem p (0 if none).  The backward keeps
  * three fp32 values per (query head, row) (Delta, the power-of-two scales of Q and dO),
  * 256 bytes of launch-wide maxima, fp16 copies of Q and dO (2 * B * Lq * Hq * D * 2
- * bytes) and of K (B * Lk * Hkv * D * 2 bytes); the decode keeps its split partials. */
+ * bytes) and of K (B * Lk * Hkv * D * 2 bytes); the decode keeps its split partials.
+ * COWA_OP_MALA_BWD adds one byte per forward tile (Hkv * ceil(Lq / Bq_f) * ceil(Lk / 64),
+ * Bq_f the forward's tile height, rounded up to 256) to the backward's workspace. */
 int cowa_workspace_size(int op, const cowa_problem* p, size_t* bytes);
 
 /* Forward (the operator of the abstract, used for training and for prefill: "CoWindow
@@ -189,14 +191,15 @@ int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan,
  * row loses at most its dropped mass times max |v| per dimension.  The window is the
  * visibility the scoring covers (COWA_BAND_DENSE: full causal scoring, as the pages
  * describe MALA; the CoWA windows give MALA on top of CoWA).
- * q,k,v,o bf16 as in cowa_fwd, D = 128; lse fp32 [B, Hq, Lq] (written: the full LSE).
+ * q,k,v,o bf16 as in cowa_fwd, D = 128; lse fp32 [B, Hq, Lq] (written: the full LSE);
+ * o_lo (may be NULL): O's bf16 rounding residual, as in cowa_fwd, for cowa_mala_bwd.
  * kept (may be NULL; B = 1 only): int32 per entry of the plan's row lists, set to 1 where
  * the tile's PV was done and 0 where it was skipped.  The plan is a forward plan
  * (cowa_tile_sizes(COWA_OP_FWD)).  Errors: INVALID_ARG (also for tau < 0 or NaN, and kept
  * with B > 1), UNSUPPORTED (not BF16 / D = 128), PLAN_MISMATCH, HIP. */
 int cowa_mala_fwd(const cowa_problem* p, const cowa_plan_dev* plan, float tau,
                   const void* q, const void* k, const void* v, void* o, float* lse,
-                  int32_t* kept, void* stream);
+                  void* o_lo, int32_t* kept, void* stream);
 
 /* Backward from the saved LSE: the pattern serves training forward and backward alike
  * (beyondmarketintelligence.com post, second paragraph; "CoWindow Attention" abstract),
@@ -231,6 +234,29 @@ int cowa_bwd(const cowa_problem* p, const cowa_plan_dev* plan,
              const void* q, const void* k, const void* v, const void* o, const void* o_lo,
              const float* lse, const void* dout, void* dq, void* dk, void* dv, int stages,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/* MALA backward: the gradients of cowa_mala_fwd's output with its tile decisions held
+ * fixed (the decision is a threshold test, piecewise constant in the inputs; the pages
+ * describe MALA as a drop-in operator for training and inference alike:
+ * beyondmarketintelligence.com post, second paragraph).  With P = exp(scale q.k - LSE)
+ * over every visible key (the full scoring) and m = 1 on kept tiles, 0 on skipped ones:
+ *   Delta_i = dO_i . O_i,  dP = m (dO.v),  dS = P (dP - Delta)
+ *   dQ = scale dS K,  dK = scale dS^T Q,  dV = (m P)^T dO,
+ * so skipped tiles give dV nothing and pass dS = -P Delta to dQ and dK through the
+ * denominator.  tau = 0 (every tile kept) is exactly cowa_bwd.
+ * kept: the int32 flags cowa_mala_fwd wrote for fwd_plan's row lists (device); o, o_lo
+ * and lse: its outputs (o_lo may be NULL: Delta then uses the bf16 O alone).  fwd_plan: the forward plan the forward ran with
+ * (cowa_tile_sizes(COWA_OP_FWD)); plan: a backward plan with row and column lists
+ * (cowa_tile_sizes(COWA_OP_MALA_BWD), the same as COWA_OP_BWD).  Precision and ranges as
+ * cowa_bwd.  Runs all three stages.  workspace: cowa_workspace_size(COWA_OP_MALA_BWD),
+ * 256-byte aligned.
+ * Supported: dtype BF16, D = 128, B = 1.  Errors: INVALID_ARG (also for kept NULL),
+ * UNSUPPORTED, WORKSPACE_TOO_SMALL, PLAN_MISMATCH (either plan), HIP. */
+int cowa_mala_bwd(const cowa_problem* p, const cowa_plan_dev* fwd_plan, const cowa_plan_dev* plan,
+                  const int32_t* kept, const void* q, const void* k, const void* v,
+                  const void* o, const void* o_lo, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /* Decode: one new query token per sequence (p->Lq == 1) over a KV cache of p->Lk
  * positions that already holds the new token's K/V; the query sits at position Lk-1,

@@ -14,7 +14,8 @@ from . import _cowa as C
 
 MODES = {"complementary": C.COWA_BAND_COMPLEMENTARY, "duplicated": C.COWA_BAND_DUPLICATED,
          "dense": C.COWA_BAND_DENSE}
-OPS = {"fwd": C.COWA_OP_FWD, "bwd": C.COWA_OP_BWD, "decode": C.COWA_OP_DECODE}
+OPS = {"fwd": C.COWA_OP_FWD, "bwd": C.COWA_OP_BWD, "decode": C.COWA_OP_DECODE,
+       "mala_bwd": C.COWA_OP_MALA_BWD}
 
 
 def make_window(Lmax, Hkv, sink, near, gap=0, mode="complementary"):
@@ -152,9 +153,10 @@ def fwd(q, k, v, win, scale=None, plan=None, out=None, lse=None, o_lo=None):
     return out, lse
 
 
-def mala_fwd(q, k, v, win, tau, scale=None, plan=None, out=None, lse=None, kept=None):
+def mala_fwd(q, k, v, win, tau, scale=None, plan=None, out=None, lse=None, kept=None, o_lo=None):
     """MALA forward (cowa_mala_fwd): -> (o like q, lse [B,Hq,Lq] fp32).  kept: optional
-    int32 tensor of the plan's nnz entries, filled with the per-tile keep decisions."""
+    int32 tensor of the plan's nnz entries, filled with the per-tile keep decisions;
+    o_lo: optional tensor like q for O's rounding residual (for mala_bwd)."""
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     scale = D ** -0.5 if scale is None else scale
@@ -169,10 +171,12 @@ def mala_fwd(q, k, v, win, tau, scale=None, plan=None, out=None, lse=None, kept=
     _check_tensor("lse", lse, (B, Hq, Lq), torch.float32, q.device)
     if kept is not None:
         _check_tensor("kept", kept, (max(1, plan.info.nnz),), torch.int32, q.device)
+    if o_lo is not None:
+        _check_tensor("o_lo", o_lo, (B, Lq, Hq, D), q.dtype, q.device)
     C.check("cowa_mala_fwd", C.lib.cowa_mala_fwd(
         ctypes.byref(prob), ctypes.byref(plan.struct), float(tau), q.data_ptr(), k.data_ptr(),
-        v.data_ptr(), out.data_ptr(), lse.data_ptr(), None if kept is None else kept.data_ptr(),
-        _stream(q.device)))
+        v.data_ptr(), out.data_ptr(), lse.data_ptr(), None if o_lo is None else o_lo.data_ptr(),
+        None if kept is None else kept.data_ptr(), _stream(q.device)))
     return out, lse
 
 
@@ -204,6 +208,37 @@ def bwd(q, k, v, o, lse, dout, win, scale=None, plan=None, grads=None, workspace
                                        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                        int(stages), workspace.data_ptr(), workspace.numel(),
                                        _stream(q.device)))
+    return dq, dk, dv
+
+
+def mala_bwd(q, k, v, o, lse, dout, kept, fwd_plan, win, scale=None, plan=None, grads=None,
+             workspace=None, o_lo=None):
+    """MALA backward (cowa_mala_bwd) with the forward's tile decisions held fixed: kept is
+    the int32 tensor mala_fwd filled for fwd_plan; -> (dq like q, dk like k, dv like v)."""
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    scale = D ** -0.5 if scale is None else scale
+    prob = problem(B, Lq, Lk, Hq, Hkv, D, q.dtype, scale, win)
+    for name, t, shp in (("q", q, (B, Lq, Hq, D)), ("k", k, (B, Lk, Hkv, D)), ("v", v, (B, Lk, Hkv, D)),
+                         ("o", o, (B, Lq, Hq, D)), ("dout", dout, (B, Lq, Hq, D))):
+        _check_tensor(name, t, shp, q.dtype, q.device)
+    _check_tensor("lse", lse, (B, Hq, Lq), torch.float32, q.device)
+    _check_tensor("kept", kept, (max(1, fwd_plan.info.nnz),), torch.int32, q.device)
+    if o_lo is not None:
+        _check_tensor("o_lo", o_lo, (B, Lq, Hq, D), q.dtype, q.device)
+    plan = build_plan("mala_bwd", prob, q.device) if plan is None else plan
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    _check_tensor("dq", dq, (B, Lq, Hq, D), q.dtype, q.device)
+    _check_tensor("dk", dk, (B, Lk, Hkv, D), q.dtype, q.device)
+    _check_tensor("dv", dv, (B, Lk, Hkv, D), q.dtype, q.device)
+    workspace = _workspace("workspace", workspace, workspace_size("mala_bwd", prob), q.device)
+    C.check("cowa_mala_bwd", C.lib.cowa_mala_bwd(
+        ctypes.byref(prob), ctypes.byref(fwd_plan.struct), ctypes.byref(plan.struct), kept.data_ptr(),
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), None if o_lo is None else o_lo.data_ptr(),
+        lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream(q.device)))
     return dq, dk, dv
 
 

@@ -228,6 +228,10 @@ constexpr int QTL = QBK * D;     // elements per K or V tile (16 KB)
 // direct copies of tile t + 1 in flight into the other): for each 32-key half, S^T = K Q^T
 // (fp16) and dP^T = V dO^T (bf16), then P and dS on the VALU, then dQ^T += K^T dS^T (fp16)
 // with K^T read by ds_read_b64_tr_b16 from the row-major tile.
+// MALA (the backward of cowa_mala_fwd with its tile decisions held fixed): dP is taken as
+// 0 on the 64-key tiles the forward skipped for the row's forward q-block (a.mala_mask),
+// so dS = -P Delta there.
+template <bool MALA>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16384))) __bf16 sK0[QTL];
   __shared__ __attribute__((aligned(16384))) __bf16 sK1[QTL];
@@ -365,15 +369,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     int ent_nxt = ent_cur;                      // entry of tile tt + 1
     int ent_ahead = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * 1, 0);  // of tile 2
     copy_tile(ent_cur, 0, sK0, sV0);
+    // MALA: this row's keep flags by 64-key block (of its forward q-block), the one of
+    // tile tt + 1 fetched during tile tt
+    const uint8_t* mrow = nullptr;
+    int flag_cur = 1, flag_nxt = 1;
+    if constexpr (MALA) {
+      mrow = a.mala_mask + ((int64_t)h * a.mala_nqb + (rvalid ? t / a.mala_bq : 0)) * a.mala_nkb;
+      flag_cur = mrow[min(tile_j0(ent_cur, 0) / QBK, a.mala_nkb - 1)];
+    }
 
     auto tile = [&](auto bufc, const int tt) {
       constexpr int BUF = decltype(bufc)::value;
       wait_loads_and_barrier();  // tile tt resident; every wave is done with tile tt - 1
       if (tt + 1 < ntile) copy_tile(ent_nxt, tt + 1, kbuf(IC<BUF ^ 1>{}), vbuf(IC<BUF ^ 1>{}));
+      if constexpr (MALA) {
+        // (a last half past Lk holds no key: any flag serves, the clamp keeps it in bounds)
+        if (tt + 1 < ntile) flag_nxt = mrow[min(tile_j0(ent_nxt, tt + 1) / QBK, a.mala_nkb - 1)];
+      }
       const __bf16* kt = kbuf(IC<BUF>{});
       const __bf16* vt = vbuf(IC<BUF>{});
       const int j0 = tile_j0(ent_cur, tt);
       const bool partial = ent_cur & 1;
+      // MALA: the dP factor of the dS constant is 0 on a skipped tile.  The products
+      // themselves all run: the VALU reads each result only after the products that
+      // follow it in this interleaved order, and leaving some out would remove that
+      // distance.
+      const float fqt = MALA ? (flag_cur ? fq : 0.f) : fq;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         f32x16 sv, dv;
@@ -399,7 +420,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
             const int i0 = 8 * hf + 2 * q;
             const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[i0], crow, -lse2));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[i0 + 1], crow, -lse2));
-            w[hf][q] = pack_f16x2(p0 * fmaf(dv[i0], fq, -tq), p1 * fmaf(dv[i0 + 1], fq, -tq));
+            w[hf][q] = pack_f16x2(p0 * fmaf(dv[i0], fqt, -tq), p1 * fmaf(dv[i0 + 1], fqt, -tq));
           }
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -415,6 +436,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       // next tile's successor starts a new entry, fetched two tiles ago; after an odd tile
       // it shares the next tile's entry
       ent_cur = ent_nxt;
+      flag_cur = flag_nxt;
       if ((tt & 1) == 0) {
         ent_nxt = __builtin_amdgcn_readfirstlane(ent_ahead);
         ent_ahead = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * ((tt >> 1) + 2), 0);
@@ -472,7 +494,14 @@ __device__ __forceinline__ bf16x8 bf16_to_f16_scaled(const bf16x8& x, int e) {
   return __builtin_bit_cast(bf16x8, h);
 }
 
+// MALA (the backward of cowa_mala_fwd with its tile decisions held fixed): for the rows
+// whose forward tile of this wave's 64 keys was skipped, dP and the P of the dV product
+// are taken as 0 (a mask factor per row and key half, staged with the row constants and
+// folded into the dS constant f), so dS = -P Delta there and dV gets nothing.
+template <bool MALA>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  // row constants per q-block: 4 (CoWA) or 7 (MALA: f and the mask factor per key half)
+  constexpr int NLT = MALA ? 7 : 4;
   // Q (fp16 copy) and dO of a q-block, [Q, dO][rows] with swizzled 256-byte rows
   // (lds_swz); dO sits at a fixed distance from Q, so one address serves both.  Two
   // separate arrays (not one indexed by the buffer): every read names the array it reads,
@@ -481,8 +510,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 sQD0[2 * QTILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sQD1[2 * QTILE];
   // per-row constants of a q-block: [LSE log2 e, c_r, 2^e_r, 2^e_r Delta][rows]
-  __shared__ __attribute__((aligned(16))) float sLT0[4 * ROWS];
-  __shared__ __attribute__((aligned(16))) float sLT1[4 * ROWS];
+  __shared__ __attribute__((aligned(16))) float sLT0[NLT * ROWS];
+  __shared__ __attribute__((aligned(16))) float sLT1[NLT * ROWS];
   __shared__ int sRt[ROWS];  // row -> token in the q-block
   __shared__ float sKmax[4];  // max |k| of each wave's keys
   __shared__ float sVmax[4];  // max over each wave's keys of |v_j|^2
@@ -583,6 +612,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // q-block's first use), so the loads do not stall the wave when they are issued.
   const int my_rt = tid / G, my_g = tid - my_rt * G;
   float plse = 0.f, pdel = 0.f, pqs = 1.f, pdx = 0.f, ck = a.scale_log2;
+  int pm0 = 1, pm1 = 1;  // MALA: keep flags of the row's forward tiles of the two key halves
+  // the dS constant f of this wave's key half, and (MALA) its mask factor, in the row table
+  const int f_off = (MALA && wave >= 2) ? 4 * ROWS : 2 * ROWS;
+  const int m_off = (wave >= 2) ? 6 * ROWS : 5 * ROWS;
   // dS range scale of this item (2^sc, see below) and the dK output factor scale 2^-sc;
   // the exponent eV of the item's fp16 V; the dV product's common exponent F
   float dsc = 1.f, dk_out = a.scale;
@@ -622,6 +655,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       pdel = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_del, vo, 0, 0));
       pqs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_qs, vo, 0, 0));
       pdx = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dx, vo, 0, 0));
+      if constexpr (MALA) {
+        const int tok = min(t0 + my_rt, a.Lq - 1);
+        const uint8_t* mr = a.mala_mask + ((int64_t)h * a.mala_nqb + tok / a.mala_bq) * a.mala_nkb;
+        pm0 = 2 * kb < a.mala_nkb ? mr[2 * kb] : 0;
+        pm1 = 2 * kb + 1 < a.mala_nkb ? mr[2 * kb + 1] : 0;
+      }
     }
   };
   auto copy = [&](int i, auto bufc) {
@@ -645,7 +684,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const int er = min(fr - fcommon, 0);
       lt[tid] = (pvalid && plse != -INFINITY) ? plse * kLog2e - (float)er : INFINITY;
       lt[ROWS + tid] = pvalid ? ck * pqs : ck;
-      lt[2 * ROWS + tid] = pvalid ? __builtin_amdgcn_ldexpf(pqs * dsc, fr + ev - er) : 0.f;
+      const float fv = pvalid ? __builtin_amdgcn_ldexpf(pqs * dsc, fr + ev - er) : 0.f;
+      if constexpr (MALA) {
+        const float m0 = pm0 ? 1.f : 0.f, m1 = pm1 ? 1.f : 0.f;
+        lt[2 * ROWS + tid] = fv * m0;
+        lt[4 * ROWS + tid] = fv * m1;
+        lt[5 * ROWS + tid] = m0;
+        lt[6 * ROWS + tid] = m1;
+      } else {
+        lt[2 * ROWS + tid] = fv;
+      }
       lt[3 * ROWS + tid] = pvalid ? __builtin_amdgcn_ldexpf(pdel * (pqs * dsc), -er) : 0.f;
     }
   };
@@ -794,7 +842,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i)
           wA.pr[4 * i4 + i] = __builtin_amdgcn_exp2f(fmaf(s[4 * i4 + i], c4[i], -l4[i]));
       }
-      wA.f0 = *(const f32x4*)(lt + 2 * ROWS);
+      wA.f0 = *(const f32x4*)(lt + f_off);
       wA.t0 = *(const f32x4*)(lt + 3 * ROWS);
     }
 
@@ -858,6 +906,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       f32x4 f4[4], t4[4], l4[4], c4[4];
       f4[0] = cur.f0;
       t4[0] = cur.t0;
+      f32x4 mk[4];  // MALA: mask factors of block g's rows for this wave's key half
+      if constexpr (MALA) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) mk[i4] = *(const f32x4*)(lg + m_off + 8 * i4);
+      }
       float ds[16], prv[3], dpv[3];
       uint32_t wpa[2][4], wds[2][4];
 #pragma unroll
@@ -881,7 +934,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         // the next block's group 0, for phase 2
         if ((x & 3) == 0 && x < 12) {
           const int i4 = (x >> 2) + 1;
-          f4[i4] = *(const f32x4*)(lg + 2 * ROWS + 8 * i4);
+          f4[i4] = *(const f32x4*)(lg + f_off + 8 * i4);
           t4[i4] = *(const f32x4*)(lg + 3 * ROWS + 8 * i4);
         }
         if (x == 12) {
@@ -893,7 +946,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         // ahead of the slot's dS
         if (x & 1) {
           const int q = x >> 1;
-          wpa[q >> 2][q & 3] = pack_f16x2(prv[(x - 1) % 3], prv[x % 3]);
+          if constexpr (MALA)
+            wpa[q >> 2][q & 3] = pack_f16x2(prv[(x - 1) % 3] * mk[(x - 1) >> 2][(x - 1) & 3],
+                                            prv[x % 3] * mk[x >> 2][x & 3]);
+          else
+            wpa[q >> 2][q & 3] = pack_f16x2(prv[(x - 1) % 3], prv[x % 3]);
         } else if (x >= 2) {
           const int q = (x - 2) >> 1;
           pin_out(wpa[q >> 2][q & 3]);
@@ -960,7 +1017,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           c4[i4] = *(const f32x4*)(lt + ROWS + 8 * i4);
         }
         if (x == 12) {
-          nxt.f0 = *(const f32x4*)(lt + 2 * ROWS);
+          nxt.f0 = *(const f32x4*)(lt + f_off);
           nxt.t0 = *(const f32x4*)(lt + 3 * ROWS);
         }
         // the next step's first operands (rows of block g + 2)
@@ -1016,7 +1073,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
+// MALA: the forward's keep flags (one per entry of its row lists) as a dense mask
+// [Hkv * nqb_f, nkb64]: one work group per forward row item scatters its entries (the
+// forward's k-blocks are the 64-key blocks); unlisted tiles see no key and stay 0.
+__global__ __launch_bounds__(256) void mala_mask_clear_kernel(uint8_t* m, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) m[i] = 0;
+}
+__global__ __launch_bounds__(256) void mala_mask_kernel(MalaMaskArgs a) {
+  const int item = blockIdx.x;
+  const int e0 = a.row_ptr[item], e1 = a.row_ptr[item + 1];
+  for (int e = e0 + (int)threadIdx.x; e < e1; e += 256)
+    a.mask[(int64_t)item * a.nkb + (a.row_ent[e] >> 1)] = a.kept[e] ? 1 : 0;
+}
+
 }  // namespace
+
+hipError_t launch_mala_mask(const MalaMaskArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.n_items * a.nkb;
+  hipLaunchKernelGGL(mala_mask_clear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.mask, n);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(mala_mask_kernel, dim3(a.n_items), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd_bf16_d128(const BwdArgs& a, int stages, hipStream_t s) {
   hipError_t err = hipSuccess;
@@ -1032,11 +1112,13 @@ hipError_t launch_bwd_bf16_d128(const BwdArgs& a, int stages, hipStream_t s) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (stages & COWA_BWD_DQ) {
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(a.Hkv * a.nqb, a.B), dim3(256), 0, s, a);
+    if (a.mala_mask) hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(a.Hkv * a.nqb, a.B), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(a.Hkv * a.nqb, a.B), dim3(256), 0, s, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (stages & COWA_BWD_DKDV) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(a.Hkv * a.nkb, a.B), dim3(256), 0, s, a);
+    if (a.mala_mask) hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(a.Hkv * a.nkb, a.B), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(a.Hkv * a.nkb, a.B), dim3(256), 0, s, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return err;

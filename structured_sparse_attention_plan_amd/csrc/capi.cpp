@@ -56,6 +56,10 @@ int check_op_support(int op, const cowa_problem* p) {
     case COWA_OP_BWD:
       return (p->dtype == COWA_DTYPE_BF16 && p->D == 128 && G <= kBwdRows) ? COWA_OK
                                                                            : COWA_ERR_UNSUPPORTED;
+    case COWA_OP_MALA_BWD:  // one sequence: the forward's keep flags exist for B = 1 only
+      return (p->dtype == COWA_DTYPE_BF16 && p->D == 128 && G <= kBwdRows && p->B == 1)
+                 ? COWA_OK
+                 : COWA_ERR_UNSUPPORTED;
     case COWA_OP_DECODE:
       if (p->dtype != COWA_DTYPE_BF16 || p->D != 128 || p->Lq != 1) return COWA_ERR_UNSUPPORTED;
       return decode_supports_group(G) ? COWA_OK : COWA_ERR_UNSUPPORTED;
@@ -77,6 +81,7 @@ void tiles_for(int op, const cowa_problem* p, int32_t* Bq, int32_t* Bk) {
       }
       return;
     case COWA_OP_BWD:
+    case COWA_OP_MALA_BWD:
       *Bq = kBwdRows / G;
       *Bk = kBwdBk;
       return;
@@ -145,6 +150,21 @@ BwdLayout bwd_layout(const cowa_problem* p) {
   return l;
 }
 
+// MALA backward: the forward's tiling (Bq_f tokens, 64 keys) and the byte mask of its
+// keep flags [Hkv, nqb_f, nkb_f] after the backward workspace.
+struct MalaTiles {
+  int32_t bq, nqb, nkb;
+  size_t mask_bytes;
+};
+MalaTiles mala_tiles(const cowa_problem* p) {
+  MalaTiles t;
+  tiles_for(COWA_OP_FWD, p, &t.bq, &t.nkb);
+  t.nkb = (p->Lk + kFwdBk - 1) / kFwdBk;
+  t.nqb = (p->Lq + t.bq - 1) / t.bq;
+  t.mask_bytes = round256((size_t)p->Hkv * t.nqb * t.nkb);
+  return t;
+}
+
 }  // namespace
 
 extern "C" const char* cowa_status_string(int status) {
@@ -181,6 +201,9 @@ extern "C" int cowa_workspace_size(int op, const cowa_problem* p, size_t* bytes)
       break;
     case COWA_OP_BWD:
       *bytes = bwd_layout(p).total;
+      break;
+    case COWA_OP_MALA_BWD:
+      *bytes = bwd_layout(p).total + mala_tiles(p).mask_bytes;
       break;
     default: {
       const size_t rows = (size_t)p->B * p->Hq * decode_splits(p);
@@ -235,8 +258,8 @@ extern "C" int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan, const 
 }
 
 extern "C" int cowa_mala_fwd(const cowa_problem* p, const cowa_plan_dev* plan, float tau, const void* q,
-                             const void* k, const void* v, void* o, float* lse, int32_t* kept,
-                             void* stream) {
+                             const void* k, const void* v, void* o, float* lse, void* o_lo,
+                             int32_t* kept, void* stream) {
   int st = check_problem(p);
   if (st != COWA_OK) return st;
   if (p->dtype != COWA_DTYPE_BF16) return COWA_ERR_UNSUPPORTED;
@@ -268,29 +291,18 @@ extern "C" int cowa_mala_fwd(const cowa_problem* p, const cowa_plan_dev* plan, f
   a.scale = p->scale;
   a.scale_log2 = p->scale * 1.44269504088896340736f;
   a.win = dev_window(p->win);
+  a.o_lo = o_lo;
   a.mala_tau = tau;
   a.kept = (p->B == 1) ? kept : nullptr;
   if (kept && p->B != 1) return COWA_ERR_INVALID_ARG;
   return hip_status(launch_mala_fwd_bf16_d128(a, (hipStream_t)stream));
 }
 
-extern "C" int cowa_bwd(const cowa_problem* p, const cowa_plan_dev* plan, const void* q, const void* k,
-                        const void* v, const void* o, const void* o_lo, const float* lse,
-                        const void* dout, void* dq, void* dk, void* dv, int stages, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  int st = check_problem(p);
-  if (st != COWA_OK) return st;
-  st = check_op_support(COWA_OP_BWD, p);
-  if (st != COWA_OK) return st;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return COWA_ERR_INVALID_ARG;
-  if (stages < 1 || stages > COWA_BWD_ALL) return COWA_ERR_INVALID_ARG;
-  st = check_plan(COWA_OP_BWD, p, plan, true);
-  if (st != COWA_OK) return st;
-  size_t need = 0;
-  cowa_workspace_size(COWA_OP_BWD, p, &need);
-  if (!workspace || workspace_bytes < need) return COWA_ERR_WORKSPACE_TOO_SMALL;
-  if (((uintptr_t)workspace & 255) != 0) return COWA_ERR_INVALID_ARG;
-
+namespace {
+// The backward's arguments (everything but the MALA fields) after the checks passed.
+BwdArgs bwd_args(const cowa_problem* p, const cowa_plan_dev* plan, const void* q, const void* k,
+                 const void* v, const void* o, const void* o_lo, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, void* workspace) {
   BwdArgs a{};
   a.q = q;
   a.k = k;
@@ -330,7 +342,65 @@ extern "C" int cowa_bwd(const cowa_problem* p, const cowa_plan_dev* plan, const 
   a.scale = p->scale;
   a.scale_log2 = p->scale * 1.44269504088896340736f;
   a.win = dev_window(p->win);
+  return a;
+}
+}  // namespace
+
+extern "C" int cowa_bwd(const cowa_problem* p, const cowa_plan_dev* plan, const void* q, const void* k,
+                        const void* v, const void* o, const void* o_lo, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, int stages, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int st = check_problem(p);
+  if (st != COWA_OK) return st;
+  st = check_op_support(COWA_OP_BWD, p);
+  if (st != COWA_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return COWA_ERR_INVALID_ARG;
+  if (stages < 1 || stages > COWA_BWD_ALL) return COWA_ERR_INVALID_ARG;
+  st = check_plan(COWA_OP_BWD, p, plan, true);
+  if (st != COWA_OK) return st;
+  size_t need = 0;
+  cowa_workspace_size(COWA_OP_BWD, p, &need);
+  if (!workspace || workspace_bytes < need) return COWA_ERR_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)workspace & 255) != 0) return COWA_ERR_INVALID_ARG;
+  const BwdArgs a = bwd_args(p, plan, q, k, v, o, o_lo, lse, dout, dq, dk, dv, workspace);
   return hip_status(launch_bwd_bf16_d128(a, stages, (hipStream_t)stream));
+}
+
+extern "C" int cowa_mala_bwd(const cowa_problem* p, const cowa_plan_dev* fwd_plan,
+                             const cowa_plan_dev* plan, const int32_t* kept, const void* q,
+                             const void* k, const void* v, const void* o, const void* o_lo,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_problem(p);
+  if (st != COWA_OK) return st;
+  st = check_op_support(COWA_OP_MALA_BWD, p);
+  if (st != COWA_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !kept) return COWA_ERR_INVALID_ARG;
+  st = check_plan(COWA_OP_FWD, p, fwd_plan, false);
+  if (st != COWA_OK) return st;
+  st = check_plan(COWA_OP_MALA_BWD, p, plan, true);
+  if (st != COWA_OK) return st;
+  size_t need = 0;
+  cowa_workspace_size(COWA_OP_MALA_BWD, p, &need);
+  if (!workspace || workspace_bytes < need) return COWA_ERR_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)workspace & 255) != 0) return COWA_ERR_INVALID_ARG;
+  BwdArgs a = bwd_args(p, plan, q, k, v, o, o_lo, lse, dout, dq, dk, dv, workspace);
+  const MalaTiles mt = mala_tiles(p);
+  MalaMaskArgs m{};
+  m.mask = (uint8_t*)workspace + bwd_layout(p).total;
+  m.row_ptr = fwd_plan->row_ptr;
+  m.row_ent = fwd_plan->row_ent;
+  m.kept = kept;
+  m.n_items = p->Hkv * mt.nqb;
+  m.nkb = mt.nkb;
+  hipStream_t s = (hipStream_t)stream;
+  st = hip_status(launch_mala_mask(m, s));
+  if (st != COWA_OK) return st;
+  a.mala_mask = m.mask;
+  a.mala_bq = mt.bq;
+  a.mala_nqb = mt.nqb;
+  a.mala_nkb = mt.nkb;
+  return hip_status(launch_bwd_bf16_d128(a, COWA_BWD_ALL, s));
 }
 
 extern "C" int cowa_decode(const cowa_problem* p, const cowa_plan_dev* plan, const void* q,

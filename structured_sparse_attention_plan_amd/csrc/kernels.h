@@ -69,6 +69,10 @@ struct BwdArgs {
   int32_t Bq, Bk;
   float scale, scale_log2;
   DevWindow win;
+  // MALA backward: keep flags [Hkv, mala_nqb, mala_nkb] by (KV head, forward q-block of
+  // mala_bq tokens, 64-key block); null for the CoWA backward
+  const uint8_t* mala_mask;
+  int32_t mala_bq, mala_nqb, mala_nkb;
 };
 
 struct DecodeArgs {
@@ -107,6 +111,15 @@ struct WcacheAppendArgs {
 hipError_t launch_fwd_f32_d64(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16_d128(const FwdArgs& a, hipStream_t s);
 hipError_t launch_mala_fwd_bf16_d128(const FwdArgs& a, hipStream_t s);  // scoring, then the gated pass
+// MALA backward: the forward's per-entry keep flags scattered to a dense mask
+struct MalaMaskArgs {
+  uint8_t* mask;           // [n_items, nkb]
+  const int32_t* row_ptr;  // the forward plan's row lists
+  const int32_t* row_ent;
+  const int32_t* kept;     // per forward entry
+  int32_t n_items, nkb;
+};
+hipError_t launch_mala_mask(const MalaMaskArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16_d128(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t s);  // varlen when a.seqlens
 hipError_t launch_wcache_append(const WcacheAppendArgs& a, hipStream_t s);

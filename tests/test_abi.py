@@ -49,6 +49,13 @@ def test_tile_sizes_and_workspace():
     # Delta and the power-of-two scales of Q and dO (fp32 each), 256 bytes of launch-wide
     # maxima, the fp16 copies of Q and dO, then that of K
     assert api.workspace_size("bwd", p) == 3 * 40 * 256 * 4 + 256 + 2 * 256 * 40 * 128 * 2 + 256 * 8 * 128 * 2
+    # MALA backward: the backward's tiling and workspace, then one byte per forward tile
+    # (8 KV heads x ceil(256 / 51) q-blocks x 4 64-key blocks, rounded up to 256)
+    assert api.tile_sizes("mala_bwd", p) == api.tile_sizes("bwd", p)
+    assert api.workspace_size("mala_bwd", p) == api.workspace_size("bwd", p) + 256
+    pl = _prob(Lq=4096, Lk=4096)
+    assert (api.workspace_size("mala_bwd", pl) - api.workspace_size("bwd", pl)
+            == -(-(8 * -(-4096 // 51) * 64) // 256) * 256)
     pd = _prob(Lq=1, Lk=4096)
     assert api.tile_sizes("decode", pd) == (1, 64)
     assert api.workspace_size("decode", pd) > 0
@@ -63,6 +70,8 @@ def test_tile_sizes_and_workspace():
     ("bwd", dict(dtype=C.COWA_DTYPE_F32, D=64), C.COWA_ERR_UNSUPPORTED),
     ("decode", dict(Lq=2), C.COWA_ERR_UNSUPPORTED),        # decode is one query row
     ("decode", dict(Lq=1, Hq=24, Hkv=8), C.COWA_ERR_UNSUPPORTED),   # G = 3 not built
+    ("mala_bwd", dict(B=2), C.COWA_ERR_UNSUPPORTED),       # one sequence only
+    ("mala_bwd", dict(dtype=C.COWA_DTYPE_F32, D=64), C.COWA_ERR_UNSUPPORTED),
     ("fwd", dict(B=0), C.COWA_ERR_INVALID_ARG),
     ("fwd", dict(scale=0.0), C.COWA_ERR_INVALID_ARG),
 ])
@@ -113,6 +122,30 @@ def test_entry_points_validate_before_launch():
         assert C.lib.cowa_bwd(ctypes.byref(p), ctypes.byref(pb), x, x, x, x, None, x, x, x, x, x,
                               bad_stages, ctypes.c_void_p(256), 1 << 24,
                               None) == C.COWA_ERR_INVALID_ARG
+    # MALA backward: NULL keep flags, plans swapped (a backward plan is no forward plan),
+    # workspace too small for the mask after the backward's arrays
+    pf = _fake_plan(p, "fwd")
+    pm = _fake_plan(p, "mala_bwd")
+    big = 1 << 30
+    assert C.lib.cowa_mala_bwd(ctypes.byref(p), ctypes.byref(pf), ctypes.byref(pm), None, x, x, x, x,
+                               None, x, x, x, x, x, ctypes.c_void_p(256), big,
+                               None) == C.COWA_ERR_INVALID_ARG
+    assert C.lib.cowa_mala_bwd(ctypes.byref(p), ctypes.byref(pm), ctypes.byref(pm), x, x, x, x, x,
+                               None, x, x, x, x, x, ctypes.c_void_p(256), big,
+                               None) == C.COWA_ERR_PLAN_MISMATCH
+    assert C.lib.cowa_mala_bwd(ctypes.byref(p), ctypes.byref(pf), ctypes.byref(pf), x, x, x, x, x,
+                               None, x, x, x, x, x, ctypes.c_void_p(256), big,
+                               None) == C.COWA_ERR_PLAN_MISMATCH
+    assert C.lib.cowa_mala_bwd(ctypes.byref(p), ctypes.byref(pf), ctypes.byref(pm), x, x, x, x, x,
+                               None, x, x, x, x, x, ctypes.c_void_p(256), api.workspace_size("bwd", p),
+                               None) == C.COWA_ERR_WORKSPACE_TOO_SMALL
+    # MALA forward: negative tau, keep flags with B > 1
+    assert C.lib.cowa_mala_fwd(ctypes.byref(p), ctypes.byref(pf), -0.5, x, x, x, x, x, None, None,
+                               None) == C.COWA_ERR_INVALID_ARG
+    p2b = _prob(B=2)
+    pf2 = _fake_plan(p2b, "fwd")
+    assert C.lib.cowa_mala_fwd(ctypes.byref(p2b), ctypes.byref(pf2), 0.1, x, x, x, x, x, None, x,
+                               None) == C.COWA_ERR_INVALID_ARG
     # decode: workspace too small
     pd = _prob(Lq=1, Lk=4096, win=api.make_window(4096, 8, 4, 16))
     pld = _fake_plan(pd, "decode")

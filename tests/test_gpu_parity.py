@@ -600,3 +600,98 @@ def test_mala_fwd_32k_dense_sampled_qblocks():
     rng = np.random.default_rng(141)
     qblocks = sorted({0, 1, nqb - 1} | set(int(x) for x in rng.choice(nqb, 13, replace=False)))
     mala_check(qc, kc, vc, ow, win, 0.004, qblocks=qblocks)
+
+
+# ------------------------------------------------------------------- MALA backward
+
+def _mala_forward_for_bwd(q, k, v, win, tau):
+    """The MALA forward on the device with its keep flags and O's rounding residual."""
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    prob = api.problem(B, L, L, Hq, Hkv, D, torch.bfloat16, D ** -0.5, win)
+    fplan = api.build_plan("fwd", prob, DEV)
+    kept = torch.full((max(1, fplan.info.nnz),), -1, dtype=torch.int32, device=DEV)
+    o_lo = torch.empty_like(q)
+    o, lse = api.mala_fwd(q, k, v, win, tau, plan=fplan, kept=kept, o_lo=o_lo)
+    return fplan, kept, o, lse, o_lo
+
+
+def _kept_array(fplan, kept, Hkv, L, Bk=64):
+    """The device's decisions as the oracle's [Hkv, nqb, nkb] array (unlisted tiles hold
+    no visible key; their value does not matter)."""
+    tiles = _plan_tiles(fplan)
+    kg = kept.cpu().numpy()[:len(tiles)]
+    assert set(np.unique(kg)) <= {0, 1}
+    out = np.ones((Hkv, fplan.info.nqb, -(-L // Bk)), dtype=bool)
+    for (h, qb, kb), g in zip(tiles, kg):
+        out[h, qb, kb] = bool(g)
+    return out, int(kg.sum()), len(tiles)
+
+
+@pytest.mark.parametrize("L,Hq,Hkv,mode,tau,expect_skip", [
+    (700, 40, 8, "dense", 0.02, False),
+    (700, 40, 8, "dense", 0.2, True),      # about half the tiles skipped
+    (1000, 40, 8, "complementary", 0.3, True),
+    (900, 16, 2, "dense", 0.15, True),     # G = 8
+    (600, 24, 8, "dense", 0.2, True),      # G = 3: two rows of each q-block unused
+    (500, 40, 8, "dense", 1.5, True),      # nothing kept: dV = 0, dS = -P Delta everywhere
+])
+def test_mala_bwd(L, Hq, Hkv, mode, tau, expect_skip):
+    """The MALA backward with the kernel's own tile decisions against the oracle's
+    gradients under those decisions."""
+    _case(f"MALA bwd L={L} Hq={Hq} Hkv={Hkv} {mode} tau={tau}")
+    ow, win = _windows(L, Hkv, 16, 64, mode=mode)
+    q, k, v, do = inputs.attention_inputs(1, L, L, Hq, Hkv, 128, seed=43, with_dout=True)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    fplan, kept, o, lse, o_lo = _mala_forward_for_bwd(qd, kd, vd, win, tau)
+    dq, dk, dv = api.mala_bwd(qd, kd, vd, o, lse, dod, kept, fplan, win, o_lo=o_lo)
+    torch.cuda.synchronize()
+    kept_np, n_kept, n_tiles = _kept_array(fplan, kept, Hkv, L)
+    print(f"  {n_kept} of {n_tiles} tiles kept", flush=True)
+    if expect_skip:
+        assert n_kept < n_tiles
+    rq, rk, rv = oracle.mala_bwd(q, k, v, do, ow, 128 ** -0.5, fplan.info.Bq, 64, kept_np)
+    assert_bf16_close("dQ", dq, rq, gradient=True)
+    assert_bf16_close("dK", dk, rk, gradient=True)
+    assert_bf16_close("dV", dv, rv, gradient=True)
+    if n_kept == 0:
+        assert bool((dv == 0).all())
+
+
+@pytest.mark.parametrize("mode", ["dense", "complementary"])
+def test_mala_bwd_tau_zero_is_the_backward(mode):
+    """tau = 0 keeps every tile: the MALA backward of the same O and LSE is the CoWA
+    backward bit for bit (the mask factors are all 1)."""
+    L, Hq, Hkv = 800, 40, 8
+    _case(f"MALA bwd tau=0 == bwd, L={L} {mode}")
+    ow, win = _windows(L, Hkv, 16, 64, mode=mode)
+    q, k, v, do = inputs.attention_inputs(1, L, L, Hq, Hkv, 128, seed=44, with_dout=True,
+                                          device=DEV)
+    fplan, kept, o, lse, o_lo = _mala_forward_for_bwd(q, k, v, win, 0.0)
+    m = api.mala_bwd(q, k, v, o, lse, do, kept, fplan, win, o_lo=o_lo)
+    c = api.bwd(q, k, v, o, lse, do, win, o_lo=o_lo)
+    torch.cuda.synchronize()
+    assert int(kept.sum()) == fplan.info.nnz
+    for name, a, b in zip(("dQ", "dK", "dV"), m, c):
+        assert torch.equal(a, b), name
+
+
+def test_mala_bwd_4096_dense():
+    """Full causal MALA at 4096 tokens (64 key blocks per row list), a threshold that
+    skips a good part of the tiles: every gradient element against the oracle."""
+    L, Hq, Hkv, tau = 4096, 40, 8, 0.03
+    _case(f"MALA bwd L={L} dense tau={tau}")
+    ow = oracle.Window.for_length(L, Hkv, 128, 512, 0, mode="dense")
+    win = api.window(ow.sink, ow.near, ow.gap, ow.lr, "dense")
+    q, k, v, do = inputs.attention_inputs(1, L, L, Hq, Hkv, 128, seed=45, with_dout=True)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    fplan, kept, o, lse, o_lo = _mala_forward_for_bwd(qd, kd, vd, win, tau)
+    dq, dk, dv = api.mala_bwd(qd, kd, vd, o, lse, dod, kept, fplan, win, o_lo=o_lo)
+    torch.cuda.synchronize()
+    kept_np, n_kept, n_tiles = _kept_array(fplan, kept, Hkv, L)
+    print(f"  {n_kept} of {n_tiles} tiles kept", flush=True)
+    assert n_kept < 0.9 * n_tiles
+    rq, rk, rv = oracle.mala_bwd(q, k, v, do, ow, 128 ** -0.5, fplan.info.Bq, 64, kept_np)
+    assert_bf16_close("dQ", dq, rq, gradient=True)
+    assert_bf16_close("dK", dk, rk, gradient=True)
+    assert_bf16_close("dV", dv, rv, gradient=True)
