@@ -182,4 +182,42 @@ __device__ __forceinline__ bool visible(int p, int j, int Lk, int sink, int near
   return (j < Lk) & (d >= 0) & ((j < sink) | (d < near_w) | ((d >= b.lo) & (d < b.hi)));
 }
 
+// The visible keys of one query row inside a boundary tile, as one run: with
+// jc = j - jbase (jbase the tile's first key, plus any fixed lane offset), key j is
+// visible iff lo <= jc <= hi, for jc in [0, 63].  The window's three parts (sink, band,
+// near window) and the causal and Lk limits give at most three runs; when they join
+// into one (or none) this returns true, and false when the row sees two or more
+// separate runs in the tile (narrow windows or gaps), where the caller tests keys one by
+// one.  The parts in ascending order of their first key: sink [0, S1], band [B0, B1],
+// near window [N0, R] (the band lies at distances >= near, so it never starts after
+// the near window).
+__device__ __forceinline__ bool visible_run(int p, int jbase, int Lk, int sink, int near_w, HeadBand b,
+                                            int& lo, int& hi) {
+  const int P = p - jbase;                            // d >= 0  <=>  jc <= P
+  const int R = min(min(P, Lk - 1 - jbase), 63);      // last key the row may see
+  const int Pc = max(P, -1);                          // (R < 0 already when P < 0)
+  const int S1 = min(sink - 1 - jbase, R);
+  const int B0 = max(Pc - b.hi + 1, 0), B1 = min(Pc - b.lo, R);
+  const int N0 = max(Pc - near_w + 1, 0);
+  int l = 64, e = -1;  // the union so far: [l, e], empty while e < l
+  bool one = true;
+  if (S1 >= 0) {
+    l = 0;
+    e = S1;
+  }
+  if (B0 <= B1) {
+    one &= (e < l) | (B0 <= e + 1);
+    l = min(l, B0);
+    e = max(e, B1);
+  }
+  if (N0 <= R) {
+    one &= (e < l) | (N0 <= e + 1);
+    l = min(l, N0);
+    e = max(e, R);
+  }
+  lo = l;
+  hi = e;
+  return one;
+}
+
 }  // namespace cowa

@@ -307,6 +307,38 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     }
   };
 
+  // Boundary tile, both row blocks: where every row of the wave sees its visible keys
+  // of the tile as one run (visible_run), each element is tested against the row's run
+  // (three VALU operations); otherwise, with the window predicate per element.
+  auto mask_tile = [&](f32x16 (&v)[KB2][CB], int ent) __attribute__((always_inline)) {
+    if (ent & 1) {
+      int rlo[CB], rhi[CB];
+      bool one = true;
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        one &= visible_run(tok[c] + off, (ent >> 1) * BK + 4 * h2, a.Lk, a.win.sink, a.win.near_w,
+                           band, rlo[c], rhi[c]);
+        if (!rvalid[c]) rlo[c] = 64;
+      }
+      if (__builtin_amdgcn_ballot_w64(!one) == 0) {
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+          for (int k2 = 0; k2 < KB2; ++k2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              // key of element i of key block k2, less the lane's offset 4 h2
+              const int jc = 32 * k2 + 8 * (i >> 2) + (i & 3);
+              const float x = v[k2][c][i];
+              v[k2][c][i] = ((jc >= rlo[c]) & (jc <= rhi[c])) ? x : -INFINITY;
+            }
+      } else {
+        mask_rows(v, 0, ent);
+        mask_rows(v, 1, ent);
+      }
+    }
+  };
+
   // Reference check.  The softmax is exact for any reference, so P(t) is computed with
   // the current one and the reference only moves when a column's sum over the tile
   // leaves the safe range: above 2^32 (a P near overflow), or below 2^-32 while the
@@ -418,8 +450,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
       vf[0] = vfrag(vt, vofs, 0, 0, 0);
       vf[1] = vfrag(vt, vofs, 0, 0, 1);
     }
-    mask_rows(sc, 0, ent_t);
-    mask_rows(sc, 1, ent_t);
+    mask_tile(sc, ent_t);
 
     float sum[CB] = {0.f, 0.f};
     float pb[8];
@@ -591,8 +622,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     // column with no visible key in tile 0.  MALA: the reference is the given LSE (P
     // exactly normalised; +inf for rows without a token or a visible key: P = 0)
     scores(sx[0]);
-    mask_rows(sx[0], 0, ent0);
-    mask_rows(sx[0], 1, ent0);
+    mask_tile(sx[0], ent0);
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
       if constexpr (MODE == 2) {
