@@ -217,7 +217,8 @@ def _events_ms(fn, steps, warmup):
 def mala_32k(seed, taus=(0.0, 0.002, 0.004, 0.01)):
     """MALA forward (cowa_mala_fwd) at 32768 tokens with full causal scoring: ms per call
     (scoring pass + gated pass) and the share of tiles whose PV was done, per tau, beside
-    the dense causal forward (cowa_fwd) and the scoring pass alone."""
+    the dense causal forward (cowa_fwd) and the scoring pass alone; then the backward
+    with the largest tau's decisions held fixed (cowa_mala_bwd) beside cowa_bwd."""
     import torch
     from structured_sparse_attention_plan_amd import api, inputs
     dev, L = "cuda:0", 32768
@@ -239,7 +240,17 @@ def mala_32k(seed, taus=(0.0, 0.002, 0.004, 0.01)):
         torch.cuda.synchronize()
         r["by_tau"][str(tau)] = {"ms": ms, "kept_share": float(kept.float().mean().item()),
                                  "vs_dense_fwd": r["dense_fwd_ms"] / ms}
-    del q, k, v, o, lse, kept
+    # the backward with the decisions of the largest tau held fixed, beside the dense one
+    do = inputs.attention_inputs(1, L, L, HQ, HKV, D, seed=seed + 1, device=dev, with_dout=True)[3]
+    pb = api.build_plan("mala_bwd", pf, dev)
+    ws = torch.empty(api.workspace_size("mala_bwd", pf), dtype=torch.uint8, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    r["dense_bwd_ms"] = _events_ms(lambda: api.bwd(q, k, v, o, lse, do, win, plan=pb, grads=grads,
+                                                   workspace=ws), 3, 1)
+    r["mala_bwd_ms"] = _events_ms(lambda: api.mala_bwd(q, k, v, o, lse, do, kept, plan, win, plan=pb,
+                                                       grads=grads, workspace=ws), 3, 1)
+    r["mala_bwd_tau"] = taus[-1]
+    del q, k, v, o, lse, kept, do, ws, grads
     torch.cuda.empty_cache()
     return r
 
@@ -286,7 +297,7 @@ def extras(seed, main_fb_ms, main_fwd_ms, main_bwd_ms, main_dec_ms, main_E, main
         torch.cuda.empty_cache()
         return r
 
-    # fp32 forward, L=1024, Hq=4, Hkv=2, D=64, sink 64, near 128, 64x64 tiles
+    # fp32 forward, L=1024, Hq=4, Hkv=2, D=64, sink 64, near 128, 8-token x 64-key tiles
     out["fwd_f32_1k"] = fwd_bwd(1024, 128, "complementary", dtype=torch.float32, hq=4, hkv=2, d=64,
                                 sink=64, bwd=False, steps=20, warmup=5)
     # 32K prefill forward

@@ -126,7 +126,7 @@ hipError_t launch_wcache_append(const WcacheAppendArgs& a, hipStream_t s);
 bool decode_supports_group(int G);
 
 // Tile shapes of each kernel family (tokens per q-block, keys per k-block).
-constexpr int kF32Bq = 64, kF32Bk = 64;
+constexpr int kF32Bq = 8, kF32Bk = 64;
 constexpr int kFwdRows = 256;  // query rows (tokens x GQA heads) per forward work item
 constexpr int kFwdBk = 64;
 constexpr int kBwdRows = 128;  // query rows per backward q-block

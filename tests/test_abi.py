@@ -60,7 +60,7 @@ def test_tile_sizes_and_workspace():
     assert api.tile_sizes("decode", pd) == (1, 64)
     assert api.workspace_size("decode", pd) > 0
     f = _prob(dtype=C.COWA_DTYPE_F32, D=64, Hq=4, Hkv=2)
-    assert api.tile_sizes("fwd", f) == (64, 64)
+    assert api.tile_sizes("fwd", f) == (8, 64)
 
 
 @pytest.mark.parametrize("op,kw,status", [

@@ -50,6 +50,26 @@ def test_fwd_f32_config1():
 
 
 @pytest.mark.parametrize("B,Lq,Lk,Hq,Hkv,sink,near,mode", [
+    (2, 300, 300, 4, 1, 8, 40, "complementary"),    # G = 4: 256 threads per group
+    (1, 200, 500, 2, 2, 16, 64, "duplicated"),      # G = 1, prefill chunk (Lq < Lk)
+    (1, 400, 250, 4, 2, 8, 40, "complementary"),    # Lq > Lk: the first 150 rows see nothing
+    (1, 333, 333, 4, 2, 0, 0, "complementary"),     # near = 0, no sink: empty rows
+    (1, 517, 517, 4, 2, 5, 20, "dense"),
+])
+def test_fwd_f32_small(B, Lq, Lk, Hq, Hkv, sink, near, mode):
+    _case(f"fwd f32 B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} sink={sink} near={near} {mode}")
+    ow, win = _windows(Lk, Hkv, sink, near, mode=mode)
+    q, k, v = inputs.attention_inputs(B, Lq, Lk, Hq, Hkv, 64, dtype=torch.float32, seed=3)
+    o, lse = api.fwd(q.to(DEV), k.to(DEV), v.to(DEV), win, scale=1 / 8)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.attn_fwd(q, k, v, ow, 1 / 8)
+    e_o, _ = errors(o, Oo)
+    e_l, _ = errors(lse, Lo)
+    print(f"  O max_abs={e_o:.3e} LSE max_abs={e_l:.3e}", flush=True)
+    assert e_o <= F32_MAX_ABS and e_l <= F32_MAX_ABS
+
+
+@pytest.mark.parametrize("B,Lq,Lk,Hq,Hkv,sink,near,mode", [
     (1, 1000, 1000, 40, 8, 16, 100, "complementary"),
     (2, 700, 700, 40, 8, 0, 64, "duplicated"),
     (1, 600, 600, 40, 8, 3, 50, "dense"),
