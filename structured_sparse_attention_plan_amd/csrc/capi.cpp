@@ -115,17 +115,6 @@ int decode_splits(const cowa_problem* p) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? COWA_OK : COWA_ERR_HIP; }
 
-// Blocks per decode split: the longest list a query at any position can have (the sink's blocks, the near window and the band each spanning at most
-// one block more than their length in blocks), so that split sizes follow the work.
-int32_t decode_split_blocks(const cowa_problem* p, int nsplit) {
-  const int64_t nkb = (p->Lk + kDecBk - 1) / kDecBk;
-  const int64_t bw = p->win.band_mode == COWA_BAND_DENSE ? (int64_t)p->Lk : (int64_t)p->win.lr;
-  int64_t tmax = ((int64_t)p->win.sink + kDecBk - 1) / kDecBk + ((int64_t)p->win.near_w + kDecBk - 1) / kDecBk + 1 +
-                 (bw + kDecBk - 1) / kDecBk + 1;
-  if (tmax > nkb) tmax = nkb;
-  return (int32_t)((tmax + nsplit - 1) / nsplit);
-}
-
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Byte offsets of the backward workspace: three fp32 arrays per (query head, row) (Delta,
@@ -425,7 +414,6 @@ extern "C" int cowa_decode(const cowa_problem* p, const cowa_plan_dev* plan, con
   a.o = o;
   a.lse = lse;
   a.nsplit = decode_splits(p);
-  a.split_blocks = decode_split_blocks(p, a.nsplit);
   const size_t rows = (size_t)p->B * p->Hq * a.nsplit;
   a.part = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + (rows * p->D * sizeof(float) + 255) / 256 * 256);
@@ -466,7 +454,6 @@ extern "C" int cowa_decode_varlen(const cowa_problem* p, const void* q, const vo
   a.part = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + (rows * p->D * sizeof(float) + 255) / 256 * 256);
   a.seqlens = seqlens_k;
-  a.split_blocks = decode_split_blocks(p, a.nsplit);
   a.B = p->B;
   a.Lk = p->Lk;
   a.Hq = p->Hq;
@@ -546,7 +533,6 @@ extern "C" int cowa_wcache_decode(const cowa_problem* p, const cowa_wcache* c, c
   a.part = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + (rows * p->D * sizeof(float) + 255) / 256 * 256);
   a.seqlens = seqlens;
-  a.split_blocks = decode_split_blocks(p, a.nsplit);
   a.B = p->B;
   a.Lk = p->Lk;
   a.Hq = p->Hq;

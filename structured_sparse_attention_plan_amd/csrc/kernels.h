@@ -88,7 +88,6 @@ struct DecodeArgs {
   const int32_t* seqlens;  // varlen / window-cache decode: [B] cache lengths (no plan); else null
   int32_t B, Lk, Hq, Hkv, G;
   int32_t Bk, nsplit;
-  int32_t split_blocks;  // varlen / window cache: visible blocks per split (at least)
   float scale_log2;
   DevWindow win;
   // window-only cache (wcache.h): k, v are [B, wslots, D]; null window_mode: full caches
