@@ -16,8 +16,9 @@
 //       operands (reading accumulation registers while the matrix core runs costs several
 //       cycles per value);
 //   [B] online softmax of S(t) in base 2 (scale * log2 e folded into one FMA), one
-//       element per slot beside the MFMAs; a boundary (PARTIAL) block gets the window
-//       predicate per element first;
+//       element per slot beside the MFMAs; a boundary (PARTIAL) block is masked first
+//       (each row's visible keys as one run where they form one, else the window
+//       predicate per element);
 //   [C] O^T += V(t-1)^T P(t-1)^T on the odd slots: P^T goes from the softmax registers
 //       straight into the B operand (no LDS round trip) and V^T is read from the
 //       row-major LDS tile with ds_read_b64_tr_b16, two 4-key runs per operand matching
