@@ -419,6 +419,92 @@ def mala_bwd(q, k, v, do, win, scale, Bq, Bk, kept):
     return dq, dk, dv
 
 
+def _kept_keys(kept, h, rows, Bq, Bk, keys):
+    """K_ij of the MALA backward for the given rows and keys: 1.0 where key j lies in a
+    kept tile (KV head h, forward q-block i // Bq, key block j // Bk), else 0.0."""
+    return np.asarray(kept[h][np.ix_(np.asarray(rows) // Bq, np.asarray(keys) // Bk)], dtype=np.float64)
+
+
+def mala_bwd_dq_rows(q, k, v, do, win, scale, Bq, Bk, kept, rows):
+    """dQ of mala_bwd on the query rows `rows` only: each row needs just its own full
+    softmax, its kept keys and Delta_i = sum_j P_ij dP_ij.  B must be 1.  -> [1, R, Hq, D]"""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Lq, Hq, D = q.shape
+    _, Lk, Hkv, _ = k.shape
+    assert B == 1
+    G = Hq // Hkv
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.arange(Lk)
+    dq = np.zeros((1, len(rows), Hq, D))
+    for h in range(Hkv):
+        P = _mala_rows(q, k, win, scale, h, rows, G, Lq)
+        kk = _kept_keys(kept, h, rows, Bq, Bk, keys)
+        for gi, qh in enumerate(range(h * G, (h + 1) * G)):
+            p = P[gi]
+            dp = (do[0, rows, qh, :] @ v[0, :, h, :].T) * kk
+            delta = (p * dp).sum(axis=1, keepdims=True)
+            dq[0, :, qh, :] = scale * ((p * (dp - delta)) @ k[0, :, h, :])
+    return dq
+
+
+def mala_bwd_dkdv_cols(q, k, v, do, win, scale, Bq, Bk, kept, cols, row_chunk=256, workers=1):
+    """dK and dV of mala_bwd on the key columns `cols` only, the way attn_bwd_dkdv_cols
+    gathers them: the rows that see a requested column are found from the mask, and per
+    chunk of such rows their full softmax over the keys the chunk sees, their kept keys
+    K_ij and Delta_i = dO_i . O_i with O_i = sum_j K_ij P_ij v_j (the MALA output) give
+      dS_ij = P_ij (K_ij dO_i . v_j - Delta_i),  dV_j = sum_i K_ij P_ij dO_i.
+    B must be 1.  -> dK [1, C, Hkv, D], dV [1, C, Hkv, D]"""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Lq, Hq, D = q.shape
+    _, Lk, Hkv, _ = k.shape
+    assert B == 1
+    G = Hq // Hkv
+    cols = np.asarray(cols, dtype=np.int64)
+
+    def chunk_part(h, rows):
+        dk = np.zeros((len(cols), D))
+        dv = np.zeros((len(cols), D))
+        m = mask_rows(rows, Lq, Lk, h, win)
+        keys = np.nonzero(m.any(axis=0))[0]
+        m = m[:, keys]
+        at = np.searchsorted(keys, cols)
+        seen = (at < len(keys)) & (keys[np.minimum(at, len(keys) - 1)] == cols)
+        kk = _kept_keys(kept, h, rows, Bq, Bk, keys)
+        kc = _kept_keys(kept, h, rows, Bq, Bk, cols)
+        ks, vs = k[0, keys, h, :], v[0, keys, h, :]
+        for qh in range(h * G, (h + 1) * G):
+            s = scale * (q[0, rows, qh, :] @ ks.T)
+            p, _ = _masked_softmax_row_stats(s, m)
+            o = (p * kk) @ vs
+            delta = (do[0, rows, qh, :] * o).sum(axis=1, keepdims=True)
+            pc = np.where(seen[None, :], p[:, np.minimum(at, len(keys) - 1)], 0.0)
+            dpc = (do[0, rows, qh, :] @ v[0, cols, h, :].T) * kc
+            dsc = pc * (dpc - delta)
+            dk += scale * (dsc.T @ q[0, rows, qh, :])
+            dv += (pc * kc).T @ do[0, rows, qh, :]
+        return h, dk, dv
+
+    tasks = []
+    for h in range(Hkv):
+        need = mask_rows(np.arange(Lq), Lq, Lk, h, win, keys=cols).any(axis=1)
+        rows_all = np.nonzero(need)[0]
+        for start in range(0, len(rows_all), row_chunk):
+            tasks.append((h, rows_all[start:start + row_chunk]))
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+            parts = list(ex.map(lambda t: chunk_part(*t), tasks))
+    else:
+        parts = [chunk_part(*t) for t in tasks]
+    dk = np.zeros((1, len(cols), Hkv, D))
+    dv = np.zeros((1, len(cols), Hkv, D))
+    for h, pk, pv in parts:
+        dk[0, :, h, :] += pk
+        dv[0, :, h, :] += pv
+    return dk, dv
+
+
 # --------------------------------------------------------------------------- tiles
 
 def tile_lists(Lq, Lk, Hkv, Bq, Bk, win):

@@ -109,6 +109,50 @@ def test_bwd_32k_key_columns_and_rows(mode):
     assert_bf16_close("dQ[sampled rows]", dq[:, torch.as_tensor(rows, device=DEV)], dqo, gradient=True)
 
 
+def _mala_kept_array(fplan, kept, L, Bk=64):
+    """The MALA forward's per-entry decisions as the oracle's [Hkv, nqb, nkb] array
+    (tiles outside the lists hold no visible key; their value does not matter)."""
+    rp = np.asarray(fplan.host.arrays["row_ptr"])
+    ent = np.asarray(fplan.host.arrays["row_ent"])
+    nqb = fplan.info.nqb
+    items = np.repeat(np.arange(len(rp) - 1), np.diff(rp))
+    kg = kept.cpu().numpy()[:len(items)]
+    assert set(np.unique(kg)) <= {0, 1}, "every listed tile gets a decision"
+    out = np.ones((HKV, nqb, -(-L // Bk)), dtype=bool)
+    out[items // nqb, items % nqb, ent[:len(items)] >> 1] = kg.astype(bool)
+    return out, int(kg.sum()), len(items)
+
+
+@pytest.mark.parametrize("mode,tau", [("complementary", 0.02), ("dense", 0.004)])
+def test_mala_bwd_32k_key_columns_and_rows(mode, tau):
+    """The MALA backward at 32K tokens under the kernel's own decisions: dK/dV on seeded
+    key columns and dQ on 256 stratified rows against the oracle."""
+    L, sink, near = 32768, 128, 2048
+    _case(f"MALA bwd 32K {mode} tau={tau}: dK/dV key columns, dQ sampled rows")
+    ow, win, (q, k, v, do) = _setup(L, sink, near, mode, seed=70, with_dout=True)
+    prob = api.problem(1, L, L, HQ, HKV, D, torch.bfloat16, SCALE, win)
+    fplan = api.build_plan("fwd", prob, DEV)
+    kept = torch.full((max(1, fplan.info.nnz),), -1, dtype=torch.int32, device=DEV)
+    o_lo = torch.empty_like(q)
+    o, lse = api.mala_fwd(q, k, v, win, tau, plan=fplan, kept=kept, o_lo=o_lo)
+    dq, dk, dv = api.mala_bwd(q, k, v, o, lse, do, kept, fplan, win, o_lo=o_lo)
+    torch.cuda.synchronize()
+    kept_np, n_kept, n_tiles = _mala_kept_array(fplan, kept, L)
+    print(f"  {n_kept} of {n_tiles} tiles kept", flush=True)
+    assert 0 < n_kept < n_tiles
+    qc, kc, vc, doc = q.cpu(), k.cpu(), v.cpu(), do.cpu()
+    Bq = fplan.info.Bq
+    cols = _cols_32k(L, near, ow.lr, mode)
+    t0 = time.time()
+    rk, rv = oracle.mala_bwd_dkdv_cols(qc, kc, vc, doc, ow, SCALE, Bq, 64, kept_np, cols,
+                                       workers=_workers())
+    print(f"  oracle: {len(cols)} key columns in {time.time() - t0:.1f} s", flush=True)
+    _cols_check("MALA 32K", dk, dv, cols, rk, rv)
+    rows = sample_rows(L, sink, near, ow.lr, HKV, 128 // 5, 256, seed=101)
+    dqo = oracle.mala_bwd_dq_rows(qc, kc, vc, doc, ow, SCALE, Bq, 64, kept_np, rows)
+    assert_bf16_close("dQ[sampled rows]", dq[:, torch.as_tensor(rows, device=DEV)], dqo, gradient=True)
+
+
 @pytest.fixture(scope="module")
 def run_128k():
     """One forward + backward of the 131072-token workload, results copied to the host."""

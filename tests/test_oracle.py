@@ -525,3 +525,29 @@ def test_mala_bwd_finite_differences_with_fixed_decisions():
             flat[idx] = old
             num.reshape(-1)[idx] = (fp - fm) / (2 * eps)
         np.testing.assert_allclose(g, num, atol=2e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("mode", [oracle.COMPLEMENTARY, oracle.DENSE])
+def test_mala_bwd_row_and_column_subsets_match_the_full_backward(mode):
+    """The sampled MALA gradients (dQ on rows, dK/dV on key columns) equal the rows and
+    columns of the full mala_bwd, under decisions that skip tiles (taken at tau = 0.1)
+    and under an arbitrary keep pattern; chunked and threaded column gathers agree."""
+    L, Hq, Hkv, D, Bq, Bk = 48, 4, 2, 8, 6, 8
+    win = W.for_length(L, Hkv, 3, 9, 0, mode=mode)
+    q, k, v = _mala_inputs(L, Hq, Hkv, D, 130)
+    do = _rand((1, L, Hq, D), 133)
+    scale = 0.5
+    _, _, kept_tau = oracle.mala_fwd(q, k, v, win, scale, 0.1, Bq, Bk)
+    assert 0 < (~kept_tau).sum() and kept_tau.sum() > 0
+    rng = np.random.default_rng(7)
+    for kept in (kept_tau, rng.random(kept_tau.shape) < 0.5):
+        dq, dk, dv = oracle.mala_bwd(q, k, v, do, win, scale, Bq, Bk, kept)
+        rows = [0, 1, 5, 6, 17, 30, 47]
+        cols = [0, 2, 3, 8, 20, 39, 46, 47]
+        np.testing.assert_allclose(oracle.mala_bwd_dq_rows(q, k, v, do, win, scale, Bq, Bk, kept, rows),
+                                   dq[:, rows], atol=1e-12)
+        for chunk, workers in ((256, 1), (5, 3)):
+            rk, rv = oracle.mala_bwd_dkdv_cols(q, k, v, do, win, scale, Bq, Bk, kept, cols,
+                                               row_chunk=chunk, workers=workers)
+            np.testing.assert_allclose(rk, dk[:, cols], atol=1e-12)
+            np.testing.assert_allclose(rv, dv[:, cols], atol=1e-12)
