@@ -229,14 +229,16 @@ def mala_32k(seed, taus=(0.0, 0.002, 0.004, 0.01)):
     o = torch.empty_like(q)
     lse = torch.empty((1, HQ, L), dtype=torch.float32, device=dev)
     kept = torch.empty(plan.info.nnz, dtype=torch.int32, device=dev)
+    mws = torch.empty(api.workspace_size("mala_fwd", pf), dtype=torch.uint8, device=dev)
     E = plan.info.edges * (HQ // HKV)
     r = {"window": "dense (full causal scoring)", "edges": E, "tiles": plan.info.nnz,
          "dense_fwd_ms": _events_ms(lambda: api.fwd(q, k, v, win, plan=plan, out=o, lse=lse), 5, 2)}
     r["mala_scoring_only_tau_above_1_ms"] = _events_ms(
-        lambda: api.mala_fwd(q, k, v, win, 2.0, plan=plan, out=o, lse=lse), 5, 2)
+        lambda: api.mala_fwd(q, k, v, win, 2.0, plan=plan, out=o, lse=lse, workspace=mws), 5, 2)
     r["by_tau"] = {}
     for tau in taus:
-        ms = _events_ms(lambda: api.mala_fwd(q, k, v, win, tau, plan=plan, out=o, lse=lse, kept=kept), 5, 2)
+        ms = _events_ms(lambda: api.mala_fwd(q, k, v, win, tau, plan=plan, out=o, lse=lse, kept=kept,
+                                             workspace=mws), 5, 2)
         torch.cuda.synchronize()
         r["by_tau"][str(tau)] = {"ms": ms, "kept_share": float(kept.float().mean().item()),
                                  "vs_dense_fwd": r["dense_fwd_ms"] / ms}
@@ -250,7 +252,7 @@ def mala_32k(seed, taus=(0.0, 0.002, 0.004, 0.01)):
     r["mala_bwd_ms"] = _events_ms(lambda: api.mala_bwd(q, k, v, o, lse, do, kept, plan, win, plan=pb,
                                                        grads=grads, workspace=ws), 3, 1)
     r["mala_bwd_tau"] = taus[-1]
-    del q, k, v, o, lse, kept, do, ws, grads
+    del q, k, v, o, lse, kept, do, ws, grads, mws
     torch.cuda.empty_cache()
     return r
 

@@ -140,7 +140,7 @@ typedef struct cowa_plan_dev {
 
 /* ---------------------------------------------------------------- problem */
 enum { COWA_DTYPE_BF16 = 0, COWA_DTYPE_F32 = 1 };
-enum { COWA_OP_FWD = 0, COWA_OP_BWD = 1, COWA_OP_DECODE = 2, COWA_OP_MALA_BWD = 3 };
+enum { COWA_OP_FWD = 0, COWA_OP_BWD = 1, COWA_OP_DECODE = 2, COWA_OP_MALA_BWD = 3, COWA_OP_MALA_FWD = 4 };
 
 typedef struct cowa_problem {
   int32_t B, Lq, Lk, Hq, Hkv, D;
@@ -157,7 +157,8 @@ int cowa_tile_sizes(int op, const cowa_problem* p, int32_t* Bq, int32_t* Bk);
  * three fp32 values per (query head, row) (Delta, the power-of-two scales of Q and dO),
  * 256 bytes of launch-wide maxima, fp16 copies of Q and dO (2 * B * Lq * Hq * D * 2
  * bytes) and of K (B * Lk * Hkv * D * 2 bytes); the decode keeps its split partials.
- * COWA_OP_MALA_BWD adds one byte per forward tile (Hkv * ceil(Lq / Bq_f) * ceil(Lk / 64),
+ * COWA_OP_MALA_FWD needs 1 KB per visible forward tile and sequence plus the kept lists
+ * (cowa_mala_fwd); COWA_OP_MALA_BWD adds one byte per forward tile (Hkv * ceil(Lq / Bq_f) * ceil(Lk / 64),
  * Bq_f the forward's tile height, rounded up to 256) to the backward's workspace. */
 int cowa_workspace_size(int op, const cowa_problem* p, size_t* bytes);
 
@@ -183,11 +184,12 @@ int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan,
  * CoWA: beyondmarketintelligence.com post, second paragraph and takeaway; crimsonlingua.com
  * news item, fifth paragraph): the QK scoring stays full, and the softmax's own
  * statistics decide whether the rest of a tile's work is done.  Readings fixed here: a
- * first pass scores every visible key and writes the exact LSE; the second pass takes
- * each row's probability mass in every tile (KV head, q-block of the forward's tiling,
- * k-block) from P = exp(scale q.k - LSE) and issues the tile's PV products only when some
- * row of the tile puts at least `tau` of its mass there; O = sum over kept tiles of P V,
- * the denominator staying the full one.  tau = 0 keeps every tile (exact attention); a
+ * tile is (KV head, q-block of the forward's tiling, k-block); it is kept when some row
+ * of the tile puts at least `tau` of its probability mass P = exp(scale q.k - LSE) there;
+ * O = sum over kept tiles of P V, the denominator staying the full one.  A scoring pass
+ * scores every visible key, writes the exact LSE and keeps each tile's row sums; the
+ * decisions follow from them and the LSE; a last pass runs the kept tiles only
+ * (scores and PV products).  tau = 0 keeps every tile (exact attention); a
  * row loses at most its dropped mass times max |v| per dimension.  The window is the
  * visibility the scoring covers (COWA_BAND_DENSE: full causal scoring, as the pages
  * describe MALA; the CoWA windows give MALA on top of CoWA).
@@ -195,11 +197,15 @@ int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan,
  * o_lo (may be NULL): O's bf16 rounding residual, as in cowa_fwd, for cowa_mala_bwd.
  * kept (may be NULL; B = 1 only): int32 per entry of the plan's row lists, set to 1 where
  * the tile's PV was done and 0 where it was skipped.  The plan is a forward plan
- * (cowa_tile_sizes(COWA_OP_FWD)).  Errors: INVALID_ARG (also for tau < 0 or NaN, and kept
- * with B > 1), UNSUPPORTED (not BF16 / D = 128), PLAN_MISMATCH, HIP. */
+ * (cowa_tile_sizes(COWA_OP_FWD)).  workspace: cowa_workspace_size(COWA_OP_MALA_FWD) bytes
+ * (per sequence, 1 KB per visible forward tile for the row sums and 4 bytes per tile and
+ * per item for the kept lists), 256-byte aligned.  Errors: INVALID_ARG (also for tau < 0
+ * or NaN, and kept with B > 1), UNSUPPORTED (not BF16 / D = 128), WORKSPACE_TOO_SMALL,
+ * PLAN_MISMATCH, HIP. */
 int cowa_mala_fwd(const cowa_problem* p, const cowa_plan_dev* plan, float tau,
                   const void* q, const void* k, const void* v, void* o, float* lse,
-                  void* o_lo, int32_t* kept, void* stream);
+                  void* o_lo, int32_t* kept, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /* Backward from the saved LSE: the pattern serves training forward and backward alike
  * (beyondmarketintelligence.com post, second paragraph; "CoWindow Attention" abstract),

@@ -19,7 +19,7 @@ COWA_ERR_HIP = -5
 
 COWA_BAND_COMPLEMENTARY, COWA_BAND_DUPLICATED, COWA_BAND_DENSE = 0, 1, 2
 COWA_DTYPE_BF16, COWA_DTYPE_F32 = 0, 1
-COWA_OP_FWD, COWA_OP_BWD, COWA_OP_DECODE, COWA_OP_MALA_BWD = 0, 1, 2, 3
+COWA_OP_FWD, COWA_OP_BWD, COWA_OP_DECODE, COWA_OP_MALA_BWD, COWA_OP_MALA_FWD = 0, 1, 2, 3, 4
 COWA_BWD_DELTA, COWA_BWD_DQ, COWA_BWD_DKDV, COWA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTS = ("cowa_status_string", "cowa_window_make", "cowa_plan_blocks", "cowa_tile_sizes",
@@ -81,7 +81,7 @@ def _load():
                              _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
     lib.cowa_fwd.restype = ctypes.c_int
     lib.cowa_mala_fwd.argtypes = [ctypes.POINTER(cowa_problem), ctypes.POINTER(cowa_plan_dev),
-                                  ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p]
+                                  ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
     lib.cowa_mala_fwd.restype = ctypes.c_int
     lib.cowa_bwd.argtypes = [ctypes.POINTER(cowa_problem), ctypes.POINTER(cowa_plan_dev),
                              _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_int, _p, ctypes.c_size_t,

@@ -15,7 +15,7 @@ from . import _cowa as C
 MODES = {"complementary": C.COWA_BAND_COMPLEMENTARY, "duplicated": C.COWA_BAND_DUPLICATED,
          "dense": C.COWA_BAND_DENSE}
 OPS = {"fwd": C.COWA_OP_FWD, "bwd": C.COWA_OP_BWD, "decode": C.COWA_OP_DECODE,
-       "mala_bwd": C.COWA_OP_MALA_BWD}
+       "mala_bwd": C.COWA_OP_MALA_BWD, "mala_fwd": C.COWA_OP_MALA_FWD}
 
 
 def make_window(Lmax, Hkv, sink, near, gap=0, mode="complementary"):
@@ -153,10 +153,12 @@ def fwd(q, k, v, win, scale=None, plan=None, out=None, lse=None, o_lo=None):
     return out, lse
 
 
-def mala_fwd(q, k, v, win, tau, scale=None, plan=None, out=None, lse=None, kept=None, o_lo=None):
+def mala_fwd(q, k, v, win, tau, scale=None, plan=None, out=None, lse=None, kept=None, o_lo=None,
+             workspace=None):
     """MALA forward (cowa_mala_fwd): -> (o like q, lse [B,Hq,Lq] fp32).  kept: optional
     int32 tensor of the plan's nnz entries, filled with the per-tile keep decisions;
-    o_lo: optional tensor like q for O's rounding residual (for mala_bwd)."""
+    o_lo: optional tensor like q for O's rounding residual (for mala_bwd); workspace:
+    optional uint8 tensor of workspace_size("mala_fwd") bytes."""
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     scale = D ** -0.5 if scale is None else scale
@@ -173,10 +175,12 @@ def mala_fwd(q, k, v, win, tau, scale=None, plan=None, out=None, lse=None, kept=
         _check_tensor("kept", kept, (max(1, plan.info.nnz),), torch.int32, q.device)
     if o_lo is not None:
         _check_tensor("o_lo", o_lo, (B, Lq, Hq, D), q.dtype, q.device)
+    workspace = _workspace("workspace", workspace, workspace_size("mala_fwd", prob), q.device)
     C.check("cowa_mala_fwd", C.lib.cowa_mala_fwd(
         ctypes.byref(prob), ctypes.byref(plan.struct), float(tau), q.data_ptr(), k.data_ptr(),
         v.data_ptr(), out.data_ptr(), lse.data_ptr(), None if o_lo is None else o_lo.data_ptr(),
-        None if kept is None else kept.data_ptr(), _stream(q.device)))
+        None if kept is None else kept.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        _stream(q.device)))
     return out, lse
 
 

@@ -56,6 +56,9 @@ int check_op_support(int op, const cowa_problem* p) {
     case COWA_OP_BWD:
       return (p->dtype == COWA_DTYPE_BF16 && p->D == 128 && G <= kBwdRows) ? COWA_OK
                                                                            : COWA_ERR_UNSUPPORTED;
+    case COWA_OP_MALA_FWD:
+      return (p->dtype == COWA_DTYPE_BF16 && p->D == 128 && G <= kFwdRows) ? COWA_OK
+                                                                           : COWA_ERR_UNSUPPORTED;
     case COWA_OP_MALA_BWD:  // one sequence: the forward's keep flags exist for B = 1 only
       return (p->dtype == COWA_DTYPE_BF16 && p->D == 128 && G <= kBwdRows && p->B == 1)
                  ? COWA_OK
@@ -72,6 +75,7 @@ void tiles_for(int op, const cowa_problem* p, int32_t* Bq, int32_t* Bk) {
   const int G = p->Hq / p->Hkv;
   switch (op) {
     case COWA_OP_FWD:
+    case COWA_OP_MALA_FWD:
       if (p->dtype == COWA_DTYPE_F32) {
         *Bq = kF32Bq;
         *Bk = kF32Bk;
@@ -139,6 +143,21 @@ BwdLayout bwd_layout(const cowa_problem* p) {
   return l;
 }
 
+// MALA forward workspace: per (sequence, forward entry, row) the scoring pass's log2 row
+// numerator (fp32), the kept entries per (sequence, entry) and their counts per
+// (sequence, item).
+struct MalaFwdLayout {
+  size_t mass, ents, counts, total;
+};
+MalaFwdLayout mala_fwd_layout(const cowa_problem* p, int64_t nnz, int64_t n_items) {
+  MalaFwdLayout l;
+  l.mass = 0;
+  l.ents = round256((size_t)p->B * (size_t)nnz * kFwdRows * sizeof(float));
+  l.counts = l.ents + round256((size_t)p->B * (size_t)nnz * sizeof(int32_t));
+  l.total = l.counts + round256((size_t)p->B * (size_t)n_items * sizeof(int32_t));
+  return l;
+}
+
 // MALA backward: the forward's tiling (Bq_f tokens, 64 keys) and the byte mask of its
 // keep flags [Hkv, nqb_f, nkb_f] after the backward workspace.
 struct MalaTiles {
@@ -194,6 +213,16 @@ extern "C" int cowa_workspace_size(int op, const cowa_problem* p, size_t* bytes)
     case COWA_OP_MALA_BWD:
       *bytes = bwd_layout(p).total + mala_tiles(p).mask_bytes;
       break;
+    case COWA_OP_MALA_FWD: {  // the number of visible forward tiles, from the planner's count
+      int32_t Bq, Bk;
+      tiles_for(COWA_OP_FWD, p, &Bq, &Bk);
+      cowa_plan_info info{};
+      st = cowa_plan_blocks(p->Lq, p->Lk, p->Hkv, Bq, Bk, &p->win, &info, nullptr, nullptr, nullptr,
+                            nullptr, nullptr, nullptr);
+      if (st != COWA_OK) return st;
+      *bytes = mala_fwd_layout(p, info.nnz, (int64_t)p->Hkv * info.nqb).total;
+      break;
+    }
     default: {
       const size_t rows = (size_t)p->B * p->Hq * decode_splits(p);
       const size_t part = (rows * p->D * sizeof(float) + 255) / 256 * 256;
@@ -248,15 +277,19 @@ extern "C" int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan, const 
 
 extern "C" int cowa_mala_fwd(const cowa_problem* p, const cowa_plan_dev* plan, float tau, const void* q,
                              const void* k, const void* v, void* o, float* lse, void* o_lo,
-                             int32_t* kept, void* stream) {
+                             int32_t* kept, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_problem(p);
   if (st != COWA_OK) return st;
-  if (p->dtype != COWA_DTYPE_BF16) return COWA_ERR_UNSUPPORTED;
-  st = check_op_support(COWA_OP_FWD, p);
+  st = check_op_support(COWA_OP_MALA_FWD, p);
   if (st != COWA_OK) return st;
   if (!q || !k || !v || !o || !lse || !(tau >= 0.f)) return COWA_ERR_INVALID_ARG;
+  if (kept && p->B != 1) return COWA_ERR_INVALID_ARG;
   st = check_plan(COWA_OP_FWD, p, plan, false);
   if (st != COWA_OK) return st;
+  const MalaFwdLayout wl = mala_fwd_layout(p, plan->info.nnz, (int64_t)p->Hkv * plan->info.nqb);
+  if (!workspace || workspace_bytes < wl.total) return COWA_ERR_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)workspace & 255) != 0) return COWA_ERR_INVALID_ARG;
+  if (plan->info.nnz > INT32_MAX) return COWA_ERR_UNSUPPORTED;
   FwdArgs a{};
   a.q = q;
   a.k = k;
@@ -282,8 +315,12 @@ extern "C" int cowa_mala_fwd(const cowa_problem* p, const cowa_plan_dev* plan, f
   a.win = dev_window(p->win);
   a.o_lo = o_lo;
   a.mala_tau = tau;
-  a.kept = (p->B == 1) ? kept : nullptr;
-  if (kept && p->B != 1) return COWA_ERR_INVALID_ARG;
+  a.kept = kept;
+  char* const ws = (char*)workspace;
+  a.mala_mass = (float*)(ws + wl.mass);
+  a.mala_ents = (int32_t*)(ws + wl.ents);
+  a.mala_counts = (int32_t*)(ws + wl.counts);
+  a.mala_nnz = (int32_t)plan->info.nnz;
   return hip_status(launch_mala_fwd_bf16_d128(a, (hipStream_t)stream));
 }
 

@@ -106,10 +106,12 @@ __device__ __forceinline__ void mfma_v0(f32x16& acc, const bf16x8& a, const bf16
 }
 
 
-// MODE 0: the CoWA forward.  MODE 1: scoring only (no PV): LSE over every visible key.
-// MODE 2: the MALA pass, given that LSE: P = exp(scale s - LSE) exactly normalised, a
-// tile's PV is issued only when some row of the work item puts at least tau of its
-// probability mass in it, O = sum of the kept P V (no division), LSE left as it is.
+// MODE 0: the CoWA forward.  MODE 1: scoring only (no PV): LSE over every visible key,
+// and per tile and row the log2 of the row's probability numerator in the tile (the
+// tile's row sum in the reference then in use, plus that reference), from which
+// mala_decide_kernel finds each tile's largest row mass once the LSE is known.
+// MODE 2: the MALA pass over the kept tiles only, given that LSE: P = exp(scale s - LSE)
+// exactly normalised, O = sum of the kept P V (no division), LSE left as it is.
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 sQ[ROWS * D];
@@ -120,8 +122,6 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 sK1[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV0[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV1[TILE];
-  // MALA: the largest row mass of each wave in the last two tiles (by tile parity)
-  __shared__ float sMass[2][WAVES];
   auto kbuf = [&](auto c) __attribute__((always_inline)) -> __bf16* {
     if constexpr ((decltype(c)::value & 1) == 0) return sK0;
     else return sK1;
@@ -240,7 +240,9 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   }
 
   const int e0 = a.row_ptr[item];
-  const int nt = a.row_ptr[item + 1] - e0;
+  // MALA pass: the item's kept entries, compacted at the same offsets
+  const int nt = MODE == 2 ? a.mala_counts[(int64_t)b * a.n_items + item] : a.row_ptr[item + 1] - e0;
+  const int32_t* const ents = MODE == 2 ? a.mala_ents + (int64_t)b * a.mala_nnz : a.row_ent;
   // LDS addressing.  With the chunk swizzle, the operand addresses of one lane differ
   // only by an XOR of the chunk bits, so each is one XOR away from a per-lane base:
   //   K / Q rows n of a tile at dd: kofs ^ (dd << 5) bytes (+ 8192 for key / row block 1);
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   // load would share its wait counter with the LDS operand reads, whose first wait would
   // then also wait for it.
   int ent0 = 0, ent1 = 0, ent2 = 0;
-  const __amdgpu_buffer_rsrc_t r_ent = make_rsrc(a.row_ent + e0, (int64_t)nt * 4);
+  const __amdgpu_buffer_rsrc_t r_ent = make_rsrc(ents + e0, (int64_t)nt * 4);
   int ent_next = 0;  // entry t+3 in flight (VGPR)
 
   // Iteration t (parity PAR = t % 2) is one block of 64 MFMA slots:
@@ -400,16 +402,6 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   // buffers of K(t) and V(t-2), which every wave finished with in iteration t-1.
   f32x16 sx[2][KB2][CB];
   bf16x8 pf[2][KB2][CB][2];
-  // MALA: the keep decision of tile `tile` from the waves' masses of that tile, uniform
-  // across the work group (read after the barrier that follows their writes)
-  auto mala_keep = [&](int tile) __attribute__((always_inline)) {
-    const float* mp = sMass[tile & 1];
-    const float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
-    const bool keep = __builtin_amdgcn_readfirstlane(mx >= a.mala_tau ? 1 : 0) != 0;
-    if (a.kept && tid == 0) a.kept[e0 + tile] = keep ? 1 : 0;
-    return keep;
-  };
-
   auto iteration = [&](auto parity, int t) __attribute__((always_inline)) {
     constexpr int PAR = decltype(parity)::value;
     f32x16(&sc)[KB2][CB] = sx[PAR];      // S(t)
@@ -417,9 +409,6 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     bf16x8(&pfc)[KB2][CB][2] = pf[PAR];
     const bf16x8(&pfp)[KB2][CB][2] = pf[PAR ^ 1];
     wait_loads_and_barrier();  // K(t+1), V(t-1) resident; every wave is done with t-1
-    // MALA: PV of tile t-1 only when the tile is kept (none before the first tile)
-    bool keep_pv = MODE == 0;
-    if constexpr (MODE == 2) keep_pv = t > 0 && mala_keep(t - 1);
     const __amdgpu_buffer_rsrc_t rk = tile_copy_rsrc(kbase, ent2, t + 2 < nt);
     const __amdgpu_buffer_rsrc_t rv = tile_copy_rsrc(vbase, ent0, true);
     __bf16* const kdst = kbuf(IC<PAR>{});          // K(t+2)
@@ -522,27 +511,12 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     });
     };
-    if constexpr (MODE == 0) slots(IC<1>{});
-    else if constexpr (MODE == 1) slots(IC<0>{});
-    else {
-      if (keep_pv) slots(IC<1>{});
-      else slots(IC<0>{});
-    }
+    if constexpr (MODE == 1) slots(IC<0>{});
+    else slots(IC<1>{});
     fold(IC<62>{});
     fold(IC<63>{});
 
-    if constexpr (MODE == 2) {
-      // the tile's row masses (both lane halves of a column), their max over the wave's
-      // 64 rows for the keep decision at the next barrier; no reference to move: P is
-      // normalised by the given LSE
-      float mx = 0.f;
-#pragma unroll
-      for (int c = 0; c < CB; ++c) mx = fmaxf(mx, sum[c] + swap_halves(sum[c]));
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      if (lane == 0) sMass[PAR][wave] = mx;
-      return;
-    }
+    if constexpr (MODE == 2) return;  // P normalised by the given LSE: no reference to move
 
     // reference check on the column sums (both lane halves)
     float alpha[CB] = {1.f, 1.f};
@@ -582,6 +556,17 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int c = 0; c < CB; ++c) l[c] = l[c] * alpha[c] + sum[c];  // fp32 row sums set LSE
+    if constexpr (MODE == 1) {
+      // the tile's row numerators in log2 (both lane halves of a column, in the reference
+      // the sums were taken in); rows without a token get -inf
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const float cs = sum[c] + swap_halves(sum[c]);
+        const float lm = (rvalid[c] & (cs > 0.f)) ? log2f(cs) + m[c] : -INFINITY;
+        if (h2 == 0)
+          a.mala_mass[(((int64_t)b * a.mala_nnz + e0 + t) * ROWS) + wave * WROWS + c * 32 + n] = lm;
+      }
+    }
   };
 
   // O^T += V(t)^T P(t)^T for the last tile, alone
@@ -597,9 +582,9 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   };
 
   if (nt > 0) {
-    ent0 = load_uniform(a.row_ent, e0);
-    ent1 = nt > 1 ? load_uniform(a.row_ent, e0 + 1) : 0;
-    ent2 = nt > 2 ? load_uniform(a.row_ent, e0 + 2) : 0;
+    ent0 = load_uniform(ents, e0);
+    ent1 = nt > 1 ? load_uniform(ents, e0 + 1) : 0;
+    ent2 = nt > 2 ? load_uniform(ents, e0 + 2) : 0;
     ent_next = __builtin_amdgcn_raw_buffer_load_b32(r_ent, 0, 4 * 3, 0);
     {
       const __amdgpu_buffer_rsrc_t rk0 = tile_copy_rsrc(kbase, ent0, true);
@@ -643,10 +628,8 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     }
     wait_loads_and_barrier();  // V(nt-1) resident
     if constexpr (MODE != 1) {
-      if (MODE == 0 || mala_keep(nt - 1)) {
-        if ((nt - 1) & 1) last_pv(IC<1>{});
-        else last_pv(IC<0>{});
-      }
+      if ((nt - 1) & 1) last_pv(IC<1>{});
+      else last_pv(IC<0>{});
     }
   }
 
@@ -684,6 +667,52 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   }
 }
 
+// MALA decisions, one work group per (item, sequence): thread r owns row r of the item
+// (its LSE from the scoring pass); a tile is kept when its largest row mass
+// 2^(numerator - LSE) reaches tau.  Tiles go 16 at a time (16 independent loads per
+// thread, one barrier); thread 0 writes the decisions and the kept entries in list order.
+constexpr int DEC_TILES = 16;
+__global__ __launch_bounds__(ROWS) void mala_decide_kernel(FwdArgs a) {
+  __shared__ float smax[DEC_TILES][WAVES];
+  const int item = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = item / a.nqb, qb = item - h * a.nqb;
+  const int e0 = a.row_ptr[item], nt = a.row_ptr[item + 1] - e0;
+  const int rt = tid / a.G, g = tid - rt * a.G, t = qb * a.Bq + rt;
+  const bool valid = (rt < a.Bq) & (t < a.Lq);
+  const float lv = valid ? a.lse[((int64_t)b * a.Hq + h * a.G + g) * a.Lq + t] : -INFINITY;
+  const float lse2 = lv * kLog2e;
+  const float* mass = a.mala_mass + ((int64_t)b * a.mala_nnz + e0) * ROWS + tid;
+  int32_t* const ents = a.mala_ents + (int64_t)b * a.mala_nnz + e0;
+  int cnt = 0;
+  for (int i0 = 0; i0 < nt; i0 += DEC_TILES) {
+    float x[DEC_TILES];
+#pragma unroll
+    for (int j = 0; j < DEC_TILES; ++j) {
+      const float lm = i0 + j < nt ? mass[(int64_t)(i0 + j) * ROWS] : -INFINITY;
+      x[j] = (lv > -INFINITY && lm > -INFINITY) ? exp2f(lm - lse2) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < DEC_TILES; ++j) {
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) x[j] = fmaxf(x[j], __shfl_xor(x[j], off));
+      if (lane == 0) smax[j][wave] = x[j];
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int j = 0; j < DEC_TILES && i0 + j < nt; ++j) {
+        float mx = smax[j][0];
+        for (int w = 1; w < WAVES; ++w) mx = fmaxf(mx, smax[j][w]);
+        const bool keep = mx >= a.mala_tau;
+        if (a.kept && b == 0) a.kept[e0 + i0 + j] = keep ? 1 : 0;
+        if (keep) ents[cnt++] = a.row_ent[e0 + i0 + j];
+      }
+    }
+    __syncthreads();  // smax is rewritten by the next group
+  }
+  if (tid == 0) a.mala_counts[(int64_t)b * a.n_items + item] = cnt;
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16_d128(const FwdArgs& a, hipStream_t s) {
@@ -697,6 +726,8 @@ hipError_t launch_mala_fwd_bf16_d128(const FwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(fwd_bf16_d128_kernel<1>, grid, dim3(256), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(mala_decide_kernel, grid, dim3(ROWS), 0, s, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(fwd_bf16_d128_kernel<2>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

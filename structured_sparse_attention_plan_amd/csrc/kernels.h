@@ -35,6 +35,13 @@ struct FwdArgs {
   DevWindow win;
   float mala_tau;    // MALA: keep a tile when some row's probability mass in it is >= tau
   int32_t* kept;     // MALA: per row-list entry, 1 if the tile's PV was done (may be null)
+  // MALA workspace: per (sequence, row-list entry, row of the item) the log2 of the row's
+  // probability numerator in the tile (scoring pass), the kept entries of each item
+  // (compacted in list order) and their count per (sequence, item)
+  float* mala_mass;        // [B, nnz, kFwdRows]
+  int32_t* mala_ents;      // [B, nnz]
+  int32_t* mala_counts;    // [B, n_items]
+  int32_t mala_nnz;
 };
 
 struct BwdArgs {

@@ -56,6 +56,13 @@ def test_tile_sizes_and_workspace():
     pl = _prob(Lq=4096, Lk=4096)
     assert (api.workspace_size("mala_bwd", pl) - api.workspace_size("bwd", pl)
             == -(-(8 * -(-4096 // 51) * 64) // 256) * 256)
+    # MALA forward: 1 KB of row sums and 4 bytes of kept list per visible forward tile,
+    # 4 bytes per item, each part rounded up to 256
+    bq, bk = api.tile_sizes("fwd", pl)
+    info = api.plan_info(4096, 4096, 8, bq, bk, pl.win)
+    r256 = lambda x: -(-x // 256) * 256  # noqa: E731
+    assert api.workspace_size("mala_fwd", pl) == (r256(info.nnz * 1024) + r256(info.nnz * 4)
+                                                  + r256(8 * info.nqb * 4))
     pd = _prob(Lq=1, Lk=4096)
     assert api.tile_sizes("decode", pd) == (1, 64)
     assert api.workspace_size("decode", pd) > 0
@@ -139,13 +146,15 @@ def test_entry_points_validate_before_launch():
     assert C.lib.cowa_mala_bwd(ctypes.byref(p), ctypes.byref(pf), ctypes.byref(pm), x, x, x, x, x,
                                None, x, x, x, x, x, ctypes.c_void_p(256), api.workspace_size("bwd", p),
                                None) == C.COWA_ERR_WORKSPACE_TOO_SMALL
-    # MALA forward: negative tau, keep flags with B > 1
+    # MALA forward: negative tau, keep flags with B > 1, workspace too small
     assert C.lib.cowa_mala_fwd(ctypes.byref(p), ctypes.byref(pf), -0.5, x, x, x, x, x, None, None,
-                               None) == C.COWA_ERR_INVALID_ARG
+                               ctypes.c_void_p(256), big, None) == C.COWA_ERR_INVALID_ARG
     p2b = _prob(B=2)
     pf2 = _fake_plan(p2b, "fwd")
     assert C.lib.cowa_mala_fwd(ctypes.byref(p2b), ctypes.byref(pf2), 0.1, x, x, x, x, x, None, x,
-                               None) == C.COWA_ERR_INVALID_ARG
+                               ctypes.c_void_p(256), big, None) == C.COWA_ERR_INVALID_ARG
+    assert C.lib.cowa_mala_fwd(ctypes.byref(p), ctypes.byref(pf), 0.1, x, x, x, x, x, None, None,
+                               ctypes.c_void_p(256), 16, None) == C.COWA_ERR_WORKSPACE_TOO_SMALL
     # decode: workspace too small
     pd = _prob(Lq=1, Lk=4096, win=api.make_window(4096, 8, 4, 16))
     pld = _fake_plan(pd, "decode")
