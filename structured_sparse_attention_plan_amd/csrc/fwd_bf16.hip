@@ -466,8 +466,12 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
       vf[1] = vfrag(vt, vofs, 0, 0, 1);
     }
     float xin = (sc[0][0][0]);
+    float xin1 = MODE == 1 ? (sc[0][0][1]) : 0.f;  // scoring: the second element of a slot
     static_for<0, 64>([&](auto slot) __attribute__((always_inline)) {
       constexpr int s = decltype(slot)::value;
+      // scoring (MODE 1, no PV products): the odd slots hold nothing; each even slot takes
+      // the softmax of elements s and s + 1 beside its product, and the K copies
+      if constexpr (MODE == 1 && (s & 1) == 1) return;
       if constexpr ((s & 1) == 0) {
         // MFMA k = s / 2 covers dd = k / 4, (k2, c) = k % 4
         constexpr int k = s >> 1, dd = k >> 2, k2 = (k >> 1) & 1, c = k & 1;
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
         }
         acc[c][db] = mfma32x32x16(vf[g % 3], pfp[k2][c][hf], acc[c][db]);
       }
-      if constexpr ((s & 7) == 5) {
+      if constexpr ((s & 7) == (MODE == 1 ? 4 : 5)) {
         constexpr int u = s >> 3;  // 0..7: K(t+2) copies, then V(t) copies
         if constexpr (u < 4) copy_tile(rk, u, kdst);
         else if constexpr (MODE != 1) copy_tile(rv, u - 4, vdst);  // scoring reads no V
@@ -503,10 +507,26 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
         // statement does not count as a wait state, and a VALU read of a transcendental
         // result needs one.
         constexpr int c = s >> 5;
-        const float x = xin;
-        if constexpr (s + 1 < 64) xin = (sc[((s + 1) >> 4) & 1][(s + 1) >> 5][(s + 1) & 15]);
-        if constexpr (s >= 2) fold(IC<s - 2>{});
-        pb[s & 7] = __builtin_amdgcn_exp2f(fmaf(x, a.scale_log2, -m[c]));
+        if constexpr (MODE == 1) {
+          // elements s, s + 1 (one row block: s is even), their inputs taken a slot ahead;
+          // the previous slot's two elements join the row sum
+          const float x0 = xin, x1 = xin1;
+          if constexpr (s + 2 < 64) {
+            xin = (sc[((s + 2) >> 4) & 1][(s + 2) >> 5][(s + 2) & 15]);
+            xin1 = (sc[((s + 3) >> 4) & 1][(s + 3) >> 5][(s + 3) & 15]);
+          }
+          if constexpr (s >= 2) {
+            fold(IC<s - 2>{});
+            fold(IC<s - 1>{});
+          }
+          pb[s & 7] = __builtin_amdgcn_exp2f(fmaf(x0, a.scale_log2, -m[c]));
+          pb[(s + 1) & 7] = __builtin_amdgcn_exp2f(fmaf(x1, a.scale_log2, -m[c]));
+        } else {
+          const float x = xin;
+          if constexpr (s + 1 < 64) xin = (sc[((s + 1) >> 4) & 1][(s + 1) >> 5][(s + 1) & 15]);
+          if constexpr (s >= 2) fold(IC<s - 2>{});
+          pb[s & 7] = __builtin_amdgcn_exp2f(fmaf(x, a.scale_log2, -m[c]));
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     });

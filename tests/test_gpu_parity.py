@@ -606,6 +606,23 @@ def test_mala_fwd(L, Hq, Hkv, mode, tau):
         assert 0 < n_kept
 
 
+def test_mala_fwd_two_sequences_equal_one_at_a_time():
+    """B = 2 (the workspace holds each sequence's row sums and kept lists): each sequence's
+    O and LSE equal a B = 1 call on that sequence bit for bit, and the first against the
+    oracle under the decisions of its own call."""
+    L, Hq, Hkv, tau = 800, 40, 8, 0.1
+    _case(f"MALA fwd B=2 L={L} dense tau={tau} == two B=1 calls")
+    ow, win = _windows(L, Hkv, 16, 64, mode="dense")
+    q, k, v = inputs.attention_inputs(2, L, L, Hq, Hkv, 128, seed=46, device=DEV)
+    o2, l2 = api.mala_fwd(q, k, v, win, tau)
+    for bi in range(2):
+        qb, kb, vb = (t[bi:bi + 1].contiguous() for t in (q, k, v))
+        o1, l1 = api.mala_fwd(qb, kb, vb, win, tau)
+        torch.cuda.synchronize()
+        assert torch.equal(o2[bi:bi + 1], o1) and torch.equal(l2[bi:bi + 1], l1), bi
+    mala_check(q[0:1].cpu(), k[0:1].cpu(), v[0:1].cpu(), ow, win, tau)
+
+
 def test_mala_fwd_32k_dense_sampled_qblocks():
     """Full causal MALA at 32K tokens: decisions of 16 sampled q-blocks (all heads, every
     key block) and their rows' O and LSE against the oracle."""
