@@ -606,6 +606,19 @@ def test_mala_fwd(L, Hq, Hkv, mode, tau):
         assert 0 < n_kept
 
 
+def test_mala_fwd_empty_rows_and_items():
+    """near = 0 and no sink: the early rows under heads 1-3 see no key, and whole work
+    items have empty lists (no scoring sums, no kept entries): O = 0 and LSE = -inf there,
+    the rest against the oracle."""
+    L, Hq, Hkv, tau = 600, 16, 4, 0.05
+    _case(f"MALA fwd L={L} sink=0 near=0 tau={tau}: empty rows and items")
+    ow, win = _windows(L, Hkv, 0, 0)
+    q, k, v = inputs.attention_inputs(1, L, L, Hq, Hkv, 128, seed=47)
+    o, lse, n_kept, n_tiles = mala_check(q, k, v, ow, win, tau)
+    assert bool(torch.isinf(lse).any()), "some rows see no key"
+    assert 0 < n_kept < n_tiles
+
+
 def test_mala_fwd_two_sequences_equal_one_at_a_time():
     """B = 2 (the workspace holds each sequence's row sums and kept lists): each sequence's
     O and LSE equal a B = 1 call on that sequence bit for bit, and the first against the
