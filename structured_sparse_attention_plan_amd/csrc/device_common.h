@@ -169,7 +169,8 @@ struct HeadBand {
   int32_t lo, hi;
 };
 
-__device__ __forceinline__ HeadBand head_band(const DevWindow& w, int h) {
+// (host and device: the CPU test suite checks visible_run against visible)
+__host__ __device__ __forceinline__ HeadBand head_band(const DevWindow& w, int h) {
   int64_t lo = (int64_t)w.band_lo0 + (int64_t)h * w.band_step;
   int64_t hi = lo + w.band_w;
   const int64_t cap = 0x7fffffff;
@@ -177,7 +178,7 @@ __device__ __forceinline__ HeadBand head_band(const DevWindow& w, int h) {
 }
 
 // Key j (< Lk) visible to the query at key position p under a head's window.
-__device__ __forceinline__ bool visible(int p, int j, int Lk, int sink, int near_w, HeadBand b) {
+__host__ __device__ __forceinline__ bool visible(int p, int j, int Lk, int sink, int near_w, HeadBand b) {
   const int d = p - j;
   return (j < Lk) & (d >= 0) & ((j < sink) | (d < near_w) | ((d >= b.lo) & (d < b.hi)));
 }
@@ -191,7 +192,7 @@ __device__ __forceinline__ bool visible(int p, int j, int Lk, int sink, int near
 // one.  The parts in ascending order of their first key: sink [0, S1], band [B0, B1],
 // near window [N0, R] (the band lies at distances >= near, so it never starts after
 // the near window).
-__device__ __forceinline__ bool visible_run(int p, int jbase, int Lk, int sink, int near_w, HeadBand b,
+__host__ __device__ __forceinline__ bool visible_run(int p, int jbase, int Lk, int sink, int near_w, HeadBand b,
                                             int& lo, int& hi) {
   const int P = p - jbase;                            // d >= 0  <=>  jc <= P
   const int R = min(min(P, Lk - 1 - jbase), 63);      // last key the row may see
