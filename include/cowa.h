@@ -272,7 +272,8 @@ int cowa_mala_bwd(const cowa_problem* p, const cowa_plan_dev* fwd_plan, const co
  * method key point 3).
  * Each KV head reads only its visible blocks.  q/o: [B, 1, Hq, D] bf16;
  * k_cache/v_cache: [B, Lk, Hkv, D] bf16; lse: [B, Hq] fp32 or NULL.
- * Supported: dtype BF16, D = 128.  workspace: cowa_workspace_size(COWA_OP_DECODE).
+ * Supported: dtype BF16, D = 128, Hq / Hkv from 1 to 8.  workspace:
+ * cowa_workspace_size(COWA_OP_DECODE).
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, PLAN_MISMATCH, HIP. */
 int cowa_decode(const cowa_problem* p, const cowa_plan_dev* plan,
                 const void* q, const void* k_cache, const void* v_cache,

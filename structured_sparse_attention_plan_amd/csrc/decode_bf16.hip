@@ -372,14 +372,18 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t s) {
   switch (a.G) {
     case 1: return launch_g<1>(a, s);
     case 2: return launch_g<2>(a, s);
+    case 3: return launch_g<3>(a, s);
     case 4: return launch_g<4>(a, s);
     case 5: return launch_g<5>(a, s);
+    case 6: return launch_g<6>(a, s);
+    case 7: return launch_g<7>(a, s);
     case 8: return launch_g<8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-bool decode_supports_group(int G) { return G == 1 || G == 2 || G == 4 || G == 5 || G == 8; }
+// every group size up to 8 (the query rows of a KV head live in registers: G x 16 each)
+bool decode_supports_group(int G) { return G >= 1 && G <= 8; }
 
 // ---------------------------------------------------------------------- window cache append
 // Row (b, t, h) of the new tokens (position pos0[b] + t) goes to head h's slot.  Of the

@@ -76,7 +76,7 @@ def test_tile_sizes_and_workspace():
     ("fwd", dict(dtype=C.COWA_DTYPE_F32), C.COWA_ERR_UNSUPPORTED),  # f32 needs D = 64
     ("bwd", dict(dtype=C.COWA_DTYPE_F32, D=64), C.COWA_ERR_UNSUPPORTED),
     ("decode", dict(Lq=2), C.COWA_ERR_UNSUPPORTED),        # decode is one query row
-    ("decode", dict(Lq=1, Hq=24, Hkv=8), C.COWA_ERR_UNSUPPORTED),   # G = 3 not built
+    ("decode", dict(Lq=1, Hq=72, Hkv=8), C.COWA_ERR_UNSUPPORTED),   # G = 9 not built
     ("mala_bwd", dict(B=2), C.COWA_ERR_UNSUPPORTED),       # one sequence only
     ("mala_bwd", dict(dtype=C.COWA_DTYPE_F32, D=64), C.COWA_ERR_UNSUPPORTED),
     ("fwd", dict(B=0), C.COWA_ERR_INVALID_ARG),

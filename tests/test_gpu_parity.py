@@ -343,6 +343,9 @@ def test_chunked_prefill_matches_full_forward():
     (2, 2000, 8, 8, 16, 64, "complementary"),    # G = 1
     (1, 1500, 16, 8, 16, 64, "duplicated"),      # G = 2
     (2, 2500, 16, 2, 32, 128, "complementary"),  # G = 8
+    (2, 1800, 24, 8, 16, 64, "complementary"),   # G = 3
+    (1, 2100, 12, 2, 8, 50, "duplicated"),       # G = 6
+    (2, 1300, 14, 2, 16, 64, "dense"),           # G = 7
 ])
 def test_decode_small(B, Lk, Hq, Hkv, sink, near, mode):
     _case(f"decode B={B} Lk={Lk} Hq={Hq} Hkv={Hkv} sink={sink} near={near} {mode}")
