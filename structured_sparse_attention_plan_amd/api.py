@@ -42,11 +42,21 @@ def tile_sizes(op, prob):
     return bq.value, bk.value
 
 
+_WS_SIZES = {}
+
+
 def workspace_size(op, prob):
-    n = ctypes.c_size_t()
-    C.check("cowa_workspace_size", C.lib.cowa_workspace_size(OPS[op], ctypes.byref(prob),
-                                                            ctypes.byref(n)))
-    return n.value
+    """cowa_workspace_size, remembered per (op, problem): for the MALA forward the library
+    counts the visible tiles with the planner, which takes milliseconds at 32K tokens."""
+    w = prob.win
+    key = (op, prob.B, prob.Lq, prob.Lk, prob.Hq, prob.Hkv, prob.D, prob.dtype,
+           w.sink, w.near_w, w.gap, w.lr, w.band_mode)
+    if key not in _WS_SIZES:
+        n = ctypes.c_size_t()
+        C.check("cowa_workspace_size", C.lib.cowa_workspace_size(OPS[op], ctypes.byref(prob),
+                                                                ctypes.byref(n)))
+        _WS_SIZES[key] = n.value
+    return _WS_SIZES[key]
 
 
 class HostPlan:
