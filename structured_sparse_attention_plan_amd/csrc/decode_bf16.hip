@@ -50,74 +50,6 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-// Visible 64-key blocks of one query at position p of a sequence of Lb keys (Lb >= 1):
-// the prefix sink [0, sink), the near window (p - near, p] and the head's band
-// (p - hi, p - lo], each taken to blocks, sorted and merged into at most three disjoint
-// ascending runs [ba, bb) (the list the planner gives a one-row q-block).
-struct BlockRuns {
-  int ba[3], bb[3];
-  int n;      // runs
-  int total;  // blocks over all runs
-};
-__device__ __forceinline__ BlockRuns visible_block_runs(int p, int Lb, int sink, int near_w, HeadBand band) {
-  int ra[3], rb[3], n = 0;
-  if (sink > 0) {
-    ra[n] = 0;
-    rb[n] = min(sink, Lb);
-    ++n;
-  }
-  if (near_w > 0) {
-    ra[n] = max(0, p - near_w + 1);
-    rb[n] = p + 1;
-    ++n;
-  }
-  if (band.hi > band.lo && p >= band.lo) {
-    ra[n] = max(0, p - band.hi + 1);  // hi clamped to int32 max: dense bands start at 0
-    rb[n] = p - band.lo + 1;
-    ++n;
-  }
-  int ba[3], bb[3];
-  for (int k = 0; k < n; ++k) {
-    ba[k] = ra[k] / kDecBk;
-    bb[k] = (rb[k] - 1) / kDecBk + 1;
-  }
-  // sort three runs by start, then merge overlapping or adjacent ones
-  for (int x = 0; x < n; ++x)
-    for (int y = x + 1; y < n; ++y)
-      if (ba[y] < ba[x]) {
-        const int t0 = ba[x], t1 = bb[x];
-        ba[x] = ba[y];
-        bb[x] = bb[y];
-        ba[y] = t0;
-        bb[y] = t1;
-      }
-  BlockRuns r;
-  r.n = 0;
-  r.total = 0;
-  for (int k = 0; k < n; ++k) {
-    if (r.n > 0 && ba[k] <= r.bb[r.n - 1]) {
-      r.bb[r.n - 1] = max(r.bb[r.n - 1], bb[k]);
-    } else {
-      r.ba[r.n] = ba[k];
-      r.bb[r.n] = bb[k];
-      ++r.n;
-    }
-  }
-  for (int k = 0; k < r.n; ++k) r.total += r.bb[k] - r.ba[k];
-  return r;
-}
-
-// Block of run position e (0 <= e < total), runs in ascending order.
-__device__ __forceinline__ int run_block(const BlockRuns& r, int e) {
-  int kb = r.ba[0] + e;
-  if (r.n > 1 && e >= r.bb[0] - r.ba[0]) {
-    e -= r.bb[0] - r.ba[0];
-    kb = r.ba[1] + e;
-    if (r.n > 2 && e >= r.bb[1] - r.ba[1]) kb = r.ba[2] + (e - (r.bb[1] - r.ba[1]));
-  }
-  return kb;
-}
-
 // MODE: 0 full caches with the planner's row list; 1 full caches, each sequence's
 // visible blocks derived from its length (varlen); 2 window-only caches (wcache.h), blocks
 // derived from the length as in mode 1, each key read from its head's slot.
@@ -166,7 +98,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   BlockRuns runs;
   int e0, e1;
   if constexpr (VAR) {
-    runs = Lb > 0 ? visible_block_runs(p, Lb, a.win.sink, a.win.near_w, band) : BlockRuns{{0, 0, 0}, {0, 0, 0}, 0, 0};
+    runs = Lb > 0 ? visible_block_runs(p, Lb, a.win.sink, a.win.near_w, band)
+                   : BlockRuns{0, 0, 0, 0, 0, 0, 0};
     e0 = 0;
     e1 = runs.total;
   } else {

@@ -221,4 +221,71 @@ __host__ __device__ __forceinline__ bool visible_run(int p, int jbase, int Lk, i
   return one;
 }
 
+
+// Visible 64-key blocks of one query at position p of a sequence of Lb >= 1 keys, as at
+// most three disjoint ascending runs of blocks [a, b) (the list the planner gives a
+// one-row q-block): the prefix sink [0, sink), the head's band of distances [lo, hi) and
+// the near window of distances [0, near), each taken to blocks, sorted by first block and
+// merged where they overlap or touch.  Slots are fixed (an empty one has a = b = kNoRun)
+// and every index is a constant, so the runs stay in registers.
+struct BlockRuns {
+  int a0, b0, a1, b1, a2, b2;
+  int total;  // blocks over the three runs
+};
+constexpr int kNoRun = 0x3fffffff;
+
+__host__ __device__ __forceinline__ void sort_run_pair(int& a, int& b, int& c, int& d) {
+  if (c < a) {
+    const int t = a, u = b;
+    a = c;
+    b = d;
+    c = t;
+    d = u;
+  }
+}
+
+__host__ __device__ __forceinline__ BlockRuns visible_block_runs(int p, int Lb, int sink, int near_w, HeadBand band) {
+  constexpr int BK = kDecBk;
+  BlockRuns r{kNoRun, kNoRun, kNoRun, kNoRun, kNoRun, kNoRun, 0};
+  if (sink > 0) {
+    r.a0 = 0;
+    r.b0 = (min(sink, Lb) - 1) / BK + 1;
+  }
+  if (near_w > 0) {
+    r.a1 = max(0, p - near_w + 1) / BK;
+    r.b1 = p / BK + 1;
+  }
+  if (band.hi > band.lo && p >= band.lo) {
+    r.a2 = max(0, p - band.hi + 1) / BK;  // hi clamped to int32 max: dense bands start at 0
+    r.b2 = (p - band.lo) / BK + 1;
+  }
+  sort_run_pair(r.a0, r.b0, r.a1, r.b1);
+  sort_run_pair(r.a1, r.b1, r.a2, r.b2);
+  sort_run_pair(r.a0, r.b0, r.a1, r.b1);
+  // run 1 joins run 0 when it starts at or before run 0's end (both empty: nothing moves)
+  if (r.a1 <= r.b0) {
+    r.b0 = max(r.b0, r.b1);
+    r.a1 = r.b1 = kNoRun;
+  }
+  // run 2 can only meet the last non-empty run before it (runs 0 and 1 are disjoint
+  // when 1 is not empty, and 2 starts no earlier than 1)
+  if (r.a1 != kNoRun) {
+    if (r.a2 <= r.b1) {
+      r.b1 = max(r.b1, r.b2);
+      r.a2 = r.b2 = kNoRun;
+    }
+  } else if (r.a2 <= r.b0) {
+    r.b0 = max(r.b0, r.b2);
+    r.a2 = r.b2 = kNoRun;
+  }
+  r.total = (r.b0 - r.a0) + (r.b1 - r.a1) + (r.b2 - r.a2);
+  return r;
+}
+
+// Block of run position e (0 <= e < total), runs in ascending order.
+__host__ __device__ __forceinline__ int run_block(const BlockRuns& r, int e) {
+  const int n0 = r.b0 - r.a0, n1 = r.b1 - r.a1;
+  return e < n0 ? r.a0 + e : (e < n0 + n1 ? r.a1 + (e - n0) : r.a2 + (e - n0 - n1));
+}
+
 }  // namespace cowa

@@ -1,5 +1,7 @@
 """The kernels' single-run test for boundary tiles (visible_run, device_common.h) against
-the per-key window predicate, on the host: built with hipcc, run without a GPU."""
+the per-key window predicate, and the plan-free decode's block runs (visible_block_runs)
+against the blocks that hold a visible key, on the host: built with hipcc, run without a
+GPU."""
 
 import os
 import shutil
@@ -26,3 +28,4 @@ def test_visible_run_matches_the_window_predicate(tmp_path):
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "with several runs" in r.stdout
+    assert "blocks listed in order" in r.stdout
