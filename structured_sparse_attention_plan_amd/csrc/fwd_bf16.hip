@@ -654,35 +654,69 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   }
 
   // ---- finalize: l summed over the two lane halves of a column (MALA: P was normalised,
-  // O is the plain sum; scoring writes only LSE)
-  __bf16* O = (__bf16*)a.o;
+  // O is the plain sum; scoring writes only LSE).  O, and its rounding residual, leave
+  // through this wave's 64 rows of the Q tile (free once its last product has read them;
+  // an item without tiles waits here for its Q copies): each lane puts its runs of 4 dims
+  // of row n into LDS (chunk-swizzled rows), then each store writes four whole 256-byte
+  // rows (a row is one (token, head), and the G heads of a token are adjacent in O)
+  // instead of 8 bytes in each of 32 rows.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  // The lane's coordinates and rows are formed again here (from the lane count, not the
+  // work-item id) rather than carried across the tile loop, which uses every register.
+  // Item row r = token * G + head; token r / G by a multiply-shift (exact for r < 256,
+  // G <= 256).
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int n_e = lane_e & 31, h2_e = lane_e >> 5;
+  const uint32_t ginv = (65536u + (uint32_t)G - 1u) / (uint32_t)G;
+  float inv[CB];
 #pragma unroll
   for (int c = 0; c < CB; ++c) {
-    float lt = l[c] + __shfl_xor(l[c], 32);
-    const float inv = MODE == 2 ? 1.f : lt > 0.f ? 1.f / lt : 0.f;
-    if (MODE == 1 && rvalid[c] && h2 == 0)
-      a.lse[((int64_t)b * a.Hq + hq[c]) * a.Lq + tok[c]] = lt > 0.f ? (m[c] + log2f(lt)) * kLn2 : -INFINITY;
-    if (MODE != 1 && rvalid[c]) {
-      const int64_t oo = (((int64_t)b * a.Lq + tok[c]) * a.Hq + hq[c]) * D + 4 * h2;
-      __bf16* op = O + oo;
+    const float lt = l[c] + __shfl_xor(l[c], 32);
+    inv[c] = MODE == 2 ? 1.f : lt > 0.f ? 1.f / lt : 0.f;
+    const int r = wave * WROWS + c * 32 + n_e;
+    const int rt = (int)(((uint32_t)r * ginv) >> 16);
+    const int t = qb * Bq + rt;
+    if (MODE != 2 && rt < Bq && t < a.Lq && h2_e == 0)  // MALA's kept-tile pass keeps the given LSE
+      a.lse[((int64_t)b * a.Hq + h * G + (r - rt * G)) * a.Lq + t] = lt > 0.f ? (m[c] + log2f(lt)) * kLn2 : -INFINITY;
+  }
+  if constexpr (MODE != 1) {
+    __bf16* const so = sQ + wave * WROWS * D;
+    // lo = false: O / l rounded to bf16; true: what that rounding dropped, rounded to bf16
+    auto put = [&](bool lo) __attribute__((always_inline)) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int c = 0; c < CB; ++c)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float x[4];
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = acc[c][db][4 * q4 + e] * inv;
-          const bf16x4 v = to_bf16x4(x[0], x[1], x[2], x[3]);
-          *(u32x2*)(op + 32 * db + 8 * q4) = __builtin_bit_cast(u32x2, v);
-          if (a.o_lo) {  // what the bf16 rounding dropped, itself rounded to bf16
-            const bf16x4 r = to_bf16x4(x[0] - (float)v[0], x[1] - (float)v[1], x[2] - (float)v[2],
-                                       x[3] - (float)v[3]);
-            *(u32x2*)((__bf16*)a.o_lo + oo + 32 * db + 8 * q4) = __builtin_bit_cast(u32x2, r);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = acc[c][db][4 * q4 + e] * inv[c];
+            const bf16x4 v = to_bf16x4(x[0], x[1], x[2], x[3]);
+            const bf16x4 w = lo ? to_bf16x4(x[0] - (float)v[0], x[1] - (float)v[1], x[2] - (float)v[2],
+                                            x[3] - (float)v[3])
+                                : v;
+            *(u32x2*)(so + swz(c * 32 + n_e, 32 * db + 8 * q4 + 4 * h2_e)) = __builtin_bit_cast(u32x2, w);
           }
-        }
-      if (MODE == 0 && h2 == 0)
-        a.lse[((int64_t)b * a.Hq + hq[c]) * a.Lq + tok[c]] =
-            lt > 0.f ? (m[c] + log2f(lt)) * kLn2 : -INFINITY;
+    };
+    // copy u: lane L sends logical chunk L % 16 of local row 4 u + L / 16
+    auto drain = [&](__bf16* dst) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < WROWS / 4; ++u) {
+        const int rl = 4 * u + (lane_e >> 4), ch = lane_e & 15;
+        const u32x4 w = *(const u32x4*)(so + rl * D + 8 * (ch ^ sw(rl)));
+        const int r = wave * WROWS + rl;
+        const int rt = (int)(((uint32_t)r * ginv) >> 16);
+        const int t = qb * Bq + rt;
+        if (rt < Bq && t < a.Lq)
+          *(u32x4*)(dst + (((int64_t)b * a.Lq + t) * a.Hq + h * G + (r - rt * G)) * D + 8 * ch) = w;
+      }
+    };
+    put(false);
+    drain((__bf16*)a.o);
+    if (a.o_lo) {
+      put(true);
+      drain((__bf16*)a.o_lo);
     }
   }
 }
