@@ -341,8 +341,9 @@ int cowa_wcache_append(const cowa_wcache* c, const void* k_new, const void* v_ne
  * read from its head's slot; the same blocks in the same order, so the result equals
  * cowa_decode_varlen's over full caches holding the same rows, bit for bit.  p->Lk must
  * be c->Lmax, and p's B, Hkv, D and window those of c.  workspace:
- * cowa_workspace_size(COWA_OP_DECODE, p).  Errors: INVALID_ARG, UNSUPPORTED,
- * WORKSPACE_TOO_SMALL, HIP. */
+ * cowa_workspace_size(COWA_OP_DECODE, p).  Errors: INVALID_ARG, UNSUPPORTED (also when a
+ * head holds more than (2^31 - 1) / (2 D) slots: 8388607 at D = 128, the kernel's 32-bit
+ * offsets), WORKSPACE_TOO_SMALL, HIP. */
 int cowa_wcache_decode(const cowa_problem* p, const cowa_wcache* c, const void* q,
                        const int32_t* seqlens, void* o, float* lse, void* workspace,
                        size_t workspace_bytes, void* stream);

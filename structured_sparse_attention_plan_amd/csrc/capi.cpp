@@ -554,6 +554,11 @@ extern "C" int cowa_wcache_decode(const cowa_problem* p, const cowa_wcache* c, c
   if (c->B != p->B || c->Hkv != p->Hkv || c->D != p->D || c->Lmax != p->Lk || !same_window(c->win, p->win))
     return COWA_ERR_INVALID_ARG;
   if (!q || !seqlens || !o) return COWA_ERR_INVALID_ARG;
+  // the kernel addresses one head's slots with 32-bit byte offsets
+  for (int h = 0; h < c->Hkv; ++h) {
+    const WinRing r = wcache_ring(c->win, h, c->Lmax);
+    if ((r.sink_slots + r.ring) * c->D * 2 > 0x7fffffff) return COWA_ERR_UNSUPPORTED;
+  }
   size_t need = 0;
   cowa_workspace_size(COWA_OP_DECODE, p, &need);
   if (!workspace || workspace_bytes < need) return COWA_ERR_WORKSPACE_TOO_SMALL;

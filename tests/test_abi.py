@@ -168,6 +168,13 @@ def test_entry_points_validate_before_launch():
     p2 = _prob(Lq=2, Lk=4096, win=api.make_window(4096, 8, 4, 16))
     assert C.lib.cowa_decode_varlen(ctypes.byref(p2), x, x, x, x, x, None, x, 1 << 30,
                                     None) == C.COWA_ERR_UNSUPPORTED
+    # window-only caches: a head whose slots pass 2^31 bytes (dense: every position kept)
+    for Lmax, status in ((1 << 23, C.COWA_ERR_UNSUPPORTED), ((1 << 23) - 1, C.COWA_ERR_WORKSPACE_TOO_SMALL)):
+        wd = api.window(4, 16, 0, 0, "dense")
+        pw = _prob(Lq=1, Lk=Lmax, win=wd)
+        cw = C.cowa_wcache(1, pw.Hkv, 128, Lmax, wd, x, x)
+        assert C.lib.cowa_wcache_decode(ctypes.byref(pw), ctypes.byref(cw), x, x, x, None, x, 8,
+                                        None) == status
 
 
 def test_python_layer_rejects_host_and_misshapen_tensors():
