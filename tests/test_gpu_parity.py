@@ -55,6 +55,8 @@ def test_fwd_f32_config1():
     (1, 400, 250, 4, 2, 8, 40, "complementary"),    # Lq > Lk: the first 150 rows see nothing
     (1, 333, 333, 4, 2, 0, 0, "complementary"),     # near = 0, no sink: empty rows
     (1, 517, 517, 4, 2, 5, 20, "dense"),
+    (1, 450, 450, 6, 2, 16, 64, "complementary"),   # G = 3: 24 of the 32 product columns
+    (2, 129, 129, 2, 2, 1, 1, "complementary"),     # G = 1, one key per row besides the sink
 ])
 def test_fwd_f32_small(B, Lq, Lk, Hq, Hkv, sink, near, mode):
     _case(f"fwd f32 B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} sink={sink} near={near} {mode}")
