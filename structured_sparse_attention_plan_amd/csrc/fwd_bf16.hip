@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int j = j0 + 32 * k2 + 8 * (i >> 2) + (i & 3);
-          const bool vis = rvalid[c] & visible(p, j, a.Lk, a.win.sink, a.win.near_w, band);
+          const bool vis = !rvalid[c] | visible(p, j, a.Lk, a.win.sink, a.win.near_w, band);
           const float x = (v[k2][c][i]);
           v[k2][c][i] = (vis ? x : -INFINITY);
         }
@@ -312,29 +312,40 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
 
   // Boundary tile, both row blocks: where every row of the wave sees its visible keys
   // of the tile as one run (visible_run), each element is tested against the row's run
-  // (three VALU operations); otherwise, with the window predicate per element.
+  // (three VALU operations), and nothing is done when every row sees the whole tile;
+  // otherwise, with the window predicate per element.  Rows without a token (past Lq in
+  // the last q-block, which makes every tile of that q-block a boundary tile) see every
+  // key: their results are never stored, and masking them entirely would leave their
+  // column sums at 0 and send every one of those tiles through the reference move.
   auto mask_tile = [&](f32x16 (&v)[KB2][CB], int ent) __attribute__((always_inline)) {
     if (ent & 1) {
       int rlo[CB], rhi[CB];
-      bool one = true;
+      bool one = true, whole = true;
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
-        one &= visible_run(tok[c] + off, (ent >> 1) * BK + 4 * h2, a.Lk, a.win.sink, a.win.near_w,
-                           band, rlo[c], rhi[c]);
-        if (!rvalid[c]) rlo[c] = 64;
+        const bool oc = visible_run(tok[c] + off, (ent >> 1) * BK + 4 * h2, a.Lk, a.win.sink,
+                                    a.win.near_w, band, rlo[c], rhi[c]);
+        if (!rvalid[c]) {
+          rlo[c] = 0;
+          rhi[c] = BK - 1;
+        }
+        one &= oc | !rvalid[c];
+        whole &= (rlo[c] == 0) & (rhi[c] >= BK - 5);  // the lane's keys: offsets 0 .. 59
       }
       if (__builtin_amdgcn_ballot_w64(!one) == 0) {
+        if (__builtin_amdgcn_ballot_w64(!whole) != 0) {
 #pragma unroll
-        for (int c = 0; c < CB; ++c)
+          for (int c = 0; c < CB; ++c)
 #pragma unroll
-          for (int k2 = 0; k2 < KB2; ++k2)
+            for (int k2 = 0; k2 < KB2; ++k2)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              // key of element i of key block k2, less the lane's offset 4 h2
-              const int jc = 32 * k2 + 8 * (i >> 2) + (i & 3);
-              const float x = v[k2][c][i];
-              v[k2][c][i] = ((jc >= rlo[c]) & (jc <= rhi[c])) ? x : -INFINITY;
-            }
+              for (int i = 0; i < 16; ++i) {
+                // key of element i of key block k2, less the lane's offset 4 h2
+                const int jc = 32 * k2 + 8 * (i >> 2) + (i & 3);
+                const float x = v[k2][c][i];
+                v[k2][c][i] = ((jc >= rlo[c]) & (jc <= rhi[c])) ? x : -INFINITY;
+              }
+        }
       } else {
         mask_rows(v, 0, ent);
         mask_rows(v, 1, ent);
