@@ -288,67 +288,52 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     return join(lds_read_tr4(at(vt, a0 + rows)), lds_read_tr4(at(vt, (a0 ^ 32u) + 2048u + rows)));
   };
 
-  // Boundary tile: window predicate on one row block (32 columns c) of S, in place in
-  // its accumulators; element i of key block k2 is key 32 k2 + 8 (i / 4) + 4 h2 + i % 4
-  // of the tile.
-  auto mask_rows = [&](f32x16 (&v)[KB2][CB], int c, int ent) __attribute__((always_inline)) {
-    if (ent & 1) {
-      const int kb = ent >> 1;
-      const int p = tok[c] + off;
-      // taken here, so that the key indices are formed on this (rare) path only
-      int j0 = kb * BK + 4 * h2;
-      asm volatile("" : "+v"(j0));
-#pragma unroll
-      for (int k2 = 0; k2 < KB2; ++k2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = j0 + 32 * k2 + 8 * (i >> 2) + (i & 3);
-          const bool vis = !rvalid[c] | visible(p, j, a.Lk, a.win.sink, a.win.near_w, band);
-          const float x = (v[k2][c][i]);
-          v[k2][c][i] = (vis ? x : -INFINITY);
-        }
-    }
-  };
-
-  // Boundary tile, both row blocks: where every row of the wave sees its visible keys
-  // of the tile as one run (visible_run), each element is tested against the row's run
-  // (three VALU operations), and nothing is done when every row sees the whole tile;
-  // otherwise, with the window predicate per element.  Rows without a token (past Lq in
-  // the last q-block, which makes every tile of that q-block a boundary tile) see every
-  // key: their results are never stored, and masking them entirely would leave their
-  // column sums at 0 and send every one of those tiles through the reference move.
+  // Boundary tile, both row blocks: each row's visible keys of the tile as a 64-bit mask
+  // over the key offsets jc (key (ent >> 1) BK + 4 h2 + jc; the lane's 32 elements sit at
+  // the offsets of kLaneKeys), from the row's single run where its visible keys form one
+  // (visible_run, almost every boundary tile of the CoWA windows), else from the window
+  // predicate key by key in a loop (narrow windows or gaps); then one select per element,
+  // skipped when every row sees the whole tile.  One copy of the select code serves both
+  // cases, which keeps the kernel's code small enough for the instruction cache.  Rows
+  // without a token (past Lq in the last q-block, which makes every tile of that q-block a
+  // boundary tile) see every key: their results are never stored, and masking them
+  // entirely would leave their column sums at 0 and send every one of those tiles through
+  // the reference move.
+  constexpr uint64_t kLaneKeys = 0x0F0F0F0F0F0F0F0Full;  // jc = 32 k2 + 8 (i / 4) + i % 4
   auto mask_tile = [&](f32x16 (&v)[KB2][CB], int ent) __attribute__((always_inline)) {
     if (ent & 1) {
-      int rlo[CB], rhi[CB];
-      bool one = true, whole = true;
+      const int jbase = (ent >> 1) * BK + 4 * h2;
+      uint64_t bits[CB];
+      bool whole = true;
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
-        const bool oc = visible_run(tok[c] + off, (ent >> 1) * BK + 4 * h2, a.Lk, a.win.sink,
-                                    a.win.near_w, band, rlo[c], rhi[c]);
+        int lo, hi;
+        const int p = tok[c] + off;
+        const bool one = visible_run(p, jbase, a.Lk, a.win.sink, a.win.near_w, band, lo, hi);
         if (!rvalid[c]) {
-          rlo[c] = 0;
-          rhi[c] = BK - 1;
+          bits[c] = ~0ull;
+        } else if (one) {  // keys lo .. hi (none when lo > hi)
+          bits[c] = lo > hi ? 0ull : ((hi >= 63 ? ~0ull : (2ull << hi) - 1ull) & ~((1ull << lo) - 1ull));
+        } else {
+          uint64_t m = 0;
+#pragma unroll 1
+          for (int jc = 0; jc < BK - 4; ++jc)
+            m |= (uint64_t)visible(p, jbase + jc, a.Lk, a.win.sink, a.win.near_w, band) << jc;
+          bits[c] = m;
         }
-        one &= oc | !rvalid[c];
-        whole &= (rlo[c] == 0) & (rhi[c] >= BK - 5);  // the lane's keys: offsets 0 .. 59
+        whole &= (bits[c] & kLaneKeys) == kLaneKeys;
       }
-      if (__builtin_amdgcn_ballot_w64(!one) == 0) {
-        if (__builtin_amdgcn_ballot_w64(!whole) != 0) {
+      if (__builtin_amdgcn_ballot_w64(!whole) != 0) {
 #pragma unroll
-          for (int c = 0; c < CB; ++c)
+        for (int c = 0; c < CB; ++c)
 #pragma unroll
-            for (int k2 = 0; k2 < KB2; ++k2)
+          for (int k2 = 0; k2 < KB2; ++k2)
 #pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                // key of element i of key block k2, less the lane's offset 4 h2
-                const int jc = 32 * k2 + 8 * (i >> 2) + (i & 3);
-                const float x = v[k2][c][i];
-                v[k2][c][i] = ((jc >= rlo[c]) & (jc <= rhi[c])) ? x : -INFINITY;
-              }
-        }
-      } else {
-        mask_rows(v, 0, ent);
-        mask_rows(v, 1, ent);
+            for (int i = 0; i < 16; ++i) {
+              const int jc = 32 * k2 + 8 * (i >> 2) + (i & 3);
+              const float x = v[k2][c][i];
+              v[k2][c][i] = ((bits[c] >> jc) & 1ull) ? x : -INFINITY;
+            }
       }
     }
   };
