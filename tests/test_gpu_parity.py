@@ -229,6 +229,38 @@ def test_bwd_bf16_group_sizes_and_empty_rows(B, Lq, Lk, Hq, Hkv, sink, near):
     assert_bf16_close("dV", dv, rv, gradient=True)
 
 
+@pytest.mark.parametrize("Lq,Lk", [(1, 1), (1, 70), (3, 3), (2, 65), (65, 65)])
+def test_tiny_sizes(Lq, Lk):
+    """Degenerate sizes: one query and one key, a single query over a tile and a bit, keys
+    one past a tile; forward and backward in bf16, the fp32 forward, and the decode of the
+    last key position."""
+    _case(f"tiny Lq={Lq} Lk={Lk}")
+    Hq, Hkv = 8, 2
+    ow, win = _windows(Lk, Hkv, 4, 16)
+    q, k, v, do = inputs.attention_inputs(1, Lq, Lk, Hq, Hkv, 128, seed=21, with_dout=True)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse, dq, dk, dv = api.fwd_bwd(qd, kd, vd, dod, win)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.attn_fwd(q, k, v, ow, 128 ** -0.5)
+    assert_bf16_close("O", o, Oo)
+    assert_bf16_close("LSE", lse, Lo)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, do, ow, 128 ** -0.5)
+    assert_bf16_close("dQ", dq, rq, gradient=True)
+    assert_bf16_close("dK", dk, rk, gradient=True)
+    assert_bf16_close("dV", dv, rv, gradient=True)
+    qf, kf, vf = inputs.attention_inputs(1, Lq, Lk, Hq, Hkv, 64, dtype=torch.float32, seed=22)
+    of, lf = api.fwd(qf.to(DEV), kf.to(DEV), vf.to(DEV), win, scale=1 / 8)
+    torch.cuda.synchronize()
+    Of, Lf = oracle.attn_fwd(qf, kf, vf, ow, 1 / 8)
+    assert errors(of, Of)[0] <= F32_MAX_ABS and errors(lf, Lf)[0] <= F32_MAX_ABS
+    qd1, kc, vc = inputs.attention_inputs(2, 1, Lk, Hq, Hkv, 128, seed=23)
+    od, ld = api.decode(qd1.to(DEV), kc.to(DEV), vc.to(DEV), win)
+    torch.cuda.synchronize()
+    Od, Ld = oracle.decode(qd1, kc, vc, ow, 128 ** -0.5)
+    assert_bf16_close("decode O", od, Od)
+    assert_bf16_close("decode LSE", ld, Ld[:, :, 0])
+
+
 @pytest.mark.parametrize("do_exp,v_exp", [(12, 0), (-24, 0), (0, 6), (8, 5)])
 def test_bwd_bf16_gradient_ranges(do_exp, v_exp):
     """dO multiplied by 2^do_exp (a loss-scaled or a tiny upstream gradient) and V by
