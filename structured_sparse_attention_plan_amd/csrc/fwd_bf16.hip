@@ -534,41 +534,49 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
 
     if constexpr (MODE == 2) return;  // P normalised by the given LSE: no reference to move
 
-    // reference check on the column sums (both lane halves)
+    // reference check on the column sums (both lane halves).  A column's sum exceeds
+    // 2^32 only if one of its halves exceeds 2^31, and its l is 0 only if both halves'
+    // are, so when every lane passes the test on its own half no column can fail the
+    // exact test, and the exact test (two lane swaps per row block) is skipped.
     float alpha[CB] = {1.f, 1.f};
-    bool redo[CB];
+    bool near_edge = false;
 #pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const float cs = sum[c] + swap_halves(sum[c]);
-      const float cl = l[c] + swap_halves(l[c]);
-      redo[c] = (cs > kSumHi) | ((cl == 0.f) & (cs < kSumLo));
-    }
-    if (__builtin_amdgcn_ballot_w64(redo[0] | redo[1]) != 0) {
-      // rare: the tile's column max becomes the reference of the columns that need one
+    for (int c = 0; c < CB; ++c) near_edge |= (sum[c] > 0.5f * kSumHi) | ((l[c] == 0.f) & (sum[c] < kSumLo));
+    if (__builtin_amdgcn_ballot_w64(near_edge) != 0) {
+      bool redo[CB];
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int k2 = 0; k2 < KB2; ++k2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, (sc[k2][c][i]));
-        const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        const float mt = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * a.scale_log2;
-        const bool mv = redo[c] & (mt > -INFINITY);
-        alpha[c] = mv ? __builtin_amdgcn_exp2f(m[c] - mt) : 1.f;
-        m[c] = mv ? mt : m[c];
-        if (__builtin_amdgcn_ballot_w64(mv) != 0) {
-          const float s2 = softmax_rows(sc, pfc, c, m[c]);
-          sum[c] = mv ? s2 : sum[c];
-        }
+        const float cs = sum[c] + swap_halves(sum[c]);
+        const float cl = l[c] + swap_halves(l[c]);
+        redo[c] = (cs > kSumHi) | ((cl == 0.f) & (cs < kSumLo));
       }
-      // O holds tiles up to t-1 in the previous references: take it to the new ones
+      if (__builtin_amdgcn_ballot_w64(redo[0] | redo[1]) != 0) {
+        // rare: the tile's column max becomes the reference of the columns that need one
 #pragma unroll
-      for (int c = 0; c < CB; ++c)
+        for (int c = 0; c < CB; ++c) {
+          float mx = -INFINITY;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+          for (int k2 = 0; k2 < KB2; ++k2)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[c][db][i] = agpr_scale(acc[c][db][i], alpha[c]);
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, (sc[k2][c][i]));
+          const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          const float mt = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * a.scale_log2;
+          const bool mv = redo[c] & (mt > -INFINITY);
+          alpha[c] = mv ? __builtin_amdgcn_exp2f(m[c] - mt) : 1.f;
+          m[c] = mv ? mt : m[c];
+          if (__builtin_amdgcn_ballot_w64(mv) != 0) {
+            const float s2 = softmax_rows(sc, pfc, c, m[c]);
+            sum[c] = mv ? s2 : sum[c];
+          }
+        }
+        // O holds tiles up to t-1 in the previous references: take it to the new ones
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[c][db][i] = agpr_scale(acc[c][db][i], alpha[c]);
+      }
     }
 #pragma unroll
     for (int c = 0; c < CB; ++c) l[c] = l[c] * alpha[c] + sum[c];  // fp32 row sums set LSE
