@@ -104,6 +104,13 @@ __device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x
 __device__ __forceinline__ void mfma_v0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
+// the same with the B operand in AGPRs (the Q^T fragments, resident for the whole item)
+__device__ __forceinline__ void mfma_va(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_va0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
 
 
 // MODE 0: the CoWA forward.  MODE 1: scoring only (no PV): LSE over every visible key,
@@ -262,20 +269,30 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     return (const __bf16*)((const char*)base + byte_ofs);
   };
 
+  // The Q^T operands of this wave's rows (B operands of every S product), read once from
+  // the Q tile after its copies land and kept in AGPRs: the products then read only K
+  // from LDS.
+  bf16x8 qa[CB][D / 16];
+  auto load_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int dd = 0; dd < D / 16; ++dd) {
+        qa[c][dd] = load16(at(sQ, (qofs0 ^ (dd << 5)) + 8192 * c));
+        asm volatile("" : "+a"(qa[c][dd]));
+      }
+  };
   auto scores = [&](f32x16 (&s)[KB2][CB]) __attribute__((always_inline)) {  // S of tile 0
     const __bf16* kt = sK0;
 #pragma unroll
     for (int dd = 0; dd < D / 16; ++dd) {
-      bf16x8 qf[CB];
-#pragma unroll
-      for (int c = 0; c < CB; ++c) qf[c] = load16(at(sQ, (qofs0 ^ (dd << 5)) + 8192 * c));
 #pragma unroll
       for (int k2 = 0; k2 < KB2; ++k2) {
         const bf16x8 kf = load16(at(kt, (kofs0 ^ (dd << 5)) + 8192 * k2));
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
-          if (dd == 0) mfma_v0(s[k2][c], kf, qf[c]);
-          else mfma_v(s[k2][c], kf, qf[c]);
+          if (dd == 0) mfma_va0(s[k2][c], kf, qa[c][dd]);
+          else mfma_va(s[k2][c], kf, qa[c][dd]);
         }
       }
     }
@@ -418,17 +435,15 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     ent1 = ent2;
     ent2 = ent3;
 
-    // S(t+1) operands by step dd (four MFMAs, (k2, c)): the K rows of both key blocks and
-    // the Q^T columns of both row blocks at dd; step dd + 1 is read during step dd
-    uint32_t kofs = kofs0, qofs = qofs0, vofs = vofs0;
-    asm volatile("" : "+v"(kofs), "+v"(qofs), "+v"(vofs));
-    bf16x8 kq[2][4];
-    auto load_step = [&](int dd, bf16x8 (&dst)[4]) __attribute__((always_inline)) {
-      const uint32_t ka = kofs ^ (uint32_t)(dd << 5), qa = qofs ^ (uint32_t)(dd << 5);
+    // S(t+1) operands by step dd (four MFMAs, (k2, c)): the K rows of both key blocks at
+    // dd (the Q^T columns are resident); step dd + 1 is read during step dd
+    uint32_t kofs = kofs0, vofs = vofs0;
+    asm volatile("" : "+v"(kofs), "+v"(vofs));
+    bf16x8 kq[2][2];
+    auto load_step = [&](int dd, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
+      const uint32_t ka = kofs ^ (uint32_t)(dd << 5);
       dst[0] = load16(at(kt, ka));
       dst[1] = load16(at(kt, ka + 8192u));
-      dst[2] = load16(at(sQ, qa));
-      dst[3] = load16(at(sQ, qa + 8192u));
     };
     load_step(0, kq[0]);
     bf16x8 vf[3];
@@ -473,8 +488,8 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
         constexpr int k = s >> 1, dd = k >> 2, k2 = (k >> 1) & 1, c = k & 1;
         if constexpr ((k & 3) == 0 && dd + 1 < D / 16) load_step(dd + 1, kq[(dd + 1) & 1]);
         // the first product of an accumulator (dd = 0) starts from zero
-        if constexpr (dd == 0) mfma_v0(sn[k2][c], kq[dd & 1][k2], kq[dd & 1][2 + c]);
-        else mfma_v(sn[k2][c], kq[dd & 1][k2], kq[dd & 1][2 + c]);
+        if constexpr (dd == 0) mfma_va0(sn[k2][c], kq[dd & 1][k2], qa[c][dd]);
+        else mfma_va(sn[k2][c], kq[dd & 1][k2], qa[c][dd]);
       } else if constexpr (PV) {
         // MFMA k = s / 2 covers operand group g = k / 2 ((k2, hf) = g / 4, db = g % 4)
         // and row block c = k % 2; the V^T operand of group g + 2 is read at the first
@@ -631,6 +646,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     // column's top key, so a column that sees one key reproduces its V row), or 0 for a
     // column with no visible key in tile 0.  MALA: the reference is the given LSE (P
     // exactly normalised; +inf for rows without a token or a visible key: P = 0)
+    load_q();
     scores(sx[0]);
     mask_tile(sx[0], ent0);
 #pragma unroll
