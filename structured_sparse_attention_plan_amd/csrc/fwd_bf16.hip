@@ -121,14 +121,16 @@ __device__ __forceinline__ void mfma_va0(f32x16& acc, const bf16x8& a, const bf1
 // exactly normalised, O = sum of the kept P V (no division), LSE left as it is.
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) __bf16 sQ[ROWS * D];
   // K and V double buffers, one array per buffer: the tile parity is known at compile
   // time in each of the two unrolled iterations, so every read names the array it reads
-  // and the compiler can tell it from the copies in flight into the other one.
-  __shared__ __attribute__((aligned(1024))) __bf16 sK0[TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sK1[TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV0[TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV1[TILE];
+  // and the compiler can tell it from the copies in flight into the other one.  They
+  // come first in LDS, so that every operand address of the loop is a per-lane base plus
+  // an offset that fits the 16-bit offset field of the LDS reads.
+  __shared__ __attribute__((aligned(16384))) __bf16 sK0[TILE];
+  __shared__ __attribute__((aligned(16384))) __bf16 sK1[TILE];
+  __shared__ __attribute__((aligned(16384))) __bf16 sV0[TILE];
+  __shared__ __attribute__((aligned(16384))) __bf16 sV1[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ[ROWS * D];
   auto kbuf = [&](auto c) __attribute__((always_inline)) -> __bf16* {
     if constexpr ((decltype(c)::value & 1) == 0) return sK0;
     else return sK1;
@@ -252,13 +254,11 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   const int32_t* const ents = MODE == 2 ? a.mala_ents + (int64_t)b * a.mala_nnz : a.row_ent;
   // LDS addressing.  With the chunk swizzle, the operand addresses of one lane differ
   // only by an XOR of the chunk bits, so each is one XOR away from a per-lane base:
-  //   K / Q rows n of a tile at dd: kofs ^ (dd << 5) bytes (+ 8192 for key / row block 1);
+  //   K / Q rows n of a tile at dd: kofs0 ^ (dd << 5) bytes (+ 8192 for key / row block 1);
   //   V^T operand (k2, hf, db), first and second run of 4 rows:
-  //     vofs ^ (db << 6) and (vofs ^ (db << 6) ^ 32) + 2048, + 4096 (2 k2 + hf) bytes,
+  //     vofs0 ^ (db << 6) and (vofs0 ^ (db << 6) ^ 32) + 2048, + 4096 (2 k2 + hf) bytes,
   // where 16-lane group gg covers d columns 16 (gg & 1) .. +15 of a 32-column block and
-  // key run 4 (gg >> 1) (+8).  The bases are re-taken at the top of every iteration
-  // (pin), so the compiler forms the few addresses of the iteration there instead of
-  // keeping one register per address and buffer alive across the whole loop.
+  // key run 4 (gg >> 1) (+8).
   const int gg = lane >> 4, j16 = lane & 15;
   const int vrow = 4 * (gg >> 1) + (j16 >> 2);
   const int vcol = 16 * (gg & 1) + 4 * (j16 & 3);
@@ -298,11 +298,23 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     }
   };
 
-  // tr-read of the V^T operand for (k2, hf, db) from a V tile at lane base vofs
-  auto vfrag = [&](const __bf16* vt, uint32_t vofs, int k2, int hf, int db) __attribute__((always_inline)) {
-    const uint32_t a0 = vofs ^ (uint32_t)(db << 6);
+  // Loop-invariant operand bases: kb[dd] for the K rows at step dd, vb[db][0 / 1] for the
+  // first and second run of 4 rows of the V^T operand at column block db.  The loop
+  // re-takes (pins) them at the top of every iteration, so each read is one of these
+  // registers plus an immediate offset (key block, row group, buffer) and the loop does
+  // no address arithmetic.
+  uint32_t kb[D / 16], vb[4][2];
+#pragma unroll
+  for (int dd = 0; dd < D / 16; ++dd) kb[dd] = kofs0 ^ (uint32_t)(dd << 5);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    vb[db][0] = vofs0 ^ (uint32_t)(db << 6);
+    vb[db][1] = (vb[db][0] ^ 32u) + 2048u;
+  }
+  // tr-read of the V^T operand for (k2, hf, db) from a V tile
+  auto vfrag = [&](const __bf16* vt, int k2, int hf, int db) __attribute__((always_inline)) {
     const uint32_t rows = 4096u * (uint32_t)(2 * k2 + hf);
-    return join(lds_read_tr4(at(vt, a0 + rows)), lds_read_tr4(at(vt, (a0 ^ 32u) + 2048u + rows)));
+    return join(lds_read_tr4(at(vt, vb[db][0] + rows)), lds_read_tr4(at(vt, vb[db][1] + rows)));
   };
 
   // Boundary tile, both row blocks: each row's visible keys of the tile as a 64-bit mask
@@ -437,19 +449,20 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
 
     // S(t+1) operands by step dd (four MFMAs, (k2, c)): the K rows of both key blocks at
     // dd (the Q^T columns are resident); step dd + 1 is read during step dd
-    uint32_t kofs = kofs0, vofs = vofs0;
-    asm volatile("" : "+v"(kofs), "+v"(vofs));
+#pragma unroll
+    for (int dd = 0; dd < D / 16; ++dd) asm volatile("" : "+v"(kb[dd]));
+#pragma unroll
+    for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(vb[db][0]), "+v"(vb[db][1]));
     bf16x8 kq[2][2];
     auto load_step = [&](int dd, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
-      const uint32_t ka = kofs ^ (uint32_t)(dd << 5);
-      dst[0] = load16(at(kt, ka));
-      dst[1] = load16(at(kt, ka + 8192u));
+      dst[0] = load16(at(kt, kb[dd]));
+      dst[1] = load16(at(kt, kb[dd] + 8192u));
     };
     load_step(0, kq[0]);
     bf16x8 vf[3];
     if constexpr (MODE == 0) {
-      vf[0] = vfrag(vt, vofs, 0, 0, 0);
-      vf[1] = vfrag(vt, vofs, 0, 0, 1);
+      vf[0] = vfrag(vt, 0, 0, 0);
+      vf[1] = vfrag(vt, 0, 0, 1);
     }
     mask_tile(sc, ent_t);
 
@@ -473,8 +486,8 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     auto slots = [&](auto pvc) __attribute__((always_inline)) {
     constexpr bool PV = decltype(pvc)::value != 0;
     if constexpr (PV && MODE == 2) {
-      vf[0] = vfrag(vt, vofs, 0, 0, 0);
-      vf[1] = vfrag(vt, vofs, 0, 0, 1);
+      vf[0] = vfrag(vt, 0, 0, 0);
+      vf[1] = vfrag(vt, 0, 0, 1);
     }
     float xin = (sc[0][0][0]);
     float xin1 = MODE == 1 ? (sc[0][0][1]) : 0.f;  // scoring: the second element of a slot
@@ -498,7 +511,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
         constexpr int k2 = g >> 3, hf = (g >> 2) & 1, db = g & 3;
         if constexpr (c == 0 && g + 2 < 16) {
           constexpr int g2 = g + 2;
-          vf[g2 % 3] = vfrag(vt, vofs, g2 >> 3, (g2 >> 2) & 1, g2 & 3);
+          vf[g2 % 3] = vfrag(vt, g2 >> 3, (g2 >> 2) & 1, g2 & 3);
         }
         acc[c][db] = mfma32x32x16(vf[g % 3], pfp[k2][c][hf], acc[c][db]);
       }
@@ -614,7 +627,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     const __bf16* const vt = vbuf(IC<PAR>{});
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
-      const bf16x8 vf = vfrag(vt, vofs0, g >> 3, (g >> 2) & 1, g & 3);
+      const bf16x8 vf = vfrag(vt, g >> 3, (g >> 2) & 1, g & 3);
 #pragma unroll
       for (int c = 0; c < CB; ++c) acc[c][g & 3] = mfma32x32x16(vf, pf[PAR][g >> 3][c][(g >> 2) & 1], acc[c][g & 3]);
     }
