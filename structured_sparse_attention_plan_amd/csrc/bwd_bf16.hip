@@ -397,14 +397,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       const float fqt = MALA ? (flag_cur ? fq : 0.f) : fq;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
+        // the K and V operands are read two steps ahead of their products (a ring of
+        // three), in an order the fences hold: read just before its product, each one
+        // would wait for the LDS latency with the matrix core idle
         f32x16 sv, dv;
-        mfma_f16_va0(sv, load16(kt + ofs_a(k2, 0)), qf[0]);
-        mfma_bf16_va0(dv, load16(vt + ofs_a(k2, 0)), df[0]);
+        bf16x8 ka[3], va[3];
 #pragma unroll
-        for (int dd = 1; dd < 8; ++dd) {
-          mfma_f16_va(sv, load16(kt + ofs_a(k2, dd)), qf[dd]);
-          mfma_bf16_va(dv, load16(vt + ofs_a(k2, dd)), df[dd]);
+        for (int dd = 0; dd < 2; ++dd) {
+          ka[dd] = load16(kt + ofs_a(k2, dd));
+          va[dd] = load16(vt + ofs_a(k2, dd));
         }
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (dd + 2 < 8) {
+            ka[(dd + 2) % 3] = load16(kt + ofs_a(k2, dd + 2));
+            va[(dd + 2) % 3] = load16(vt + ofs_a(k2, dd + 2));
+          }
+          if (dd == 0) {
+            mfma_f16_va0(sv, ka[0], qf[0]);
+            mfma_bf16_va0(dv, va[0], df[0]);
+          } else {
+            mfma_f16_va(sv, ka[dd % 3], qf[dd]);
+            mfma_bf16_va(dv, va[dd % 3], df[dd]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
         if (partial) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
