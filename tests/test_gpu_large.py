@@ -199,22 +199,30 @@ def test_fwd_bwd_128k_sampled_rows_and_identities(run_128k):
     assert_bf16_close("dQ", r["dq"][:, idx], dqo, gradient=True)
 
 
-@pytest.mark.parametrize("cluster", ["near_end", "band3_edge"])
+@pytest.mark.parametrize("cluster", ["near_end", "band3_edge", "band456_edges", "band7_edge",
+                                     "sink"])
 def test_bwd_128k_key_columns(run_128k, cluster):
     """dK/dV on key columns of the 131072-token backward, element by element.
     near_end: the last keys, the last k-block edges, the near edge and the column at
     distance near from the last row (band 0's first distance): about 4096 rows see them.
-    band3_edge: columns whose last row sits at the lower edge of KV head 3's band
-    (L - 1 - (near + 3 lr) and neighbours), seen through the bands of heads 0-2 in full
-    (about 20000 rows each) and the near window.  The band edges of heads 4-7 (and the
-    prefix sink) are seen by many more rows, whose softmax the host would need over 20000
-    keys each; they are compared at 32K (test_bwd_32k_key_columns_and_rows)."""
+    band<h>_edge(s): columns whose last row sits at the lower edge of KV head h's band
+    (L - 1 - (near + h lr)) and their neighbours, seen through the near window (all 40
+    query heads) and, for the 5 query heads of each KV head below h, through that head's
+    whole band (15872 rows): 0.4 to 0.7 million (row, head) pairs, each needing its
+    softmax over about 20000 keys.
+    sink: the prefix sink's first and last columns and the first two past it; every row
+    and head sees the sink (5.2 million pairs)."""
     r = run_128k
     L, near, ow = r["L"], r["near"], r["ow"]
     if cluster == "near_end":
         cols = [L - 1 - near - 1, L - 1 - near, L - near, L - 129, L - 128, L - 65, L - 64, L - 2, L - 1]
+    elif cluster == "sink":
+        cols = [0, 1, r["sink"] - 1, r["sink"], r["sink"] + 1]
+    elif cluster == "band456_edges":
+        cols = sorted(L - 1 - (near + hb * ow.lr) + e for hb in (4, 5, 6) for e in (0, 1))
     else:
-        j = L - 1 - (near + 3 * ow.lr)
+        hb = 3 if cluster == "band3_edge" else 7
+        j = L - 1 - (near + hb * ow.lr)
         cols = [j - 1, j, j + 1]
     _case(f"bwd 128K dK/dV key columns ({cluster}): {cols}")
     t0 = time.time()
