@@ -233,6 +233,45 @@ def test_bwd_128k_key_columns(run_128k, cluster):
     _cols_check("128K " + cluster, r["dk"], r["dv"], cols, rk, rv)
 
 
+def test_prefill_chunk_4096_of_128k():
+    """A chunked-prefill training step at full length: the last 4096 query tokens against
+    the 131072-token keys (Lq < Lk, bottom-right distance d = i + Lk - Lq - j), forward and
+    backward.  O, LSE and dQ on 128 sampled rows, dK and dV on key columns in the sink,
+    in the bands of several heads, at the chunk's near edge and inside the chunk, each
+    element against the oracle; and the column-sum identities over all keys."""
+    Lq, Lk, sink, near = 4096, 131072, 128, 4096
+    _case(f"prefill chunk fwd+bwd Lq={Lq} Lk={Lk}")
+    ow = oracle.Window.for_length(Lk, HKV, sink, near, 0)
+    win = api.window(ow.sink, ow.near, ow.gap, ow.lr)
+    q, k, v, do = inputs.attention_inputs(1, Lq, Lk, HQ, HKV, D, seed=70, device=DEV, with_dout=True)
+    o, lse, dq, dk, dv = api.fwd_bwd(q, k, v, do, win)
+    torch.cuda.synchronize()
+    qc, kc, vc, doc = q.cpu(), k.cpu(), v.cpu(), do.cpu()
+    sk = dk.double().sum(dim=1)[0]
+    sv = dv.double().sum(dim=1)[0]
+    sdo = do.double().sum(dim=1)[0].view(HKV, HQ // HKV, D).sum(dim=1)
+    ex_k = (sk.abs() / _rounding_sigma(dk)).max().item()
+    ex_v = ((sv - sdo).abs() / (_rounding_sigma(dv) + 1e-3 / 6 * sdo.abs())).max().item()
+    print(f"  column sums: dK {ex_k:.2f} sigma, dV - dO {ex_v:.2f} sigma", flush=True)
+    assert ex_k <= 6.0 and ex_v <= 6.0
+    rng = np.random.default_rng(170)
+    must = {0, 1, 24, 25, 50, 51, 52, 255, 256, Lq - 2, Lq - 1}
+    rows = np.array(sorted(must | set(int(x) for x in rng.choice(Lq, 128 - len(must), replace=False))))
+    Oo, Lo = oracle.attn_fwd(qc, kc, vc, ow, SCALE, rows=rows)
+    idx = torch.as_tensor(rows, device=DEV)
+    assert_bf16_close("O", o[:, idx], Oo)
+    assert_bf16_close("LSE", lse[:, :, idx], Lo)
+    dqo = oracle.attn_bwd_dq_rows(qc, kc, vc, doc, ow, SCALE, rows)
+    assert_bf16_close("dQ", dq[:, idx], dqo, gradient=True)
+    off = Lk - Lq
+    cols = sorted({0, sink - 1, sink, 5000, Lk - 1 - (near + 3 * ow.lr), Lk - 1 - (near + 6 * ow.lr),
+                   off - near, off - near + 1, off - 1, off, off + 1, off + 777, Lk - 2, Lk - 1})
+    t0 = time.time()
+    rk, rv = oracle.attn_bwd_dkdv_cols(qc, kc, vc, doc, ow, SCALE, cols, workers=_workers())
+    print(f"  oracle: {len(cols)} key columns in {time.time() - t0:.1f} s", flush=True)
+    _cols_check("prefill chunk", dk, dv, cols, rk, rv)
+
+
 def test_bwd_4096_full_dk_dv():
     _case("bwd 4096 full dQ/dK/dV (the mid-size check of every key column)")
     L, sink, near = 4096, 128, 512
