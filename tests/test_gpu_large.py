@@ -272,6 +272,39 @@ def test_prefill_chunk_4096_of_128k():
     _cols_check("prefill chunk", dk, dv, cols, rk, rv)
 
 
+def test_dense_128k_sampled():
+    """Dense causal attention at 131072 tokens through the same kernels (the window that
+    the CoWA-against-dense ratios are measured with): O, LSE and dQ on 128 sampled rows,
+    dK and dV on the last key columns, and a two-sequence decode, against the oracle."""
+    L, sink, near = 131072, 128, 4096
+    _case("dense 128K fwd+bwd sampled rows, last key columns, decode")
+    ow, win, (q, k, v, do) = _setup(L, sink, near, "dense", seed=80, with_dout=True)
+    o, lse, dq, dk, dv = api.fwd_bwd(q, k, v, do, win)
+    torch.cuda.synchronize()
+    qc, kc, vc, doc = q.cpu(), k.cpu(), v.cpu(), do.cpu()
+    rows = sample_rows(L, sink, near, ow.lr, HKV, 128 // 5, 128, seed=180)
+    t0 = time.time()
+    Oo, Lo = oracle.attn_fwd(qc, kc, vc, ow, SCALE, rows=rows)
+    idx = torch.as_tensor(rows, device=DEV)
+    assert_bf16_close("O", o[:, idx], Oo)
+    assert_bf16_close("LSE", lse[:, :, idx], Lo)
+    dqo = oracle.attn_bwd_dq_rows(qc, kc, vc, doc, ow, SCALE, rows)
+    assert_bf16_close("dQ", dq[:, idx], dqo, gradient=True)
+    cols = [L - 129, L - 128, L - 65, L - 64, L - 2, L - 1]
+    rk, rv = oracle.attn_bwd_dkdv_cols(qc, kc, vc, doc, ow, SCALE, cols, workers=_workers())
+    print(f"  oracle: rows and {len(cols)} key columns in {time.time() - t0:.1f} s", flush=True)
+    _cols_check("dense 128K", dk, dv, cols, rk, rv)
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    qd, kd, vd = inputs.attention_inputs(2, 1, L, HQ, HKV, D, seed=81, device=DEV)
+    od, lsed = api.decode(qd, kd, vd, win)
+    torch.cuda.synchronize()
+    for b in range(2):
+        Oo, Lo = oracle.decode(qd[b:b + 1].cpu(), kd[b:b + 1].cpu(), vd[b:b + 1].cpu(), ow, SCALE)
+        assert_bf16_close(f"decode O[b={b}]", od[b:b + 1], Oo)
+        assert_bf16_close(f"decode LSE[b={b}]", lsed[b:b + 1], Lo[:, :, 0])
+
+
 def test_bwd_4096_full_dk_dv():
     _case("bwd 4096 full dQ/dK/dV (the mid-size check of every key column)")
     L, sink, near = 4096, 128, 512
