@@ -915,11 +915,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
       bf16x8 dt[2][4], qt[2][4];
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        dt[0][db] = join(lds_read_tr4(tg + QTILE + ofs_t(0, db)), lds_read_tr4(tg + QTILE + ofs_t(1, db)));
-        qt[0][db] = join(lds_read_tr4(tg + ofs_t(0, db)), lds_read_tr4(tg + ofs_t(1, db)));
-      }
       f32x16 sn;
       f32x4 f4[4], t4[4], l4[4], c4[4];
       f4[0] = cur.f0;
@@ -947,6 +942,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         if ((x & 1) && dd + 4 < 8) {
           qa[dd + 4] = load16(t1 + ofs_a(dd + 4));
           da[dd + 4] = load16(t1 + QTILE + ofs_a(dd + 4));
+        }
+        // copies of the next q-block: 8 in each of the first two steps, one every 2 MFMAs
+        // (here rather than beside the phase-2 products, whose slots carry the transposed
+        // reads)
+        if constexpr (RB < 2)
+          if (x & 1) copy(8 * RB + (x >> 1), IC<BUF ^ 1>{});
+        // transposed operands of half 0 for phase 2 (dO^T at slot 4 db, Q^T at 4 db + 2),
+        // one pair every other slot: issued together before the first product they made
+        // a burst of 20 LDS reads, more than the wait counter tracks, and the first
+        // product waited for ten of them
+        if ((x & 1) == 0) {
+          const int db = x >> 2;
+          if ((x & 2) == 0) dt[0][db] = join(lds_read_tr4(tg + QTILE + ofs_t(0, db)), lds_read_tr4(tg + QTILE + ofs_t(1, db)));
+          else qt[0][db] = join(lds_read_tr4(tg + ofs_t(0, db)), lds_read_tr4(tg + ofs_t(1, db)));
         }
         // dS constants of groups 1..3, four slots before their first use; P constants of
         // the next block's group 0, for phase 2
@@ -1025,9 +1034,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           const int db1 = (x - 2) >> 1;
           qt[1][db1] = join(lds_read_tr4(tg + 2048 + ofs_t(0, db1)), lds_read_tr4(tg + 2048 + ofs_t(1, db1)));
         }
-        // copies of the next q-block: 8 in each of the first two steps, one every 2 MFMAs
-        if constexpr (RB < 2)
-          if (x & 1) copy(8 * RB + (x >> 1), IC<BUF ^ 1>{});
         // P constants of groups 1..3, four slots ahead; the next step's first dS constants
         if ((x & 3) == 0 && x < 12) {
           const int i4 = (x >> 2) + 1;
