@@ -381,7 +381,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     auto tile = [&](auto bufc, const int tt) {
       constexpr int BUF = decltype(bufc)::value;
       wait_loads_and_barrier();  // tile tt resident; every wave is done with tile tt - 1
-      if (tt + 1 < ntile) copy_tile(ent_nxt, tt + 1, kbuf(IC<BUF ^ 1>{}), vbuf(IC<BUF ^ 1>{}));
+      const int64_t o_n = (int64_t)tile_j0(ent_nxt, tt + 1) * (HkvD * 2);
+      const __amdgpu_buffer_rsrc_t rk_n = tile_rsrc(kbase, kv_bytes, o_n, tt + 1 < ntile);
+      const __amdgpu_buffer_rsrc_t rv_n = tile_rsrc(vbase, kv_bytes, o_n, tt + 1 < ntile);
+      __bf16* const kd_n = kbuf(IC<BUF ^ 1>{});
+      __bf16* const vd_n = vbuf(IC<BUF ^ 1>{});
       if constexpr (MALA) {
         // (a last half past Lk holds no key: any flag serves, the clamp keeps it in bounds)
         if (tt + 1 < ntile) flag_nxt = mrow[min(tile_j0(ent_nxt, tt + 1) / QBK, a.mala_nkb - 1)];
@@ -413,6 +417,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           if (dd + 2 < 8) {
             ka[(dd + 2) % 3] = load16(kt + ofs_a(k2, dd + 2));
             va[(dd + 2) % 3] = load16(vt + ofs_a(k2, dd + 2));
+          }
+          if (k2 == 0 && (dd & 1) == 0) {
+            const int u = dd >> 1;
+            buf2lds(rk_n, voff[u], kd_n + (16 * wave + 4 * u) * D);
+            buf2lds(rv_n, voff[u], vd_n + (16 * wave + 4 * u) * D);
           }
           if (dd == 0) {
             mfma_f16_va0(sv, ka[0], qf[0]);
