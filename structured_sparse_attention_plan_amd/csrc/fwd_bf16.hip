@@ -515,8 +515,11 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
         }
         acc[c][db] = mfma32x32x16(vf[g % 3], pfp[k2][c][hf], acc[c][db]);
       }
-      if constexpr ((s & 7) == (MODE == 1 ? 4 : 5)) {
-        constexpr int u = s >> 3;  // 0..7: K(t+2) copies, then V(t) copies
+      // the tile copies, one every 4 slots in the first half of the block (slots 3, 7, ..,
+      // 31): landing early, they are done by the next barrier (one every 8 slots over the
+      // whole block took 2% longer); scoring: one every 8 slots
+      if constexpr (MODE == 1 ? (s & 7) == 4 : ((s & 3) == 3 && s < 32)) {
+        constexpr int u = MODE == 1 ? (s >> 3) : (s >> 2);  // 0..7: K(t+2) copies, then V(t) copies
         if constexpr (u < 4) copy_tile(rk, u, kdst);
         else if constexpr (MODE != 1) copy_tile(rv, u - 4, vdst);  // scoring reads no V
       }
