@@ -737,10 +737,18 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
     };
     // copy u: lane L sends logical chunk L % 16 of local row 4 u + L / 16
     auto drain = [&](__bf16* dst) __attribute__((always_inline)) {
+      // all of the wave's LDS reads first, then the stores (a read inside each store's
+      // row condition waited for its own LDS latency, 16 times over)
+      u32x4 wv[WROWS / 4];
 #pragma unroll
       for (int u = 0; u < WROWS / 4; ++u) {
         const int rl = 4 * u + (lane_e >> 4), ch = lane_e & 15;
-        const u32x4 w = *(const u32x4*)(so + rl * D + 8 * (ch ^ sw(rl)));
+        wv[u] = *(const u32x4*)(so + rl * D + 8 * (ch ^ sw(rl)));
+      }
+#pragma unroll
+      for (int u = 0; u < WROWS / 4; ++u) {
+        const int rl = 4 * u + (lane_e >> 4), ch = lane_e & 15;
+        const u32x4 w = wv[u];
         const int r = wave * WROWS + rl;
         const int rt = (int)(((uint32_t)r * ginv) >> 16);
         const int t = qb * Bq + rt;
