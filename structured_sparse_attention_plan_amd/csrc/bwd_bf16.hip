@@ -213,6 +213,42 @@ __device__ __forceinline__ void mfma_bf16_va0(f32x16& acc, const bf16x8& a, cons
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
 }
 
+// ------------------------------------------------------------------------ work queues
+// With `queues` set (one sequence), a work group does not take item order[blockIdx.x]:
+// thread 0 takes the next unclaimed position of its own XCD's queue (the launch order's
+// positions x, x + 8, ... that round-robin dispatch would give XCD x, in that order) by an
+// atomic add on the queue's head, and when that queue is used up the next position of
+// another XCD's queue.  XCDs of one chip run the same work up to 3% apart, so a fixed
+// deal ends with the slowest; with the queues a fast XCD's work groups take over positions
+// a slow one has not reached (the grid has n / 16 + 8 spare work groups for that; a work
+// group that finds every queue used up exits).  Each work group makes at most 8 attempts,
+// and every position is taken exactly once.  Returns -1 when no position is left.
+__device__ __forceinline__ int claim_item(const int32_t* order, int n, int32_t* heads) {
+  // XCC_ID hardware register: bits 3:0 hold the XCD of this work group
+  const int x = (int)__builtin_amdgcn_s_getreg((31 << 11) | 20) & 7;
+  for (int k = 0; k < 8; ++k) {
+    const int q = (x + k) & 7;
+    const int len = (n - q + 7) / 8;  // positions q, q + 8, ... below n
+    if (len <= 0) continue;
+    const int i = atomicAdd(heads + q, 1);
+    if (i < len) return order[q + 8 * i];
+  }
+  return -1;
+}
+
+// The item of this work group (every thread; one barrier): from the queues when the launch
+// has them, else the fixed position blockIdx.x of the launch order.
+__device__ __forceinline__ int take_item(const int32_t* order, int n, int32_t* heads, int* slot) {
+  if (!heads) return load_uniform(order, blockIdx.x);
+  if (threadIdx.x == 0) *slot = claim_item(order, n, heads);
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*slot);
+}
+
+__global__ __launch_bounds__(64) void bwd_queue_clear_kernel(int32_t* heads) {
+  if (threadIdx.x < 8) heads[threadIdx.x] = 0;
+}
+
 // ------------------------------------------------------------------------ dQ
 constexpr int QBK = 64;          // keys per tile
 constexpr int QTL = QBK * D;     // elements per K or V tile (16 KB)
@@ -251,7 +287,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int h2 = lane >> 5;
-  const int item = load_uniform(a.row_order, blockIdx.x);
+  __shared__ int sItem;
+  const int item = take_item(a.row_order, a.Hkv * a.nqb, a.queues, &sItem);
+  if (item < 0) return;
   const int b = blockIdx.y;
   const int h = item / a.nqb;
   const int qb = item - h * a.nqb;
@@ -557,7 +595,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: copy targets form on the SALU
   const int n = lane & 31;
   const int h2 = lane >> 5;
-  const int item = load_uniform(a.col_order, blockIdx.x);
+  __shared__ int sItem;
+  const int item = take_item(a.col_order, a.Hkv * a.nkb, a.queues ? a.queues + 8 : nullptr, &sItem);
+  if (item < 0) return;
   const int b = blockIdx.y;
   const int h = item / a.nkb;
   const int kb = item - h * a.nkb;
@@ -1144,14 +1184,24 @@ hipError_t launch_bwd_bf16_d128(const BwdArgs& a, int stages, hipStream_t s) {
     hipLaunchKernelGGL(bwd_k16_kernel, dim3((unsigned)((nkv + 15) / 16)), dim3(256), 0, s, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  // grid: every item, plus spare work groups when the queues are in use
+  auto grid = [&](int n) { return dim3((unsigned)(a.queues ? n + n / 16 + 8 : n), a.B); };
   if (stages & COWA_BWD_DQ) {
-    if (a.mala_mask) hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(a.Hkv * a.nqb, a.B), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(a.Hkv * a.nqb, a.B), dim3(256), 0, s, a);
+    if (a.queues) {
+      hipLaunchKernelGGL(bwd_queue_clear_kernel, dim3(1), dim3(64), 0, s, a.queues);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (a.mala_mask) hipLaunchKernelGGL(bwd_dq_kernel<true>, grid(a.Hkv * a.nqb), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(bwd_dq_kernel<false>, grid(a.Hkv * a.nqb), dim3(256), 0, s, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (stages & COWA_BWD_DKDV) {
-    if (a.mala_mask) hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(a.Hkv * a.nkb, a.B), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(a.Hkv * a.nkb, a.B), dim3(256), 0, s, a);
+    if (a.queues) {
+      hipLaunchKernelGGL(bwd_queue_clear_kernel, dim3(1), dim3(64), 0, s, a.queues + 8);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (a.mala_mask) hipLaunchKernelGGL(bwd_dkdv_kernel<true>, grid(a.Hkv * a.nkb), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(bwd_dkdv_kernel<false>, grid(a.Hkv * a.nkb), dim3(256), 0, s, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return err;

@@ -346,6 +346,9 @@ BwdArgs bwd_args(const cowa_problem* p, const cowa_plan_dev* plan, const void* q
   a.qscale = (float*)(ws + wl.qscale);
   a.doexp = (float*)(ws + wl.doexp);
   a.maxima = (float*)(ws + wl.maxima);
+  // per-XCD work queues of the dQ and dK/dV launches, in the unused half of the maxima
+  // block (one sequence: the launch orders cover one sequence's items)
+  a.queues = p->B == 1 ? (int32_t*)(ws + wl.maxima + 128) : nullptr;
   a.q16 = ws + wl.q16;
   a.do16 = ws + wl.do16;
   a.k16 = ws + wl.k16;

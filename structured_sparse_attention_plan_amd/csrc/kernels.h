@@ -80,6 +80,9 @@ struct BwdArgs {
   // mala_bq tokens, 64-key block); null for the CoWA backward
   const uint8_t* mala_mask;
   int32_t mala_bq, mala_nqb, mala_nkb;
+  // workspace (one sequence only, else null): per-XCD queue heads of the dQ launch [0, 8)
+  // and of the dK/dV launch [8, 16); each launch clears its own before it starts
+  int32_t* queues;
 };
 
 struct DecodeArgs {
