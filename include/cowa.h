@@ -155,8 +155,10 @@ int cowa_tile_sizes(int op, const cowa_problem* p, int32_t* Bq, int32_t* Bk);
 
 /* Bytes of device workspace `op` needs for problem p (0 if none).  The backward keeps
  * three fp32 values per (query head, row) (Delta, the power-of-two scales of Q and dO),
- * 256 bytes of launch-wide maxima, fp16 copies of Q and dO (2 * B * Lq * Hq * D * 2
- * bytes) and of K (B * Lk * Hkv * D * 2 bytes); the decode keeps its split partials.
+ * 256 bytes of launch-wide maxima (with the dQ and dK/dV launches' per-XCD work queue
+ * heads for one sequence), fp16 copies of Q and dO (2 * B * Lq * Hq * D * 2 bytes) and
+ * of K (B * Lk * Hkv * D * 2 bytes); the decode keeps its split partials; the bf16
+ * forward takes 256 bytes for its optional work queue heads.
  * COWA_OP_MALA_FWD needs 1 KB per visible forward tile and sequence plus the kept lists
  * (cowa_mala_fwd); COWA_OP_MALA_BWD adds one byte per forward tile (Hkv * ceil(Lq / Bq_f) * ceil(Lk / 64),
  * Bq_f the forward's tile height, rounded up to 256) to the backward's workspace. */
@@ -174,6 +176,12 @@ int cowa_workspace_size(int op, const cowa_problem* p, size_t* bytes);
  * significant bits instead of 8.
  * A row with no visible key (only possible with near_w = 0, or with Lq > Lk for the
  * first Lq - Lk rows) gets O = 0, LSE = -inf.
+ * workspace (optional, bf16): with at least cowa_workspace_size(COWA_OP_FWD) bytes (256),
+ * 256-byte aligned, and B = 1, it holds the launch's per-XCD work queue heads: each work
+ * group takes the next item of its XCD's part of the launch order, or of another XCD's
+ * part once its own is done, so XCDs that run slower take fewer items; NULL (or a smaller
+ * or unaligned one) keeps the fixed order.  The results are the same either way; calls
+ * that share a workspace must not overlap.
  * Errors: INVALID_ARG (also for o_lo with dtype F32), UNSUPPORTED, PLAN_MISMATCH (plan
  * tiling must be cowa_tile_sizes(COWA_OP_FWD)), HIP. */
 int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan,

@@ -139,9 +139,11 @@ def _workspace(name, ws, nbytes, device):
     return ws
 
 
-def fwd(q, k, v, win, scale=None, plan=None, out=None, lse=None, o_lo=None):
+def fwd(q, k, v, win, scale=None, plan=None, out=None, lse=None, o_lo=None, workspace=None):
     """Forward: q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] -> (o like q, lse [B,Hq,Lq] fp32).
-    o_lo (a tensor like q, bf16 only): filled with O's bf16 rounding residual, for bwd."""
+    o_lo (a tensor like q, bf16 only): filled with O's bf16 rounding residual, for bwd.
+    workspace (uint8, workspace_size("fwd") bytes; allocated when None): holds the launch's
+    work queues (bf16, one sequence)."""
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     scale = D ** -0.5 if scale is None else scale
@@ -156,9 +158,12 @@ def fwd(q, k, v, win, scale=None, plan=None, out=None, lse=None, o_lo=None):
     _check_tensor("lse", lse, (B, Hq, Lq), torch.float32, q.device)
     if o_lo is not None:
         _check_tensor("o_lo", o_lo, (B, Lq, Hq, D), q.dtype, q.device)
+    nbytes = workspace_size("fwd", prob)
+    ws = _workspace("workspace", workspace, nbytes, q.device) if nbytes else None
     C.check("cowa_fwd", C.lib.cowa_fwd(ctypes.byref(prob), ctypes.byref(plan.struct), q.data_ptr(),
                                        k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                       None if o_lo is None else o_lo.data_ptr(), None, 0,
+                                       None if o_lo is None else o_lo.data_ptr(),
+                                       None if ws is None else ws.data_ptr(), nbytes,
                                        _stream(q.device)))
     return out, lse
 

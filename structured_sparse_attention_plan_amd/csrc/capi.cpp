@@ -204,8 +204,8 @@ extern "C" int cowa_workspace_size(int op, const cowa_problem* p, size_t* bytes)
   st = check_op_support(op, p);
   if (st != COWA_OK) return st;
   switch (op) {
-    case COWA_OP_FWD:
-      *bytes = 0;
+    case COWA_OP_FWD:  // bf16: the optional per-XCD work queue heads (cowa_fwd)
+      *bytes = p->dtype == COWA_DTYPE_BF16 ? 256 : 0;
       break;
     case COWA_OP_BWD:
       *bytes = bwd_layout(p).total;
@@ -235,8 +235,6 @@ extern "C" int cowa_workspace_size(int op, const cowa_problem* p, size_t* bytes)
 extern "C" int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan, const void* q, const void* k,
                         const void* v, void* o, float* lse, void* o_lo, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int st = check_problem(p);
   if (st != COWA_OK) return st;
   st = check_op_support(COWA_OP_FWD, p);
@@ -270,6 +268,10 @@ extern "C" int cowa_fwd(const cowa_problem* p, const cowa_plan_dev* plan, const 
   a.scale = p->scale;
   a.scale_log2 = p->scale * 1.44269504088896340736f;
   a.win = dev_window(p->win);
+  // the optional workspace holds the launch's per-XCD work queue heads (one sequence)
+  if (p->dtype == COWA_DTYPE_BF16 && p->B == 1 && workspace && workspace_bytes >= 256 &&
+      ((uintptr_t)workspace & 255) == 0)
+    a.queues = (int32_t*)workspace;
   hipStream_t s = (hipStream_t)stream;
   if (p->dtype == COWA_DTYPE_F32) return hip_status(launch_fwd_f32_d64(a, s));
   return hip_status(launch_fwd_bf16_d128(a, s));

@@ -288,4 +288,36 @@ __host__ __device__ __forceinline__ int run_block(const BlockRuns& r, int e) {
   return e < n0 ? r.a0 + e : (e < n0 + n1 ? r.a1 + (e - n0) : r.a2 + (e - n0 - n1));
 }
 
+// Work queues.
+// With `queues` set (one sequence), a work group does not take item order[blockIdx.x]:
+// thread 0 takes the next unclaimed position of its own XCD's queue (the launch order's
+// positions x, x + 8, ... that round-robin dispatch would give XCD x, in that order) by an
+// atomic add on the queue's head, and when that queue is used up the next position of
+// another XCD's queue.  XCDs of one chip run the same work up to 3% apart, so a fixed
+// deal ends with the slowest; with the queues a fast XCD's work groups take over positions
+// a slow one has not reached (the grid has n / 16 + 8 spare work groups for that; a work
+// group that finds every queue used up exits).  Each work group makes at most 8 attempts,
+// and every position is taken exactly once.  Returns -1 when no position is left.
+__device__ __forceinline__ int claim_item(const int32_t* order, int n, int32_t* heads) {
+  // XCC_ID hardware register: bits 3:0 hold the XCD of this work group
+  const int x = (int)__builtin_amdgcn_s_getreg((31 << 11) | 20) & 7;
+  for (int k = 0; k < 8; ++k) {
+    const int q = (x + k) & 7;
+    const int len = (n - q + 7) / 8;  // positions q, q + 8, ... below n
+    if (len <= 0) continue;
+    const int i = atomicAdd(heads + q, 1);
+    if (i < len) return order[q + 8 * i];
+  }
+  return -1;
+}
+
+// The item of this work group (every thread; one barrier): from the queues when the launch
+// has them, else the fixed position blockIdx.x of the launch order.
+__device__ __forceinline__ int take_item(const int32_t* order, int n, int32_t* heads, int* slot) {
+  if (!heads) return load_uniform(order, blockIdx.x);
+  if (threadIdx.x == 0) *slot = claim_item(order, n, heads);
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*slot);
+}
+
 }  // namespace cowa

@@ -145,7 +145,9 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_d128_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
   const int n = lane & 31;
   const int h2 = lane >> 5;
-  const int item = a.row_order[blockIdx.x];
+  __shared__ int sItem;
+  const int item = take_item(a.row_order, a.n_items, a.queues, &sItem);
+  if (item < 0) return;
   const int b = blockIdx.y;
   const int h = item / a.nqb;
   const int qb = item - h * a.nqb;
@@ -813,8 +815,19 @@ __global__ __launch_bounds__(ROWS) void mala_decide_kernel(FwdArgs a) {
 
 }  // namespace
 
+// clears the 8 queue heads of one launch (see claim_item)
+__global__ __launch_bounds__(64) void fwd_queue_clear_kernel(int32_t* heads) {
+  if (threadIdx.x < 8) heads[threadIdx.x] = 0;
+}
+
 hipError_t launch_fwd_bf16_d128(const FwdArgs& a, hipStream_t s) {
-  dim3 grid(a.n_items, a.B);
+  // with the queues, spare work groups let fast XCDs take over positions of slow ones
+  dim3 grid(a.queues ? a.n_items + a.n_items / 16 + 8 : a.n_items, a.B);
+  if (a.queues) {
+    hipLaunchKernelGGL(fwd_queue_clear_kernel, dim3(1), dim3(64), 0, s, a.queues);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(fwd_bf16_d128_kernel<0>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -41,6 +41,9 @@ struct FwdArgs {
   float* mala_mass;        // [B, nnz, kFwdRows]
   int32_t* mala_ents;      // [B, nnz]
   int32_t* mala_counts;    // [B, n_items]
+  // workspace (one sequence only, else null): the 8 per-XCD queue heads of the launch,
+  // cleared by the launch before it starts
+  int32_t* queues;
   int32_t mala_nnz;
 };
 
